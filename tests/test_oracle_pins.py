@@ -1,0 +1,313 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU.  The oracle is checked against:
+  * the worked 8-value group and the outlier toy group printed in "What
+    actually happens when you quantize a KV cache" (§3 steps 3-5 and 7);
+  * an exact-rational brute force (tests/bruteforce.py) on tiny random shapes
+    and crafted corner-case groups, for every bit width 2..8;
+  * the closed-form bound |x - x_hat| <= s/2 of §4, and its clamped refinement;
+  * a round-trip fixpoint on weights built exactly on a quantization grid;
+  * special cases of the product that reduce to a library matmul or a dot
+    product, row independence of the batch, and an independent unpacking;
+  * the byte and FLOP accounting printed on the pages.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import bruteforce
+import wq_inputs
+from conftest import read_golden
+from edge_groups import crafted_groups, on_grid_matrix
+
+F16 = np.float16
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# Printed worked examples
+# --------------------------------------------------------------------------
+
+def test_worked_group_matches_page(oracle_mod):
+    g = read_golden("kvq_worked_group.txt")
+    x = np.array([float(v) for v in g["x"].split()], dtype=F16)[None, :]
+    codes, scales, zeros = oracle_mod.quantize(x, 8, int(g["bits"]))
+    s = float(scales[0, 0])
+    # The page prints s to 4 significant digits (exact quotient 1.15/15); the
+    # stored fp16 scale must round to the same printed value.
+    assert abs(s - float(g["s"])) < 5e-5
+    assert float(zeros[0, 0]) == float(g["z"])
+    assert _bits(zeros)[0, 0] == 0x4400
+    # Codes: unpack low nibble = even channel, high nibble = odd channel.
+    q = np.empty(8, dtype=np.int64)
+    q[0::2] = codes[0] & 0xF
+    q[1::2] = codes[0] >> 4
+    assert q.tolist() == [int(v) for v in g["codes"].split()]
+    assert [f"0x{b:02x}" for b in codes[0]] == g["packed_bytes"].split()
+    # Reconstruction and error columns agree with the printed 4-decimal values.
+    xhat = oracle_mod.dequantize(codes, scales, zeros, 1, 8, 8, 4)[0]
+    assert np.allclose(xhat, [float(v) for v in g["x_hat"].split()], atol=1.5e-4)
+    # The page's error column is x_hat minus the printed decimal input.
+    x_dec = np.array([float(v) for v in g["x"].split()])
+    assert np.allclose(xhat - x_dec, [float(v) for v in g["error"].split()], atol=2e-4)
+    # Bound: every error (against the fp16 input) within s/2 (printed as 0.038).
+    err = xhat - x[0].astype(np.float64)
+    assert np.max(np.abs(err)) <= s / 2
+    assert round(s / 2, 3) == float(g["bound"])
+
+
+def test_outlier_group_matches_page(oracle_mod):
+    g = read_golden("kvq_outlier_group.txt")
+    x = np.array([float(v) for v in g["x"].split()], dtype=F16)[None, :]
+    codes, scales, zeros = oracle_mod.quantize(x, 8, int(g["bits"]))
+    assert round(float(scales[0, 0]), 3) == float(g["s"])
+    assert _bits(zeros)[0, 0] == 0x0000  # z = 0 stored as +0.0
+    q = np.empty(8, dtype=np.int64)
+    q[0::2] = codes[0] & 0xF
+    q[1::2] = codes[0] >> 4
+    assert q.tolist() == [int(v) for v in g["codes"].split()]
+    assert [f"0x{b:02x}" for b in codes[0]] == g["packed_bytes"].split()
+    xhat = oracle_mod.dequantize(codes, scales, zeros, 1, 8, 8, 4)[0]
+    assert np.all(xhat[:7] == 0.0)  # seven of eight channels are erased
+
+
+# --------------------------------------------------------------------------
+# Exact brute force
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_oracle_matches_bruteforce_random(oracle_mod, bits):
+    rng = np.random.default_rng(100 + bits)
+    for group, K in [(8, 16), (16, 32), (8, 64), (64, 64)]:
+        N = 3
+        W = (rng.standard_normal((N, K)) * rng.choice([0.02, 1.0, 300.0])).astype(F16)
+        codes, scales, zeros = oracle_mod.quantize(W, group, bits)
+        bc, bs, bz = bruteforce.quantize(W, group, bits)
+        assert np.array_equal(codes, bc)
+        assert np.array_equal(_bits(scales), bs)
+        assert np.array_equal(_bits(zeros), bz)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("group", [8, 32])
+def test_oracle_matches_bruteforce_crafted(oracle_mod, bits, group):
+    W = crafted_groups(group, bits)
+    codes, scales, zeros = oracle_mod.quantize(W, group, bits)
+    bc, bs, bz = bruteforce.quantize(W, group, bits)
+    assert np.array_equal(_bits(scales), bs)
+    assert np.array_equal(_bits(zeros), bz)
+    assert np.array_equal(codes, bc)
+
+
+def test_degenerate_and_signed_zero_readings(oracle_mod):
+    # Constant group -> scale 1.0; zero point of 0 is +0.0; -0.0 codes like 0.
+    W = np.array([[0.0] * 8, [-0.0, 0.0] * 4, [0.3] * 8], dtype=F16)
+    codes, scales, zeros = oracle_mod.quantize(W, 8, 4)
+    assert _bits(scales)[0, 0] == 0x3C00 and _bits(zeros)[0, 0] == 0x0000
+    assert _bits(scales)[1, 0] == 0x3C00 and _bits(zeros)[1, 0] == 0x0000
+    assert np.all(codes[:2] == 0)
+    # Constant 0.3 with s = 1: z = round(-0.3) = 0 and every code rounds to 0.
+    assert _bits(zeros)[2, 0] == 0x0000 and np.all(codes[2] == 0)
+    # Saturating zero point at b = 8 on a tiny range far from zero.
+    W = np.array([[1000.0, 1000.5] * 4], dtype=F16)
+    _, _, zeros = oracle_mod.quantize(W, 8, 8)
+    assert _bits(zeros)[0, 0] == 0xFBFF  # -65504
+
+
+# --------------------------------------------------------------------------
+# Closed forms
+# --------------------------------------------------------------------------
+
+def _group_view(a, group):
+    N, K = a.shape
+    return a.reshape(N, K // group, group)
+
+
+def _unpack(codes, K, bits):
+    """Independent unpacking: numpy bit unpacking in little-endian bit order."""
+    N = codes.shape[0]
+    bitsarr = np.unpackbits(codes, axis=1, bitorder="little")[:, :K * bits]
+    w = (1 << np.arange(bits, dtype=np.int64))
+    return (bitsarr.reshape(N, K, bits).astype(np.int64) * w).sum(-1)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (4, 32), (8, 4096)])
+def test_error_bound(oracle_mod, bits, group):
+    """§4: |x - x_hat| <= s/2 for every element whose code is not clamped.
+
+    Only the top clamp can fire (the zero point is z itself whenever |z| is
+    small), and only when the fp16 scale fell below (max-min)/(2^b-1); then the
+    error is at most s/2 + |range - (2^b-1)*s|.  All comparisons are exact in
+    double (every quantity is a short multiple of 2^-24).
+    """
+    W, _ = wq_inputs.workload_arrays("mlp7b_up_k4096_n11008_g128", rows=256)
+    if group > W.shape[1]:
+        pytest.skip("group wider than the sample")
+    codes, scales, zeros = oracle_mod.quantize(W, group, bits)
+    N, K = W.shape
+    M = 2 ** bits - 1
+    q = _unpack(codes, K, bits)
+    x = W.astype(np.float64)
+    s = np.repeat(scales.astype(np.float64), group, axis=1)
+    z = np.repeat(zeros.astype(np.float64), group, axis=1)
+    xhat = (q - z) * s
+    err = np.abs(x - xhat)
+    xg = _group_view(x, group)
+    rng_ = np.repeat(xg.max(-1) - xg.min(-1), group, axis=1)
+    inner = (q > 0) & (q < M)
+    assert np.all(err[inner] <= s[inner] / 2)
+    assert np.all(err <= s / 2 + np.abs(rng_ - M * s))
+    # The clamp is rare and its excess is small, as the fp16 scale rounding
+    # allows (at most M*2^-11 relative to s at b=4 with normal scales).
+    assert np.max(err / s) < 0.5 + M * 2.0 ** -11 + 1e-12
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_fixpoint_on_grid(oracle_mod, bits):
+    group = 32
+    W, q, s, z = on_grid_matrix(6, 128, group, bits)
+    codes, scales, zeros = oracle_mod.quantize(W, group, bits)
+    assert np.array_equal(scales.astype(np.float64), s)
+    assert np.array_equal(zeros.astype(np.float64), z.astype(np.float64))
+    assert np.array_equal(_unpack(codes, 128, bits), q)
+    # Dequantization reproduces the grid exactly.
+    assert np.array_equal(oracle_mod.dequantize(codes, scales, zeros, 6, 128, group, bits),
+                          W.astype(np.float64))
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (4, 128), (8, 256), (3, 64)])
+def test_dequantize_definition(oracle_mod, bits, group):
+    rng = np.random.default_rng(7)
+    W = (rng.standard_normal((5, 256)) * 0.02).astype(F16)
+    codes, scales, zeros = oracle_mod.quantize(W, group, bits)
+    q = _unpack(codes, 256, bits)
+    want = (q - np.repeat(zeros.astype(np.float64), group, 1)) * \
+        np.repeat(scales.astype(np.float64), group, 1)
+    got = oracle_mod.dequantize(codes, scales, zeros, 5, 256, group, bits)
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------
+# The product
+# --------------------------------------------------------------------------
+
+def test_gemm_on_grid_equals_library_matmul(oracle_mod):
+    W, _, _, _ = on_grid_matrix(24, 256, 64, 4, seed=5)
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((5, 256)).astype(F16)
+    codes, scales, zeros = oracle_mod.quantize(W, 64, 4)
+    Y = oracle_mod.gemm(X, codes, scales, zeros, 24, 256, 64, 4)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    assert np.allclose(Y, ref, rtol=1e-12, atol=1e-300)
+
+
+def test_gemm_single_row_is_a_dot_product(oracle_mod):
+    rng = np.random.default_rng(8)
+    W = (rng.standard_normal((16, 512)) * 0.02).astype(F16)
+    x = rng.standard_normal((1, 512)).astype(F16)
+    codes, scales, zeros = oracle_mod.quantize(W, 128, 4)
+    Wh = oracle_mod.dequantize(codes, scales, zeros, 16, 512, 128, 4)
+    Y = oracle_mod.gemm(x, codes, scales, zeros, 16, 512, 128, 4)
+    for n in range(16):
+        exact = math.fsum(float(a) * float(b) for a, b in zip(x[0], Wh[n]))
+        assert abs(Y[0, n] - exact) <= 1e-12 * max(1.0, abs(exact))
+
+
+def test_gemm_row_independence_and_sampling(oracle_mod):
+    rng = np.random.default_rng(9)
+    W = (rng.standard_normal((40, 256)) * 0.02).astype(F16)
+    X = rng.standard_normal((6, 256)).astype(F16)
+    codes, scales, zeros = oracle_mod.quantize(W, 128, 4)
+    Y = oracle_mod.gemm(X, codes, scales, zeros, 40, 256, 128, 4)
+    for b in range(6):
+        Yb = oracle_mod.gemm(X[b:b + 1], codes, scales, zeros, 40, 256, 128, 4)
+        assert np.array_equal(Yb[0], Y[b])
+    rows = np.array([39, 0, 17, 17, 5])
+    Ys = oracle_mod.gemm(X, codes, scales, zeros, 40, 256, 128, 4, rows=rows)
+    assert np.array_equal(Ys, Y[:, rows])
+
+
+def test_oracle_rejects_bad_input(oracle_mod):
+    W = np.zeros((2, 64), dtype=F16)
+    with pytest.raises(ValueError):
+        oracle_mod.quantize(W, 48, 4)  # K % group != 0
+    W[1, 3] = np.inf
+    with pytest.raises(ValueError):
+        oracle_mod.quantize(W, 32, 4)
+
+
+# --------------------------------------------------------------------------
+# Accounting and roofline model
+# --------------------------------------------------------------------------
+
+def test_byte_accounting_matches_page():
+    from bit_weight_only_wq_amd import roofline as rl
+    g = read_golden("kvq_byte_counts.txt")
+    assert rl.packed_bytes(1, 128, 128, 4) == int(g["record_bytes_g128"])
+    assert 2 * 128 == int(g["fp16_bytes_g128"])
+    assert round(rl.compression_ratio(4, 128), 2) == float(g["ratio_g128"])
+    vals = int(g["per_token_values"])
+    assert 2 * vals == int(g["per_token_fp16_bytes"])
+    assert vals * 4 // 8 == int(g["per_token_int4_bytes"])
+    assert vals // 128 == int(g["per_token_groups"])
+    assert rl.packed_bytes(1, vals, 128, 4) - vals // 2 == int(g["per_token_header_bytes"])
+    assert 2 * vals // 1024 == int(g["per_token_total_kib_fp16"])
+    assert rl.packed_bytes(1, vals, 128, 4) // 1024 == int(g["per_token_total_kib_int4"])
+    for item in g["effective_bits"].split():
+        G, eb = item.split(":")
+        assert f"{rl.effective_bits(4, int(G)):.2f}" == eb
+    for item in g["ratio_by_group"].split():
+        G, r = item.split(":")
+        assert f"{rl.compression_ratio(4, int(G)):.2f}" == r
+
+
+def test_roofline_cards_match_page():
+    from bit_weight_only_wq_amd import roofline as rl
+    g = read_golden("qio_roofline_cards.txt")
+    for line in g["card"]:
+        name, tf, tb, ratio, be16, be4 = line.split()
+        flops, bw = float(tf) * 1e12, float(tb) * 1e12
+        assert round(rl.ridge_flop_per_byte(flops, bw)) == int(ratio)
+        assert round(rl.break_even_batch(flops, bw, 2.0)) == int(be16)
+        assert round(rl.break_even_batch(flops, bw, 0.5)) == int(be4)
+    b16, b4 = [float(v.split(":")[1]) for v in g["bytes_per_token_70b"].split()]
+    assert rl.bytes_read_per_token(70e9, 16) == b16
+    assert rl.bytes_read_per_token(70e9, 4) == b4
+    # Intensity 2B/w does not depend on the parameter count.
+    assert rl.intensity(8, 0.5) == 2 * 8 / 0.5
+    assert rl.gemm_flops(3, 7, 11) / rl.packed_bytes(7, 11 * 128, 128, 4) != 0
+
+
+# --------------------------------------------------------------------------
+# Quality statistic (not parity)
+# --------------------------------------------------------------------------
+
+def test_quality_band_on_the_4096_square_matrix(oracle_mod):
+    """Relative output error of 4-bit g128 on a 4096^2 N(0, 0.02) matrix.
+
+    "Quantization & inference optimisation" (section "Quantization") reports
+    0.1001 for its float-offset variant grouped along the output axis.  The
+    integer-zero, K-grouped codec here lands in the same band (about 0.099).
+    """
+    rng = np.random.default_rng(0)
+    Min_out = (rng.standard_normal((4096, 4096)) * 0.02).astype(np.float32)
+    x = rng.standard_normal(4096).astype(np.float32)
+    W = np.ascontiguousarray(Min_out.T).astype(F16)  # [N=out, K=in]
+    codes, scales, zeros = oracle_mod.quantize(W, 128, 4)
+    Wh = oracle_mod.dequantize(codes, scales, zeros, 4096, 4096, 128, 4)
+    ref = W.astype(np.float64) @ x.astype(np.float64)
+    err = np.linalg.norm(Wh @ x.astype(np.float64) - ref) / np.linalg.norm(ref)
+    assert 0.09 <= err <= 0.11
+
+
+def test_workloads_have_no_degenerate_groups():
+    for name in ("gemv_k896_n4864_g32", "mlp7b_up_k4096_n11008_g128"):
+        cfg = wq_inputs.WORKLOADS[name]
+        W, _ = wq_inputs.workload_arrays(name, rows=512)
+        g = W.reshape(W.shape[0], -1, cfg["group"]).astype(np.float64)
+        assert np.all(g.max(-1) > g.min(-1))
