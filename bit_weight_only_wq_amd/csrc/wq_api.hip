@@ -1,0 +1,146 @@
+// C ABI of the weight-only group-quantized decode GEMM (declared in include/wq.h).
+// Validation happens here, synchronously, before anything is enqueued; the
+// kernels are then launched on the caller's stream without synchronizing.
+#include <stdio.h>
+#include <string.h>
+
+#include "wq.h"
+#include "wq_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+wq_status fail(wq_status st, const char* fmt, long long a = 0, long long b = 0) {
+    snprintf(g_last_error, sizeof(g_last_error), fmt, a, b);
+    return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Compute units of the current device, cached per device.
+int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
+wq_status check_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return WQ_OK;
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
+    return WQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wq_version(void) { return WQ_VERSION; }
+
+const char* wq_status_string(wq_status s) {
+    switch (s) {
+        case WQ_OK: return "ok";
+        case WQ_ERR_INVALID_ARG: return "invalid argument";
+        case WQ_ERR_UNSUPPORTED: return "unsupported shape or layout";
+        case WQ_ERR_MISALIGNED: return "misaligned pointer or stride";
+        case WQ_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* wq_last_error(void) { return g_last_error; }
+
+size_t wq_codes_bytes(int64_t N, int64_t K, int32_t bits) {
+    if (N < 0 || K < 0 || bits < 1 || bits > 8 || (K * bits) % 8 != 0) return 0;
+    return (size_t)(N * K * bits / 8);
+}
+
+int64_t wq_num_groups(int64_t N, int64_t K, int32_t group) {
+    if (N < 0 || K < 0 || group < 1 || K % group != 0) return -1;
+    return N * (K / group);
+}
+
+int32_t wq_gemv_max_batch(void) { return 4; }
+
+wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, int32_t bits,
+                           void* codes, void* scales, void* zeros, void* stream) {
+    g_last_error[0] = '\0';
+    if (N < 0 || K < 1 || group < 1)
+        return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: need N >= 0, K >= 1, group >= 1 (N=%lld K=%lld)", N, K);
+    if (K % group != 0)
+        return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: K=%lld is not a multiple of group=%lld", K, group);
+    if (bits < 1 || bits > 8)
+        return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: bits=%lld out of range", bits);
+    if (bits != 4 && bits != 8)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: GPU codec takes bits 4 or 8 (got %lld)", bits);
+    if (group % 8 != 0)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: group=%lld must be a multiple of 8", group);
+    if (N == 0) return WQ_OK;
+    if (!W || !codes || !scales || !zeros)
+        return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: null pointer");
+    if (!aligned(W, 16) || !aligned(codes, bits == 4 ? 4 : 8) || !aligned(scales, 2) || !aligned(zeros, 2))
+        return fail(WQ_ERR_MISALIGNED, "wq_quantize_pack: W needs 16-byte, codes %lld-byte alignment",
+                    bits == 4 ? 4 : 8);
+    return check_hip(wq::launch_quantize_pack(W, N, K, group, bits, codes, scales, zeros,
+                                              static_cast<hipStream_t>(stream)),
+                     "wq_quantize_pack launch");
+}
+
+wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales, const void* zeros,
+                     void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                     int32_t path, void* stream) {
+    g_last_error[0] = '\0';
+    if (B < 0 || N < 0 || K < 1 || group < 1)
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm: need B >= 0, N >= 0, K >= 1, group >= 1 (B=%lld K=%lld)", B, K);
+    if (K % group != 0)
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm: K=%lld is not a multiple of group=%lld", K, group);
+    if (bits != 4 && bits != 8)
+        return fail(bits >= 1 && bits <= 8 ? WQ_ERR_UNSUPPORTED : WQ_ERR_INVALID_ARG,
+                    "wq_gemm: bits=%lld (GPU kernels take 4 or 8)", bits);
+    if (path < WQ_PATH_AUTO || path > WQ_PATH_MFMA)
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm: unknown path %lld", path);
+    const int vals = 128 / bits;  // codes per 16-byte chunk
+    if (K % vals != 0 || group % vals != 0)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: K=%lld and group=%lld must be multiples of the 16-byte chunk",
+                    K, group);
+    if (B == 0 || N == 0) return WQ_OK;
+    if (!X || !codes || !scales || !zeros || !Y)
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm: null pointer");
+    if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(Y, 2))
+        return fail(WQ_ERR_MISALIGNED, "wq_gemm: X and codes need 16-byte alignment");
+
+    const bool gemv_ok = wq::gemv_supports(K, bits);
+    const bool mfma_ok = wq::mfma_supports(K, group, bits);
+    int use = path;
+    if (use == WQ_PATH_AUTO) {
+        if (mfma_ok && (B > wq_gemv_max_batch() || !gemv_ok)) use = WQ_PATH_MFMA;
+        else use = WQ_PATH_GEMV;
+    }
+    if (use == WQ_PATH_GEMV && !gemv_ok)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: GEMV path does not take K=%lld at bits=%lld", K, bits);
+    if (use == WQ_PATH_MFMA && !mfma_ok)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: MFMA path needs group %% %lld == 0 (group=%lld)",
+                    bits == 4 ? 128 : 64, group);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (use == WQ_PATH_MFMA)
+        return check_hip(wq::launch_gemm_mfma(X, codes, scales, zeros, Y, B, K, N, group, bits,
+                                              num_cus(), st),
+                         "wq_gemm (mfma) launch");
+    return check_hip(wq::launch_gemv(X, codes, scales, zeros, Y, B, K, N, group, bits, num_cus(), st),
+                     "wq_gemm (gemv) launch");
+}
+
+wq_status wq_gemm(const void* X, const void* codes, const void* scales, const void* zeros,
+                  void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                  void* stream) {
+    return wq_gemm_ex(X, codes, scales, zeros, Y, B, K, N, group, bits, WQ_PATH_AUTO, stream);
+}
+
+}  // extern "C"

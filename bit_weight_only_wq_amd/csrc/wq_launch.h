@@ -1,0 +1,25 @@
+// Internal launchers (C++), called by the C ABI after validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+hipError_t launch_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
+                                int32_t bits, void* codes, void* scales, void* zeros,
+                                hipStream_t stream);
+
+// GEMV family: returns hipErrorInvalidValue when the shape is outside what the
+// instantiated tilings cover (the caller maps that to WQ_ERR_UNSUPPORTED).
+bool gemv_supports(int64_t K, int32_t bits);
+hipError_t launch_gemv(const void* X, const void* codes, const void* scales,
+                       const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
+                       int32_t group, int32_t bits, int num_cus, hipStream_t stream);
+
+bool mfma_supports(int64_t K, int32_t group, int32_t bits);
+hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales,
+                            const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
+                            int32_t group, int32_t bits, int num_cus, hipStream_t stream);
+
+}  // namespace wq

@@ -1,0 +1,142 @@
+/*
+ * wq.h — C ABI of the MI355X (gfx950) weight-only group-quantized decode GEMM.
+ *
+ * The library stores a weight matrix W[N, K] (fp16, row-major) as low-bit
+ * codes plus one fp16 scale and one fp16 zero point per group of `group`
+ * consecutive k of one row, and multiplies a batch of activations X[B, K]
+ * against it while dequantizing in registers:
+ *
+ *     Y[b, n] = sum_k X[b, k] * (q[n, k] - z[n, k/G]) * s[n, k/G]
+ *
+ * Sources (by page title and section):
+ *   "What actually happens when you quantize a KV cache", §3 steps 3-5 and §4:
+ *       s = (max - min) / (2^b - 1), z = round(-min / s),
+ *       q = clamp(round(x / s) + z, 0, 2^b - 1), x_hat = (q - z) * s,
+ *       two 4-bit codes per byte with the even channel in the low nibble, and a
+ *       4-byte header (fp16 scale + fp16 zero) per group kept in separate
+ *       contiguous arrays.
+ *   "Quantization & inference optimisation", sections "Bandwidth, not
+ *       compute" (one decode step reads the weights once for the batch: 2B/w
+ *       FLOP per byte) and "Quantization" (groups of consecutive weights from
+ *       one row; the kernel reconstructs the float as it reads).
+ *   "Serving many users at once: batching and quantization", sections
+ *       "Batching" (the B users' rows are stacked into X and multiplied once per
+ *       weight) and "Quantization" (groups along the in-features of a weight).
+ *
+ * Conventions shared by every entry point:
+ *   - All array pointers are DEVICE pointers to row-major, contiguous buffers
+ *     that the caller allocates, owns and frees.  The library allocates
+ *     nothing and keeps no state besides a cached device property.
+ *   - `stream` is a hipStream_t (NULL means the default stream).  Work is
+ *     enqueued on it and the call returns at once; the library never
+ *     synchronizes.  Buffers must stay alive until the stream has run the work.
+ *   - Arguments are validated synchronously before any launch; on error
+ *     nothing is enqueued.  A failed launch is reported as WQ_ERR_HIP.  No C++
+ *     exception crosses the ABI.  wq_last_error() describes the last failure
+ *     of the calling thread.
+ *   - Inputs must be finite (no NaN/Inf); this is not checked.
+ *   - Buffers must not alias one another.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WQ_OK = 0,
+    WQ_ERR_INVALID_ARG = 1,  /* bad size, null pointer, K % group != 0, ... */
+    WQ_ERR_UNSUPPORTED = 2,  /* valid for the codec, but not a layout the GPU kernels take */
+    WQ_ERR_MISALIGNED = 3,   /* a pointer or row stride is not aligned as required */
+    WQ_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} wq_status;
+
+/* Kernel family for wq_gemm_ex. */
+typedef enum {
+    WQ_PATH_AUTO = 0,  /* GEMV for small batches, MFMA skinny GEMM beyond */
+    WQ_PATH_GEMV = 1,  /* VALU dot products with wavefront (DPP) reductions */
+    WQ_PATH_MFMA = 2   /* fp16 matrix-core tiles with fp32 accumulation */
+} wq_path;
+
+/*
+ * Quantize and pack W (group-wise asymmetric, groups along K), as defined by
+ * "What actually happens when you quantize a KV cache" §3 steps 3-5 and §4:
+ *   per row n and group g of `group` consecutive k:
+ *     s = fp16(round-half-even((max - min) / (2^bits - 1)))  (1.0 if that is 0)
+ *     z = round-half-even(-min / s), stored as fp16 (saturating at +-65504;
+ *         0 is stored as +0.0)
+ *     q = clamp(round-half-even(x / s) + z, 0, 2^bits - 1)
+ *   All rounding decisions are exact (as in exact rational arithmetic).
+ *
+ * W       fp16 [N, K]                 input, 16-byte aligned
+ * codes   u8   [N, K*bits/8]          output; row n, code k sits at bits
+ *                                     [k*bits, k*bits+bits) of the row
+ *                                     (bits = 4: even k in the low nibble)
+ * scales  fp16 [N, K/group]           output (group index fastest)
+ * zeros   fp16 [N, K/group]           output
+ * N >= 0 (N == 0 is a no-op), K >= 1, group >= 1, K % group == 0.
+ * bits in {4, 8}; group % 8 == 0; codes 4-byte aligned (bits 4) or
+ * 8-byte aligned (bits 8); scales/zeros 2-byte aligned.
+ */
+wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
+                           int32_t bits, void* codes, void* scales, void* zeros,
+                           void* stream);
+
+/*
+ * Decode-step product with in-register dequantization ("Quantization &
+ * inference optimisation", "Bandwidth, not compute" and "Quantization"):
+ *     Y[b, n] = sum_k X[b, k] * (q[n, k] - zeros[n, k/group]) * scales[n, k/group]
+ * accumulated in fp32 and rounded once to fp16.
+ *
+ * X       fp16 [B, K]                 16-byte aligned
+ * codes, scales, zeros                as produced by wq_quantize_pack
+ *                                     (codes 16-byte aligned)
+ * Y       fp16 [B, N]                 output, 2-byte aligned
+ * B >= 0, N >= 0 (either 0 is a no-op), K >= 1, K % group == 0.
+ * bits 4: K % 32 == 0 and group % 32 == 0.  bits 8: K % 16 == 0 and
+ * group % 16 == 0.  The MFMA path additionally needs group % 128 (bits 4) or
+ * group % 64 (bits 8); WQ_PATH_AUTO falls back to the GEMV path otherwise.
+ * Results are deterministic: no atomics, fixed reduction order.
+ */
+wq_status wq_gemm(const void* X, const void* codes, const void* scales,
+                  const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
+                  int32_t group, int32_t bits, void* stream);
+
+/* wq_gemm with an explicit kernel family (for benchmarks and parity tests of
+ * each path).  Returns WQ_ERR_UNSUPPORTED if the forced path cannot take the
+ * shape. */
+wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales,
+                     const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
+                     int32_t group, int32_t bits, int32_t path, void* stream);
+
+/* Largest batch that WQ_PATH_AUTO sends to the GEMV path when the MFMA path
+ * can take the shape. */
+int32_t wq_gemv_max_batch(void);
+
+/* Bytes of the codes array: N * K * bits / 8 (0 on invalid input). */
+size_t wq_codes_bytes(int64_t N, int64_t K, int32_t bits);
+
+/* Number of groups: N * K / group, the element count of scales and of zeros
+ * (-1 on invalid input). */
+int64_t wq_num_groups(int64_t N, int64_t K, int32_t group);
+
+/* Static description of a status code. */
+const char* wq_status_string(wq_status s);
+
+/* Description of the calling thread's last failed call ("" if none). */
+const char* wq_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t wq_version(void);
+
+#define WQ_VERSION 100
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

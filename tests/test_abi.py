@@ -1,0 +1,99 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/wq.h declares, and rejects bad arguments synchronously (validation runs
+before any HIP call, so none of these calls touches a device)."""
+
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+wq = pytest.importorskip("bit_weight_only_wq_amd")
+from bit_weight_only_wq_amd import _lib  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "wq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = wq.load()
+    names = declared_functions()
+    assert "wq_quantize_pack" in names and "wq_gemm" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    # The Python binding declares a signature for each of them, and no others.
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_version_and_status_strings():
+    lib = wq.load()
+    assert lib.wq_version() == 100
+    for st in range(5):
+        assert lib.wq_status_string(st)
+    assert lib.wq_status_string(99) == b"unknown status"
+
+
+def test_size_helpers():
+    lib = wq.load()
+    assert lib.wq_codes_bytes(11008, 4096, 4) == 11008 * 4096 // 2
+    assert lib.wq_codes_bytes(4096, 11008, 8) == 4096 * 11008
+    assert lib.wq_codes_bytes(-1, 8, 4) == 0
+    assert lib.wq_num_groups(28672, 8192, 128) == 28672 * 64
+    assert lib.wq_num_groups(4, 100, 128) == -1
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def _gemm(B=4, K=256, N=64, group=128, bits=4, path=0, X=FAKE, C=FAKE, S=FAKE, Z=FAKE, Y=FAKE):
+    return wq.load().wq_gemm_ex(X, C, S, Z, Y, B, K, N, group, bits, path, None)
+
+
+def _quant(N=64, K=256, group=128, bits=4, W=FAKE, C=FAKE, S=FAKE, Z=FAKE):
+    return wq.load().wq_quantize_pack(W, N, K, group, bits, C, S, Z, None)
+
+
+def test_gemm_validation_errors():
+    assert _gemm(K=250) == _lib.WQ_ERR_INVALID_ARG          # K % group
+    assert _gemm(B=-1) == _lib.WQ_ERR_INVALID_ARG
+    assert _gemm(K=0) == _lib.WQ_ERR_INVALID_ARG
+    assert _gemm(group=0) == _lib.WQ_ERR_INVALID_ARG
+    assert _gemm(bits=3) == _lib.WQ_ERR_UNSUPPORTED
+    assert _gemm(bits=9) == _lib.WQ_ERR_INVALID_ARG
+    assert _gemm(path=7) == _lib.WQ_ERR_INVALID_ARG
+    assert _gemm(group=16, K=256) == _lib.WQ_ERR_UNSUPPORTED  # chunk spans groups
+    assert _gemm(X=0) == _lib.WQ_ERR_INVALID_ARG
+    assert _gemm(Y=0) == _lib.WQ_ERR_INVALID_ARG
+    assert _gemm(X=FAKE + 8) == _lib.WQ_ERR_MISALIGNED
+    assert _gemm(C=FAKE + 4) == _lib.WQ_ERR_MISALIGNED
+    assert _gemm(Y=FAKE + 1) == _lib.WQ_ERR_MISALIGNED
+    # The MFMA path needs group % 128 at 4 bits.
+    assert _gemm(group=32, path=_lib.WQ_PATH_MFMA) == _lib.WQ_ERR_UNSUPPORTED
+    assert wq.load().wq_last_error()
+
+
+def test_empty_calls_are_no_ops():
+    assert _gemm(B=0, X=0, Y=0) == _lib.WQ_OK
+    assert _gemm(N=0, C=0, S=0, Z=0, Y=0) == _lib.WQ_OK
+    assert _quant(N=0, W=0, C=0, S=0, Z=0) == _lib.WQ_OK
+
+
+def test_quantize_validation_errors():
+    assert _quant(K=250) == _lib.WQ_ERR_INVALID_ARG
+    assert _quant(bits=0) == _lib.WQ_ERR_INVALID_ARG
+    assert _quant(bits=3) == _lib.WQ_ERR_UNSUPPORTED
+    assert _quant(group=4, K=256) == _lib.WQ_ERR_UNSUPPORTED
+    assert _quant(W=0) == _lib.WQ_ERR_INVALID_ARG
+    assert _quant(W=FAKE + 2) == _lib.WQ_ERR_MISALIGNED
+    assert _quant(bits=8, C=FAKE + 4) == _lib.WQ_ERR_MISALIGNED
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(wq.WQError):
+        _lib.check(_gemm(K=250), "wq_gemm")
