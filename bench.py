@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 group-quantized decode GEMM on one MI355X.
+
+One step is one pass of the whole hot path over the 70B-class MLP
+up-projection (K=8192, N=28672, 4-bit codes, group 128 along K):
+    wq_quantize_pack(W)                      fp16 weights -> codes + fp16 headers
+    wq_gemm(X[B], codes) for B = 1, 16, 64   decode-step products
+Each kernel works on its own copy from a pool of packed weights larger than
+1 GiB (two fp16 weight copies for the quantizer), so no call finds its inputs
+in the 256 MB Infinity Cache or the L2: every call streams from HBM.  Inputs
+are resident in HBM before timing starts.
+
+Printed: one JSON line with the whole step's algorithmic bytes per second
+(value, GB/s), the roofline of the B=1 product (the metric's kernel) with
+its duration measured by HIP events on the stream it runs on, the other
+kernels' rooflines, and the CPU oracle timed on a bounded sample of the
+same step.
+
+    python bench.py [--steps 20] [--warmup 5] [--no-cpu]
+    python bench.py --sweep     # batch sweep across the ridge (K=N=8192), table only
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for int4 group-quant decode GEMM at B=1..64"
+WORKLOAD = "mlp70b_up_k8192_n28672_g128"
+POOL_BYTES = 1 << 30          # packed-weight pool, >= 4x the 256 MB Infinity Cache
+CPU_SAMPLE_ROWS = 16384       # rows of the workload the oracle processes
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=WORKLOAD)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--sweep", action="store_true", help="batch sweep on K=N=8192 (table)")
+    p.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
+    return p.parse_args()
+
+
+def kernel_entry(name, nbytes, flops, ms_list, bound="hbm"):
+    from bit_weight_only_wq_amd import roofline as rl
+    ms = sum(ms_list) / len(ms_list)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    e = {"kernel": name, "avg_us": round(ms * 1e3, 3), "bytes": int(nbytes),
+         "achieved_GBps": round(gbs, 1), "frac_hbm": round(gbs * 1e9 / rl.MI355X_HBM_BYTES_PER_S, 4)}
+    if flops:
+        e["TFLOPs"] = round(tflops, 2)
+        e["frac_mfma_f16"] = round(tflops * 1e12 / rl.MI355X_FP16_MFMA_FLOPS, 4)
+    e["bound"] = bound
+    return e
+
+
+def read_traffic(kernel_tag):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, _, v = line.partition(":")
+            vals[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "bit_weight_only_wq_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(src)):
+        h.update(open(os.path.join(src, f), "rb").read())
+    if vals.get("csrc_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(name, batches):
+    import numpy as np
+    import oracle
+    import wq_inputs
+    from bit_weight_only_wq_amd import roofline as rl
+    cfg = wq_inputs.WORKLOADS[name]
+    rows = min(CPU_SAMPLE_ROWS, cfg["N"])
+    W, X = wq_inputs.workload_arrays(name, rows=rows)
+    K, G, bits = cfg["K"], cfg["group"], cfg["bits"]
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    c, s, z = oracle.quantize(W, G, bits)
+    for B in batches:
+        oracle.gemm(X[:B], c, s, z, rows, K, G, bits)
+    dt = time.perf_counter() - t0
+    nbytes = rl.quantize_bytes(rows, K, G, bits) + sum(rl.gemm_bytes(B, rows, K, G, bits)
+                                                      for B in batches)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {rows} of {cfg['N']} rows of {name}: exact quantize/pack + "
+                      f"double-precision GEMM at B={','.join(map(str, batches))}"}
+
+
+def run_step_bench(args):
+    import numpy as np
+    import torch
+
+    import bit_weight_only_wq_amd as wq
+    import wq_inputs
+    from bit_weight_only_wq_amd import roofline as rl
+
+    cfg = wq_inputs.WORKLOADS[args.workload]
+    N, K, G, bits = cfg["N"], cfg["K"], cfg["group"], cfg["bits"]
+    batches = [b for b in cfg["batches"] if b <= 64] or [1]
+    dev = torch.device("cuda:0")
+    Wn, Xn = wq_inputs.workload_arrays(args.workload)
+    Wd = [torch.from_numpy(Wn).to(dev) for _ in range(2)]
+    Xd = torch.from_numpy(Xn).to(dev)
+    Xb = {B: Xd[:B].contiguous() for B in batches}
+    Yb = {B: torch.empty((B, N), dtype=torch.float16, device=dev) for B in batches}
+    slot_bytes = rl.packed_bytes(N, K, G, bits)
+    P = max(len(batches) + 3, -(-POOL_BYTES // slot_bytes))
+    P = max(P, 2 * len(batches) + 3)
+    pool = [wq.quantize_pack(Wd[0], G, bits) for _ in range(P)]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    nb = len(batches)
+    # The timed loop calls the C ABI directly with precomputed pointers, so
+    # host-side overhead stays far below the kernels' duration.
+    lib = wq.load()
+    hs = stream.cuda_stream
+    path_id = {"auto": wq.WQ_PATH_AUTO, "gemv": wq.WQ_PATH_GEMV, "mfma": wq.WQ_PATH_MFMA}[args.path]
+    slot_ptrs = [(c.data_ptr(), s.data_ptr(), z.data_ptr()) for c, s, z in pool]
+    w_ptrs = [w.data_ptr() for w in Wd]
+    xy = {B: (Xb[B].data_ptr(), Yb[B].data_ptr()) for B in batches}
+
+    def step(i, evs=None):
+        # Products first, each on its own pool slot; then the quantizer writes a
+        # slot that is next read two steps later (>1 GB of traffic in between).
+        if evs is not None:
+            evs[0].record(stream)
+        for j, B in enumerate(batches):
+            c, s, z = slot_ptrs[(nb * i + j) % P]
+            st = lib.wq_gemm_ex(xy[B][0], c, s, z, xy[B][1], B, K, N, G, bits, path_id, hs)
+            if st:
+                wq.check(st, "wq_gemm")
+            if evs is not None:
+                evs[j + 1].record(stream)
+        c, s, z = slot_ptrs[(nb * i + 2 * nb + 1) % P]
+        st = lib.wq_quantize_pack(w_ptrs[i % 2], N, K, G, bits, c, s, z, hs)
+        if st:
+            wq.check(st, "wq_quantize_pack")
+        if evs is not None:
+            evs[nb + 1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nb + 2)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+
+    per = {B: [] for B in batches}
+    per_q = []
+    for e in evs:
+        for j, B in enumerate(batches):
+            per[B].append(e[j].elapsed_time(e[j + 1]))
+        per_q.append(e[nb].elapsed_time(e[nb + 1]))
+
+    step_bytes = rl.quantize_bytes(N, K, G, bits) + sum(rl.gemm_bytes(B, N, K, G, bits)
+                                                       for B in batches)
+    kernels = {}
+    for B in batches:
+        kernels[f"wq_gemm_B{B}"] = kernel_entry(
+            f"wq_gemm B={B}", rl.gemm_bytes(B, N, K, G, bits), rl.gemm_flops(B, N, K), per[B])
+    kernels["wq_quantize_pack"] = kernel_entry(
+        "wq_quantize_pack", rl.quantize_bytes(N, K, G, bits), 0, per_q)
+
+    head = kernels[f"wq_gemm_B{batches[0]}"]
+    traffic = read_traffic(f"wq_gemm_b{batches[0]}_{args.workload}")
+    roof = {"kernel": head["kernel"], "bound": "hbm", "achieved": head["achieved_GBps"],
+            "peak": rl.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
+            "frac": round(head["achieved_GBps"] * 1e9 / rl.MI355X_HBM_BYTES_PER_S, 4),
+            "traffic": traffic, "avg_us": head["avg_us"], "bytes_per_launch": head["bytes"]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "N": N, "K": K, "group": G, "bits": bits,
+                   "batches": batches, "path": args.path,
+                   "step": "wq_quantize_pack + wq_gemm at B=" + ",".join(map(str, batches)),
+                   "step_bytes": int(step_bytes), "pool_slots": P,
+                   "wall_s": round(wall, 4)},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    del pool, Wd
+    torch.cuda.empty_cache()
+    return out, batches
+
+
+def run_sweep(args):
+    import torch
+
+    import bit_weight_only_wq_amd as wq
+    import wq_inputs
+    from bit_weight_only_wq_amd import roofline as rl
+
+    name = "ridge_sweep_k8192_n8192_g128"
+    cfg = wq_inputs.WORKLOADS[name]
+    N, K, G, bits = cfg["N"], cfg["K"], cfg["group"], cfg["bits"]
+    dev = torch.device("cuda:0")
+    Wn, Xn = wq_inputs.workload_arrays(name)
+    W = torch.from_numpy(Wn).to(dev)
+    X = torch.from_numpy(Xn).to(dev)
+    P = -(-POOL_BYTES // rl.packed_bytes(N, K, G, bits)) + 1
+    pool = [wq.quantize_pack(W, G, bits) for _ in range(P)]
+    rows = []
+    for B in cfg["batches"]:
+        for path in ("gemv", "mfma"):
+            if path == "gemv" and B > 8:
+                continue
+            Xb = X[:B].contiguous()
+            Y = torch.empty((B, N), dtype=torch.float16, device=dev)
+            for i in range(3):
+                c, s, z = pool[i % P]
+                wq.gemm(Xb, c, s, z, N=N, K=K, group=G, bits=bits, path=path, out=Y)
+            torch.cuda.synchronize()
+            reps = 30
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                c, s, z = pool[i % P]
+                wq.gemm(Xb, c, s, z, N=N, K=K, group=G, bits=bits, path=path, out=Y)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            nbytes = rl.gemm_bytes(B, N, K, G, bits)
+            fl = rl.gemm_flops(B, N, K)
+            model = rl.roofline_time_s(nbytes, fl) * 1e3
+            rows.append({"B": B, "path": path, "us": round(ms * 1e3, 2),
+                         "GBps": round(nbytes / ms / 1e6, 1),
+                         "TFLOPs": round(fl / ms / 1e9, 2),
+                         "intensity_2B_over_w": round(rl.intensity(B, rl.bytes_per_weight(bits, G)), 1),
+                         "roofline_us": round(model * 1e3, 2)})
+            print(json.dumps(rows[-1]), flush=True)
+    return rows
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if args.sweep:
+        run_sweep(args)
+        return
+    out, batches = run_step_bench(args)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(args.workload, batches)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

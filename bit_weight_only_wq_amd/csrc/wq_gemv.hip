@@ -32,7 +32,9 @@ struct ChunkGeom {
     static constexpr int PAIRS_PER_WORD = PAIRS / 4;
 };
 
-// Pair p of word j pairs up the codes at chunk positions (first, second).
+// X positions (within a chunk) of fp16 pair p of word j, in unpack order.
+// 4-bit: pairs (q0,q4) (q1,q5) (q2,q6) (q3,q7) of each 8-code word.
+// 8-bit: pairs (q0,q2) (q1,q3) of each 4-code word.
 template <int BITS>
 __device__ __forceinline__ void pair_positions(int j, int p, int& a, int& b) {
     if constexpr (BITS == 4) {
@@ -44,114 +46,233 @@ __device__ __forceinline__ void pair_positions(int j, int p, int& a, int& b) {
     }
 }
 
-template <int BITS>
-__device__ __forceinline__ uint32_t code_pair(uint32_t w, int p) {
-    if constexpr (BITS == 4) return nib_pair(w, p);
-    else return byte_pair(w, p);
+// A 32-bit constant held in a VGPR.  gfx9 VOP3 instructions take no literal
+// operand, so keeping the nibble masks in registers lets every unpack step be
+// a single v_and_or_b32 (mask from a VGPR, the 0x6400 exponent from an SGPR).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+    return r;
 }
 
+// Wave-scope ordering of LDS accesses made by the lanes of one wave.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 128-bit load that bypasses cache allocation: every code byte is read once.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// X lives in LDS for the whole kernel as one record per (batch row, chunk):
+//   QPC uint4   the chunk's fp16 X pairs in the order its codes unpack;
+//   float2      (K0, xT): xT = sum of the chunk's X, and K0 the constant that
+//               the unpack offsets contribute (1024 per unscaled code, 64 per
+//               code unpacked times 16, after the 1/16 rescale);
+//   float2      padding, so records are 80 (4-bit) or 48 (8-bit) bytes apart
+//               and the 16-byte reads of consecutive threads avoid bank clashes.
+// Then for a chunk, with pa accumulated from -K0 over the unscaled codes and
+// pb over the scaled ones:  sum_k (q_k - z) x_k = pa + pb/16 - z * xT.
 template <int BITS, int NB, int TG, int CPT>
 __global__ __launch_bounds__(256) void gemv_kernel(
     const uint16_t* __restrict__ X, const uint4* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, int64_t B, int64_t N, int64_t K, int32_t G) {
     typedef ChunkGeom<BITS> CG;
-    constexpr int RPB = 256 / TG;      // rows per block pass
+    constexpr int QPC = CG::PAIRS / 4;          // uint4 of X pairs per chunk
+    constexpr int REC = QPC + 1;                // uint4 per X record
+    constexpr int RPB = 256 / TG;               // rows per block pass
     constexpr int WPR = TG > 64 ? TG / 64 : 1;  // waves per row
+    constexpr uint32_t MAGIC = 0x64006400u;     // fp16 1024.0 in both halves
+    extern __shared__ __align__(16) unsigned char smem[];
+    // Per row slot, (scale, zero) of the row's groups as floats.  A row has at
+    // most TG*CPT chunks, hence at most TG*CPT groups.
+    __shared__ float2 hdr[RPB * TG * CPT];
     __shared__ float red[(TG > 64) ? 4 * NB : 1];
 
     const int tid = threadIdx.x;
     const int rs = tid / TG;           // row slot in the pass
     const int tl = tid % TG;           // thread within the row
-    const int64_t C = K / CG::VALS;    // chunks per row
+    const int C = (int)(K / CG::VALS); // chunks per row
     const int64_t ngrp = K / G;        // groups per row
     const int cpg = G / CG::VALS;      // chunks per group
     const int64_t b0 = (int64_t)blockIdx.y * NB;
     const int nb = (int)((B - b0) < NB ? (B - b0) : NB);
+    const int64_t passes = (N + RPB - 1) / RPB;
+    float2* row_hdr = hdr + rs * (TG * CPT);
+    uint4* xrec = reinterpret_cast<uint4*>(smem);
+    const uint32_t m_lo = vgpr_const(BITS == 4 ? 0x000F000Fu : 0x00FF00FFu);
+    const uint32_t m_hi = vgpr_const(0x00F000F0u);
 
-    // ---- X fragments in registers (permuted pairs) and chunk sums ----------
-    uint32_t xp[CPT][NB][CG::PAIRS];
-    float xsum[CPT][NB];
+    // This thread's chunks: clamped index, group and liveness (ragged rows).
+    int cidx[CPT], gidx[CPT];
+    bool cin[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-        const int64_t c = tl + (int64_t)TG * i;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            uint16_t xv[CG::VALS];
-            if (c < C && b < nb) {
-                const uint4* src = reinterpret_cast<const uint4*>(X + (b0 + b) * K + c * CG::VALS);
-#pragma unroll
-                for (int v = 0; v < CG::VALS / 8; ++v) {
-                    uint4 u = src[v];
-                    uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        xv[8 * v + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
-                        xv[8 * v + 2 * e + 1] = (uint16_t)(w[e] >> 16);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int v = 0; v < CG::VALS; ++v) xv[v] = 0;
-            }
-            float s = 0.0f;
-#pragma unroll
-            for (int v = 0; v < CG::VALS; ++v) s += half_bits_to_float(xv[v]);
-            xsum[i][b] = s;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int p = 0; p < CG::PAIRS_PER_WORD; ++p) {
-                    int a, bb;
-                    pair_positions<BITS>(j, p, a, bb);
-                    xp[i][b][j * CG::PAIRS_PER_WORD + p] = (uint32_t)xv[a] | ((uint32_t)xv[bb] << 16);
-                }
-        }
+        const int c = tl + TG * i;
+        cin[i] = c < C;
+        cidx[i] = c < C ? c : C - 1;
+        gidx[i] = cidx[i] / cpg;
     }
 
-    // ---- stream rows ---------------------------------------------------------
-    const int64_t passes = (N + RPB - 1) / RPB;
-    for (int64_t pass = blockIdx.x; pass < passes; pass += gridDim.x) {
-        const int64_t n = pass * RPB + rs;
-        const bool row_ok = n < N;
-        uint4 w[CPT];
-        float s[CPT], zc[CPT];
+    // Global loads of one pass: this thread's code chunks of row n, and the
+    // header entries tl, tl+TG, ... of that row (coalesced 2-byte loads, kept
+    // in separate registers so that nothing waits on them before use).
+    // Branches are block-uniform; per-lane bounds clamp the address instead
+    // (a clamped chunk is loaded but later weighted by a zero scale).
+    int hidx[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int64_t g = tl + (int64_t)TG * i;
+        hidx[i] = (int)(g < ngrp ? g : ngrp - 1);
+    }
+    auto load_pass = [&](int64_t pass, uint4* w, uint32_t* hs, uint32_t* hz) {
+        if (pass >= passes) return;
+        int64_t n = pass * RPB + rs;
+        n = n < N ? n : N - 1;
+        const uint4* rowc = codes + n * C;
+        const uint16_t* rows = scales + n * ngrp;
+        const uint16_t* rowz = zeros + n * ngrp;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int64_t c = tl + (int64_t)TG * i;
-            if (row_ok && c < C) {
-                w[i] = codes[n * C + c];
-                const int64_t gi = n * ngrp + c / cpg;
-                s[i] = half_bits_to_float(scales[gi]);
-                zc[i] = 1024.0f + half_bits_to_float(zeros[gi]);
-            } else {
-                w[i] = make_uint4(0u, 0u, 0u, 0u);
-                s[i] = 0.0f;
-                zc[i] = 0.0f;
+            if (TG * i < C) w[i] = load_stream(rowc + cidx[i]);
+            if ((int64_t)TG * i < ngrp) {
+                hs[i] = rows[hidx[i]];
+                hz[i] = rowz[hidx[i]];
             }
         }
+    };
+
+    int64_t pass = blockIdx.x;
+    uint4 wA[CPT], wB[CPT];
+    uint32_t sA[CPT], sB[CPT], zA[CPT], zB[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        wA[i] = wB[i] = make_uint4(0u, 0u, 0u, 0u);
+        sA[i] = sB[i] = zA[i] = zB[i] = 0u;
+    }
+    load_pass(pass, wA, sA, zA);        // first codes in flight before the X setup
+
+    // ---- X records into LDS (whole block) ------------------------------------
+    for (int e = tid; e < NB * C; e += 256) {
+        const int b = e / C, c = e % C;
+        uint16_t xv[CG::VALS];
+        if (b < nb) {
+            const uint4* src = reinterpret_cast<const uint4*>(X + (b0 + b) * K + (int64_t)c * CG::VALS);
+#pragma unroll
+            for (int v = 0; v < CG::VALS / 8; ++v) {
+                uint4 u = src[v];
+                uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    xv[8 * v + 2 * q] = (uint16_t)(ww[q] & 0xFFFFu);
+                    xv[8 * v + 2 * q + 1] = (uint16_t)(ww[q] >> 16);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < CG::VALS; ++v) xv[v] = 0;
+        }
+        uint32_t pr[CG::PAIRS];
+        float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int p = 0; p < CG::PAIRS_PER_WORD; ++p) {
+                int a, bb;
+                pair_positions<BITS>(j, p, a, bb);
+                pr[j * CG::PAIRS_PER_WORD + p] = (uint32_t)xv[a] | ((uint32_t)xv[bb] << 16);
+                const float t = half_bits_to_float(xv[a]) + half_bits_to_float(xv[bb]);
+                if (BITS == 4 && (p & 1)) sb += t;
+                else sa += t;
+            }
+        uint4* rec = xrec + (size_t)e * REC;
+#pragma unroll
+        for (int r = 0; r < QPC; ++r)
+            rec[r] = make_uint4(pr[4 * r], pr[4 * r + 1], pr[4 * r + 2], pr[4 * r + 3]);
+        const float k0 = 1024.0f * sa + 64.0f * sb;
+        rec[QPC] = make_uint4(__builtin_bit_cast(uint32_t, k0), __builtin_bit_cast(uint32_t, sa + sb), 0u, 0u);
+    }
+    __syncthreads();
+
+    // One pass: stage the row's header in LDS, compute, reduce, store.
+    auto compute_pass = [&](int64_t ps, const uint4* w, const uint32_t* hs, const uint32_t* hz) {
+        const int64_t n = ps * RPB + rs;
+        const bool row_ok = n < N;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+            if ((int64_t)TG * i < ngrp)   // uniform; clamped lanes rewrite the last entry
+                row_hdr[hidx[i]] = make_float2(half_bits_to_float((uint16_t)hs[i]),
+                                               half_bits_to_float((uint16_t)hz[i]));
+        if constexpr (TG > 64) __syncthreads();
+        else wave_lds_sync();
+
         float acc[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
+            const float2 sz = row_hdr[gidx[i]];
+            const float s = (row_ok && cin[i]) ? sz.x : 0.0f;
             const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-            float part[NB];
+            const uint4* rec[NB];
+            float pa[NB], pb[NB], xt[NB];
+            // The X records do not change between passes; an opaque copy of the
+            // index keeps their LDS reads inside the pass loop instead of being
+            // hoisted into registers (which would cost occupancy).
+            // The dependency on acc also orders chunk i's X reads after chunk
+            // i-1's math, which bounds the registers holding X in flight.
+            int ci = cidx[i];
+            asm volatile("" : "+v"(ci) : "v"(acc[0]));
 #pragma unroll
-            for (int b = 0; b < NB; ++b) part[b] = 0.0f;
+            for (int b = 0; b < NB; ++b) {
+                rec[b] = xrec + (size_t)(b * C + ci) * REC;
+                const uint4 kx = rec[b][QPC];
+                pa[b] = -__builtin_bit_cast(float, kx.x);
+                xt[b] = __builtin_bit_cast(float, kx.y);
+                pb[b] = 0.0f;
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t sh = ww[j] >> 8;
+                if constexpr (BITS == 4) {
+                    // (q0,q4) and (q2,q6) unpack as 1024+q, (q1,q5) and (q3,q7)
+                    // as 1024+16q: one AND-OR each, one shift per word.
+                    const h2_t q04 = as_h2((ww[j] & m_lo) | MAGIC);
+                    const h2_t q15 = as_h2((ww[j] & m_hi) | MAGIC);
+                    const h2_t q26 = as_h2((sh & m_lo) | MAGIC);
+                    const h2_t q37 = as_h2((sh & m_hi) | MAGIC);
 #pragma unroll
-                for (int p = 0; p < CG::PAIRS_PER_WORD; ++p) {
-                    const h2_t q = as_h2(code_pair<BITS>(ww[j], p));
+                    for (int b = 0; b < NB; ++b) {
+                        const uint4 xv = rec[b][j];
+                        pa[b] = __builtin_amdgcn_fdot2(q04, as_h2(xv.x), pa[b], false);
+                        pb[b] = __builtin_amdgcn_fdot2(q15, as_h2(xv.y), pb[b], false);
+                        pa[b] = __builtin_amdgcn_fdot2(q26, as_h2(xv.z), pa[b], false);
+                        pb[b] = __builtin_amdgcn_fdot2(q37, as_h2(xv.w), pb[b], false);
+                    }
+                } else {
+                    const h2_t q02 = as_h2((ww[j] & m_lo) | MAGIC);
+                    const h2_t q13 = as_h2((sh & m_lo) | MAGIC);
 #pragma unroll
-                    for (int b = 0; b < NB; ++b)
-                        part[b] = __builtin_amdgcn_fdot2(
-                            q, as_h2(xp[i][b][j * CG::PAIRS_PER_WORD + p]), part[b], false);
+                    for (int b = 0; b < NB; ++b) {
+                        const uint4 xv = rec[b][j >> 1];
+                        pa[b] = __builtin_amdgcn_fdot2(q02, as_h2((j & 1) ? xv.z : xv.x), pa[b], false);
+                        pa[b] = __builtin_amdgcn_fdot2(q13, as_h2((j & 1) ? xv.w : xv.y), pa[b], false);
+                    }
                 }
+            }
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                acc[b] = __builtin_fmaf(s[i], __builtin_fmaf(-zc[i], xsum[i][b], part[b]), acc[b]);
+            for (int b = 0; b < NB; ++b) {
+                float t = pa[b];
+                if constexpr (BITS == 4) t = __builtin_fmaf(pb[b], 0.0625f, t);
+                t = __builtin_fmaf(-sz.y, xt[b], t);
+                acc[b] = __builtin_fmaf(s, t, acc[b]);
+            }
         }
         // ---- reduce over the row's TG threads --------------------------------
         if constexpr (TG <= 64) {
@@ -162,6 +283,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(
                 for (int b = 0; b < NB; ++b)
                     if (b < nb) Y[(b0 + b) * N + n] = float_to_half_bits_rne(acc[b]);
             }
+            wave_lds_sync();
         } else {
             const int wave = tid / 64;       // 0..3
             const int lane = tid % 64;
@@ -184,6 +306,18 @@ __global__ __launch_bounds__(256) void gemv_kernel(
             }
             __syncthreads();
         }
+    };
+
+    // ---- stream rows, two passes per iteration (ping-pong registers) --------
+    const int64_t step = gridDim.x;
+    while (pass < passes) {
+        load_pass(pass + step, wB, sB, zB);
+        compute_pass(pass, wA, sA, zA);
+        pass += step;
+        if (pass >= passes) break;
+        load_pass(pass + step, wA, sA, zA);
+        compute_pass(pass, wB, sB, zB);
+        pass += step;
     }
 }
 
@@ -197,20 +331,30 @@ int pow2_ceil(int64_t v) {
     return p;
 }
 
-// Batch tile NB covers the whole batch up to 8; X registers per thread are
-// CPT*NB*PAIRS words, so CPT shrinks (and TG grows) as NB grows.
+// LDS bytes of X per batch row and chunk: the permuted pairs plus one uint4
+// holding the chunk constants.
+size_t x_lds_per_chunk(int32_t bits) {
+    return ((size_t)(64 / bits) / 4 + 1) * sizeof(uint4);
+}
+
+constexpr size_t kMaxXLds = 64 * 1024;
+
+// Batch tile NB covers the batch up to 8 rows while its X fits in 64 KB of
+// LDS; TG threads per row is the smallest power of two (16..256) that covers
+// a row with at most 4 chunks per thread.
 bool choose(int64_t B, int64_t K, int32_t bits, GemvChoice& ch) {
     const int vals = 128 / bits;
     if (K % vals != 0) return false;
     const int64_t C = K / vals;
     int nb = pow2_ceil(B < 8 ? B : 8);
-    int cptmax = nb >= 4 ? 1 : 4 / nb;
+    while (nb > 1 && (size_t)nb * C * x_lds_per_chunk(bits) > kMaxXLds) nb >>= 1;
+    if ((size_t)nb * C * x_lds_per_chunk(bits) > kMaxXLds) return false;
     int tg = 16;
-    while (tg < 256 && (int64_t)tg * cptmax < C) tg <<= 1;
-    int64_t need = (C + tg - 1) / tg;
+    while (tg < 256 && (int64_t)tg * 4 < C) tg <<= 1;
+    const int64_t need = (C + tg - 1) / tg;
     if (need > 4) return false;
-    int cpt = pow2_ceil(need);
-    while (nb * cpt > 8 && nb > 1) nb >>= 1;
+    const int cpt = pow2_ceil(need);
+    while (nb * cpt > 8 && nb > 1) nb >>= 1;  // bounds the accumulators per thread
     ch.nb = nb;
     ch.tg = tg;
     ch.cpt = cpt;
@@ -222,10 +366,27 @@ hipError_t launch_one(const void* X, const void* codes, const void* scales, cons
                       void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int num_cus,
                       hipStream_t stream) {
     constexpr int RPB = 256 / TG;
+    typedef ChunkGeom<BITS> CG;
+    const int64_t C = K / CG::VALS;
+    const size_t lds = (size_t)NB * C * x_lds_per_chunk(BITS);
+    // Persistent grid: as many blocks as fit on the chip at once, each looping
+    // over row passes, so X is staged once per resident block.
+    // Occupancy depends on the X record size; remember the last answer.
+    static thread_local size_t cached_lds = (size_t)-1;
+    static thread_local int cached_per_cu = 1;
+    if (cached_lds != lds) {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, gemv_kernel<BITS, NB, TG, CPT>, 256, lds) !=
+                hipSuccess || v <= 0)
+            v = 1;
+        cached_lds = lds;
+        cached_per_cu = v;
+    }
+    const int per_cu = cached_per_cu;
     const int64_t passes = (N + RPB - 1) / RPB;
-    const int64_t cap = (int64_t)num_cus * 8;
+    const int64_t cap = (int64_t)num_cus * per_cu;
     const dim3 grid((unsigned)(passes < cap ? passes : cap), (unsigned)((B + NB - 1) / NB));
-    gemv_kernel<BITS, NB, TG, CPT><<<grid, dim3(256), 0, stream>>>(
+    gemv_kernel<BITS, NB, TG, CPT><<<grid, dim3(256), lds, stream>>>(
         static_cast<const uint16_t*>(X), static_cast<const uint4*>(codes),
         static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
         static_cast<uint16_t*>(Y), B, N, K, G);
@@ -265,7 +426,7 @@ hipError_t by_shape(const GemvChoice& ch, const void* X, const void* codes, cons
 
 bool gemv_supports(int64_t K, int32_t bits) {
     GemvChoice ch;
-    return choose(1, K, bits, ch) && choose(8, K, bits, ch);
+    return choose(1, K, bits, ch);
 }
 
 hipError_t launch_gemv(const void* X, const void* codes, const void* scales,
