@@ -85,9 +85,8 @@ wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, i
     if (N == 0) return WQ_OK;
     if (!W || !codes || !scales || !zeros)
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: null pointer");
-    if (!aligned(W, 16) || !aligned(codes, bits == 4 ? 4 : 8) || !aligned(scales, 2) || !aligned(zeros, 2))
-        return fail(WQ_ERR_MISALIGNED, "wq_quantize_pack: W needs 16-byte, codes %lld-byte alignment",
-                    bits == 4 ? 4 : 8);
+    if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
+        return fail(WQ_ERR_MISALIGNED, "wq_quantize_pack: W and codes need 16-byte alignment");
     return check_hip(wq::launch_quantize_pack(W, N, K, group, bits, codes, scales, zeros,
                                               static_cast<hipStream_t>(stream)),
                      "wq_quantize_pack launch");

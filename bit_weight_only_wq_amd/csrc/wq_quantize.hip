@@ -20,34 +20,9 @@ namespace wq {
 
 namespace {
 
-template <int BITS>
-struct Pack8;
-
-template <>
-struct Pack8<4> {
-    typedef uint32_t type;  // 8 nibbles
-    __device__ static type pack(const float* q) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w |= (uint32_t)q[i] << (4 * i);
-        return w;
-    }
-};
-
-template <>
-struct Pack8<8> {
-    typedef uint2 type;  // 8 bytes
-    __device__ static type pack(const float* q) {
-        uint2 w;
-        w.x = (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) | ((uint32_t)q[3] << 24);
-        w.y = (uint32_t)q[4] | ((uint32_t)q[5] << 8) | ((uint32_t)q[6] << 16) | ((uint32_t)q[7] << 24);
-        return w;
-    }
-};
-
-__device__ __forceinline__ void load8(const uint16_t* p, float* x) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+__device__ __forceinline__ void load8(const uint16_t* p, float* x, uint4& raw) {
+    raw = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         x[2 * i] = half_bits_to_float((uint16_t)(w[i] & 0xFFFFu));
@@ -55,9 +30,20 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* x) {
     }
 }
 
+// Min and max of 8 fp16 values on packed halves (exact comparisons).
+__device__ __forceinline__ void minmax8(const uint4& raw, float& mn, float& mx) {
+    const h2_t a = as_h2(raw.x), b = as_h2(raw.y), c = as_h2(raw.z), d = as_h2(raw.w);
+    const h2_t lo = __builtin_elementwise_min(__builtin_elementwise_min(a, b),
+                                              __builtin_elementwise_min(c, d));
+    const h2_t hi = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                              __builtin_elementwise_max(c, d));
+    mn = __builtin_fminf((float)lo.x, (float)lo.y);
+    mx = __builtin_fmaxf((float)hi.x, (float)hi.y);
+}
+
 // Per-group header from the exact min and max.
 struct GroupHeader {
-    float s, rcp, Z;
+    float s, rcp, Z, thr;
     uint16_t sbits, zbits;
 };
 
@@ -70,47 +56,122 @@ __device__ __forceinline__ GroupHeader make_header(float mn, float mx, int M) {
     float k = rne_div_exact(-mn, h.s, h.rcp, -131072.0f, 131072.0f);
     h.zbits = zero_bits_from_int(k);
     h.Z = half_bits_to_float(h.zbits);
+    // |x*rcp - x/s| <= |x/s| * 2^-22 (rcp within 1 ulp, one rounding of the
+    // product).  A fraction |t - rint(t)| at most thr therefore cannot be a tie
+    // or on the wrong side of one; thr keeps a 4x margin on that bound.
+    const float tmax = __builtin_fmaxf(__builtin_fabsf(mn), __builtin_fabsf(mx)) * h.rcp;
+    h.thr = 0.5f - (tmax + 1.0f) * 0x1p-20f;
     return h;
 }
 
+// Codes of 8 values packed into 4 bytes (4-bit, even position in the low
+// nibble) or 8 bytes (8-bit), little-endian.
 template <int BITS>
-__device__ __forceinline__ typename Pack8<BITS>::type encode8(const float* x, const GroupHeader& h) {
+struct Packed8;
+template <>
+struct Packed8<4> {
+    typedef uint32_t type;
+};
+template <>
+struct Packed8<8> {
+    typedef uint2 type;
+};
+
+template <int BITS>
+__device__ __forceinline__ typename Packed8<BITS>::type encode8(const float* x, const GroupHeader& h) {
     constexpr float M = (float)((1 << BITS) - 1);
-    // Outside [-Z-2, M-Z+2] every estimate clamps to code 0 or M anyway.
-    const float lo = -h.Z - 2.0f, hi = M - h.Z + 2.0f;
-    float q[8];
+    // Fast path: rint of the fp32 quotient estimate, exact unless the estimate
+    // falls within the error band around a half-integer.
+    float k[8];
+    bool near = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float k = rne_div_exact(x[i], h.s, h.rcp, lo, hi) + h.Z;
-        q[i] = __builtin_fminf(__builtin_fmaxf(k, 0.0f), M);
+        const float t = x[i] * h.rcp;
+        k[i] = __builtin_rintf(t);
+        near |= __builtin_fabsf(t - k[i]) > h.thr;
     }
-    return Pack8<BITS>::pack(q);
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+        // Rare (wave-uniform) exact path: outside [-Z-2, M-Z+2] every value
+        // clamps to code 0 or M anyway.
+        const float lo = -h.Z - 2.0f, hi = M - h.Z + 2.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) k[i] = rne_div_exact(x[i], h.s, h.rcp, lo, hi);
+    }
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_fmed3f(k[i] + h.Z, 0.0f, M);
+    if constexpr (BITS == 4) {
+        // Bytes (q0,q2,q4,q6) and (q1,q3,q5,q7); byte j = q[2j] | q[2j+1] << 4.
+        uint32_t ev = 0, od = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ev = __builtin_amdgcn_cvt_pk_u8_f32(q[2 * j], j, ev);
+            od = __builtin_amdgcn_cvt_pk_u8_f32(q[2 * j + 1], j, od);
+        }
+        return ev | (od << 4);
+    } else {
+        uint2 w = make_uint2(0u, 0u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w.x = __builtin_amdgcn_cvt_pk_u8_f32(q[j], j, w.x);
+            w.y = __builtin_amdgcn_cvt_pk_u8_f32(q[4 + j], j, w.y);
+        }
+        return w;
+    }
 }
 
-// Groups of G = 8*T values, T lanes per group (T a power of two <= 64).
-// Thread t owns chunk t (values [8t, 8t+8) of the flat array).
-template <int BITS, int T>
+// Store the packed codes of CPL consecutive 8-value chunks with one vector
+// store (4*CPL bytes at 4 bits, 8*CPL bytes at 8 bits).
+template <int BITS, int CPL>
+__device__ __forceinline__ void store_codes(uint8_t* dst, const typename Packed8<BITS>::type* p) {
+    if constexpr (BITS == 4) {
+        if constexpr (CPL == 4) *reinterpret_cast<uint4*>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
+        else if constexpr (CPL == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(p[0], p[1]);
+        else *reinterpret_cast<uint32_t*>(dst) = p[0];
+    } else {
+        if constexpr (CPL == 4) {
+            reinterpret_cast<uint4*>(dst)[0] = make_uint4(p[0].x, p[0].y, p[1].x, p[1].y);
+            reinterpret_cast<uint4*>(dst)[1] = make_uint4(p[2].x, p[2].y, p[3].x, p[3].y);
+        } else if constexpr (CPL == 2) {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(p[0].x, p[0].y, p[1].x, p[1].y);
+        } else {
+            *reinterpret_cast<uint2*>(dst) = p[0];
+        }
+    }
+}
+
+// Groups of G = 8*CPL*T values: T lanes per group (a power of two <= 64), each
+// lane owning CPL consecutive 8-value chunks (lane t of a team holds values
+// [8*CPL*t, 8*CPL*(t+1)) of its group).  Lane u of the grid therefore covers
+// the flat values [8*CPL*u, 8*CPL*(u+1)), the same for W and, packed, codes.
+template <int BITS, int T, int CPL>
 __global__ __launch_bounds__(256) void quantize_team_kernel(
-    const uint16_t* __restrict__ W, typename Pack8<BITS>::type* __restrict__ codes,
-    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t nchunks) {
+    const uint16_t* __restrict__ W, uint8_t* __restrict__ codes,
+    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t nlanes) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool live = t < nchunks;           // teams are all live or all dead
-    const int64_t c = live ? t : nchunks - 1;
-    float x[8];
-    load8(W + c * 8, x);
-    float mn = x[0], mx = x[0];
+    const bool live = t < nlanes;            // teams are all live or all dead
+    const int64_t u = live ? t : nlanes - 1;
+    float x[CPL][8];
+    float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
 #pragma unroll
-    for (int i = 1; i < 8; ++i) {
-        mn = __builtin_fminf(mn, x[i]);
-        mx = __builtin_fmaxf(mx, x[i]);
+    for (int i = 0; i < CPL; ++i) {
+        uint4 raw;
+        load8(W + (u * CPL + i) * 8, x[i], raw);
+        float a, b;
+        minmax8(raw, a, b);
+        mn = __builtin_fminf(mn, a);
+        mx = __builtin_fmaxf(mx, b);
     }
     group_minmax<T>(mn, mx);
     const GroupHeader h = make_header(mn, mx, (1 << BITS) - 1);
     if (!live) return;
-    codes[c] = encode8<BITS>(x, h);
+    typename Packed8<BITS>::type p[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) p[i] = encode8<BITS>(x[i], h);
+    store_codes<BITS, CPL>(codes + u * CPL * BITS, p);
     if ((threadIdx.x & (T - 1)) == 0) {
-        scales[c / T] = h.sbits;
-        zeros[c / T] = h.zbits;
+        scales[u / T] = h.sbits;
+        zeros[u / T] = h.zbits;
     }
 }
 
@@ -118,7 +179,7 @@ __global__ __launch_bounds__(256) void quantize_team_kernel(
 // pass 1 reduces min/max over the group, pass 2 re-reads and encodes.
 template <int BITS>
 __global__ __launch_bounds__(256) void quantize_wave_kernel(
-    const uint16_t* __restrict__ W, typename Pack8<BITS>::type* __restrict__ codes,
+    const uint16_t* __restrict__ W, typename Packed8<BITS>::type* __restrict__ codes,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ngroups,
     int64_t G) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -128,19 +189,19 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
     const int64_t c0 = g * cpg;
     float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
     for (int64_t j = lane; j < cpg; j += kWave) {
-        float x[8];
-        load8(W + (c0 + j) * 8, x);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            mn = __builtin_fminf(mn, x[i]);
-            mx = __builtin_fmaxf(mx, x[i]);
-        }
+        float x[8], a, b;
+        uint4 raw;
+        load8(W + (c0 + j) * 8, x, raw);
+        minmax8(raw, a, b);
+        mn = __builtin_fminf(mn, a);
+        mx = __builtin_fmaxf(mx, b);
     }
     group_minmax<kWave>(mn, mx);
     const GroupHeader h = make_header(mn, mx, (1 << BITS) - 1);
     for (int64_t j = lane; j < cpg; j += kWave) {
         float x[8];
-        load8(W + (c0 + j) * 8, x);
+        uint4 raw;
+        load8(W + (c0 + j) * 8, x, raw);
         codes[c0 + j] = encode8<BITS>(x, h);
     }
     if (lane == 0) {
@@ -149,33 +210,42 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
     }
 }
 
+template <int BITS, int T, int CPL>
+hipError_t launch_team(const uint16_t* w, uint8_t* c, uint16_t* s, uint16_t* z, int64_t nvals,
+                       hipStream_t stream) {
+    const int64_t nlanes = nvals / (8 * CPL);
+    const dim3 grid((unsigned)((nlanes + 255) / 256));
+    quantize_team_kernel<BITS, T, CPL><<<grid, dim3(256), 0, stream>>>(w, c, s, z, nlanes);
+    return hipGetLastError();
+}
+
 template <int BITS>
 hipError_t launch_bits(const void* W, int64_t N, int64_t K, int32_t G, void* codes,
                        void* scales, void* zeros, hipStream_t stream) {
-    typedef typename Pack8<BITS>::type P;
+    typedef typename Packed8<BITS>::type P;
     const uint16_t* w = static_cast<const uint16_t*>(W);
-    P* c = static_cast<P*>(codes);
+    uint8_t* c = static_cast<uint8_t*>(codes);
     uint16_t* s = static_cast<uint16_t*>(scales);
     uint16_t* z = static_cast<uint16_t*>(zeros);
-    const int64_t nchunks = N * K / 8;
-    const int64_t ngroups = N * K / G;
-    const int T = G / 8;
-    const dim3 block(256);
-    const dim3 team_grid((unsigned)((nchunks + 255) / 256));
-    switch ((G <= 512 && (T & (T - 1)) == 0) ? T : 0) {
-        case 1: quantize_team_kernel<BITS, 1><<<team_grid, block, 0, stream>>>(w, c, s, z, nchunks); break;
-        case 2: quantize_team_kernel<BITS, 2><<<team_grid, block, 0, stream>>>(w, c, s, z, nchunks); break;
-        case 4: quantize_team_kernel<BITS, 4><<<team_grid, block, 0, stream>>>(w, c, s, z, nchunks); break;
-        case 8: quantize_team_kernel<BITS, 8><<<team_grid, block, 0, stream>>>(w, c, s, z, nchunks); break;
-        case 16: quantize_team_kernel<BITS, 16><<<team_grid, block, 0, stream>>>(w, c, s, z, nchunks); break;
-        case 32: quantize_team_kernel<BITS, 32><<<team_grid, block, 0, stream>>>(w, c, s, z, nchunks); break;
-        case 64: quantize_team_kernel<BITS, 64><<<team_grid, block, 0, stream>>>(w, c, s, z, nchunks); break;
+    const int64_t nv = N * K;
+    switch (G) {
+        case 8: return launch_team<BITS, 1, 1>(w, c, s, z, nv, stream);
+        case 16: return launch_team<BITS, 1, 2>(w, c, s, z, nv, stream);
+        case 32: return launch_team<BITS, 1, 4>(w, c, s, z, nv, stream);
+        case 64: return launch_team<BITS, 2, 4>(w, c, s, z, nv, stream);
+        case 128: return launch_team<BITS, 4, 4>(w, c, s, z, nv, stream);
+        case 256: return launch_team<BITS, 8, 4>(w, c, s, z, nv, stream);
+        case 512: return launch_team<BITS, 16, 4>(w, c, s, z, nv, stream);
+        case 1024: return launch_team<BITS, 32, 4>(w, c, s, z, nv, stream);
+        case 2048: return launch_team<BITS, 64, 4>(w, c, s, z, nv, stream);
         default: {
+            const int64_t ngroups = nv / G;
             const dim3 grid((unsigned)((ngroups + 3) / 4));
-            quantize_wave_kernel<BITS><<<grid, block, 0, stream>>>(w, c, s, z, ngroups, G);
+            quantize_wave_kernel<BITS><<<grid, dim3(256), 0, stream>>>(
+                w, static_cast<P*>(codes), s, z, ngroups, G);
+            return hipGetLastError();
         }
     }
-    return hipGetLastError();
 }
 
 }  // namespace

@@ -79,8 +79,8 @@ typedef enum {
  * scales  fp16 [N, K/group]           output (group index fastest)
  * zeros   fp16 [N, K/group]           output
  * N >= 0 (N == 0 is a no-op), K >= 1, group >= 1, K % group == 0.
- * bits in {4, 8}; group % 8 == 0; codes 4-byte aligned (bits 4) or
- * 8-byte aligned (bits 8); scales/zeros 2-byte aligned.
+ * bits in {4, 8}; group % 8 == 0; codes 16-byte aligned; scales/zeros
+ * 2-byte aligned.
  */
 wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
                            int32_t bits, void* codes, void* scales, void* zeros,

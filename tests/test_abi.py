@@ -92,6 +92,7 @@ def test_quantize_validation_errors():
     assert _quant(W=0) == _lib.WQ_ERR_INVALID_ARG
     assert _quant(W=FAKE + 2) == _lib.WQ_ERR_MISALIGNED
     assert _quant(bits=8, C=FAKE + 4) == _lib.WQ_ERR_MISALIGNED
+    assert _quant(bits=4, C=FAKE + 8) == _lib.WQ_ERR_MISALIGNED
 
 
 def test_binding_raises_on_error():
