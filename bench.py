@@ -35,7 +35,8 @@ if ROOT not in sys.path:
 METRIC = "achieved HBM GB/s (% of peak) for int4 group-quant decode GEMM at B=1..64"
 WORKLOAD = "mlp70b_up_k8192_n28672_g128"
 POOL_BYTES = 1 << 30          # packed-weight pool, >= 4x the 256 MB Infinity Cache
-CPU_SAMPLE_ROWS = 16384       # rows of the workload the oracle processes
+CPU_SAMPLE_ROWS = 28672       # rows of the workload the oracle processes (all of them)
+CPU_MIN_SECONDS = 10.0        # repeat the oracle's step until this much CPU time
 
 
 def parse():
@@ -47,6 +48,11 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--sweep", action="store_true", help="batch sweep on K=N=8192 (table)")
     p.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="after timing, copy this many MiB device-to-device once (a "
+                        "known-size kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn two rocprofv3 --pmc counter CSVs into profiles/traffic_*.txt")
     return p.parse_args()
 
 
@@ -67,7 +73,6 @@ def kernel_entry(name, nbytes, flops, ms_list, bound="hbm"):
 def read_traffic(kernel_tag):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel sources (else None)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
     if not os.path.exists(path):
         return None
@@ -76,16 +81,62 @@ def read_traffic(kernel_tag):
         if ":" in line and not line.startswith("#"):
             k, _, v = line.partition(":")
             vals[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "bit_weight_only_wq_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(src)):
-        h.update(open(os.path.join(src, f), "rb").read())
-    if vals.get("csrc_sha256") != h.hexdigest():
+    if vals.get("csrc_sha256") != csrc_sha256():
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def csrc_sha256():
+    import hashlib
+    src = os.path.join(ROOT, "bit_weight_only_wq_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(src)):
+        h.update(open(os.path.join(src, f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_from(fetch_csv, write_csv, copy_mib=256):
+    """Per-launch HBM bytes of each wq kernel from two rocprofv3 --pmc CSVs.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
+    counter reads for the calibration copy of copy_mib MiB (read once, written
+    once): factor = known bytes / counted bytes.
+    """
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals[(r["Kernel_Name"], r["Grid_Size"])].append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    known = copy_mib * (1 << 20)
+
+    def calib(vals):
+        cands = [(k, sum(v) / len(v)) for k, v in vals.items()
+                 if "wq::" not in k[0] and sum(v) / len(v) > 0.5 * known]
+        if not cands:
+            return None
+        k, v = max(cands, key=lambda kv: kv[1])
+        return known / v
+
+    fr, wr = calib(fetch), calib(write)
+    out = {}
+    for key in set(fetch) | set(write):
+        if "wq::" not in key[0]:
+            continue
+        f = sum(fetch.get(key, [0])) / max(1, len(fetch.get(key, [0])))
+        w = sum(write.get(key, [0])) / max(1, len(write.get(key, [0])))
+        out[key] = (f * (fr or 1.0), w * (wr or 1.0))
+    return out, fr, wr
 
 
 def cpu_baseline(name, batches):
@@ -98,17 +149,22 @@ def cpu_baseline(name, batches):
     W, X = wq_inputs.workload_arrays(name, rows=rows)
     K, G, bits = cfg["K"], cfg["group"], cfg["bits"]
     oracle.build(force=False)
+    reps = 0
     t0 = time.perf_counter()
-    c, s, z = oracle.quantize(W, G, bits)
-    for B in batches:
-        oracle.gemm(X[:B], c, s, z, rows, K, G, bits)
-    dt = time.perf_counter() - t0
+    while True:
+        c, s, z = oracle.quantize(W, G, bits)
+        for B in batches:
+            oracle.gemm(X[:B], c, s, z, rows, K, G, bits)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_MIN_SECONDS:
+            break
     nbytes = rl.quantize_bytes(rows, K, G, bits) + sum(rl.gemm_bytes(B, rows, K, G, bits)
                                                       for B in batches)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"first {rows} of {cfg['N']} rows of {name}: exact quantize/pack + "
-                      f"double-precision GEMM at B={','.join(map(str, batches))}"}
+    return {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{rows} of {cfg['N']} rows of {name}, {reps} pass(es): exact "
+                      f"quantize/pack + double-precision GEMM at B={','.join(map(str, batches))}"}
 
 
 def run_step_bench(args):
@@ -282,6 +338,12 @@ def run_sweep(args):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        out, fr, wr = traffic_from(*args.traffic_from)
+        for (name, grid), (f, w) in sorted(out.items()):
+            print(f"{name[:90]} grid={grid}: fetch {f / 1e6:.2f} MB, write {w / 1e6:.2f} MB "
+                  f"(copy scale fetch {fr}, write {wr})")
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -290,6 +352,16 @@ def main():
         run_sweep(args)
         return
     out, batches = run_step_bench(args)
+    if args.copy_calibration_mib:
+        import torch
+        # An elementwise kernel (not a DMA copy, which the counters do not see)
+        # that reads and writes exactly copy_calibration_mib MiB each.
+        a = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda:0")
+        a.fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.mul(a, 3, out=b)
+        torch.cuda.synchronize()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.workload, batches)
     print(json.dumps(out), flush=True)

@@ -25,8 +25,11 @@
  *
  * Conventions shared by every entry point:
  *   - All array pointers are DEVICE pointers to row-major, contiguous buffers
- *     that the caller allocates, owns and frees.  The library allocates
- *     nothing and keeps no state besides a cached device property.
+ *     that the caller allocates, owns and frees.  The library keeps no state
+ *     besides cached device properties.  The only memory it allocates is the
+ *     fp32 split-K workspace of the MFMA path (B * N * 4 bytes per K split),
+ *     taken and released in stream order (hipMallocAsync / hipFreeAsync on
+ *     `stream`); a failure there is reported as WQ_ERR_HIP.
  *   - `stream` is a hipStream_t (NULL means the default stream).  Work is
  *     enqueued on it and the call returns at once; the library never
  *     synchronizes.  Buffers must stay alive until the stream has run the work.
