@@ -52,7 +52,13 @@ def parse():
                    help="after timing, copy this many MiB device-to-device once (a "
                         "known-size kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                   help="turn two rocprofv3 --pmc counter CSVs into profiles/traffic_*.txt")
+                   help="turn two rocprofv3 --pmc counter CSVs into profiles/traffic_*.txt "
+                        "(with --copy-calibration-mib as used in those runs)")
+    p.add_argument("--traffic-match", nargs=2, action="append", metavar=("TAG_SUFFIX", "NAME_FRAGMENT"),
+                   help="write the summary of wq_gemm_b<TAG_SUFFIX> (or wq_quantize_pack) from "
+                        "the kernel whose name holds NAME_FRAGMENT")
+    p.add_argument("--fetch-cmd", default="", help="command line of the FETCH_SIZE run (recorded)")
+    p.add_argument("--write-cmd", default="", help="command line of the WRITE_SIZE run (recorded)")
     return p.parse_args()
 
 
@@ -70,10 +76,35 @@ def kernel_entry(name, nbytes, flops, ms_list, bound="hbm"):
     return e
 
 
+# Sources each kernel family is built from: a traffic summary stays valid only
+# while these files are unchanged.
+KERNEL_SOURCES = {
+    "gemv": ["wq_gemv.hip", "wq_device.h"],
+    "mfma": ["wq_gemm_mfma.hip", "wq_device.h"],
+    "quantize": ["wq_quantize.hip", "wq_device.h"],
+}
+# rocprofv3 kernel-name fragment of each family.
+KERNEL_NAMES = {"gemv": "gemv_kernel", "mfma": "gemm_mfma_kernel", "quantize": "quantize_"}
+
+
+def sources_sha256(files):
+    import hashlib
+    src = os.path.join(ROOT, "bit_weight_only_wq_amd", "csrc")
+    h = hashlib.sha256()
+    for f in files:
+        h.update(f.encode() + b"\0")
+        h.update(open(os.path.join(src, f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_path(kernel_tag):
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
+
+
 def read_traffic(kernel_tag):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
+    was taken on the current sources of that kernel (else None)."""
+    path = traffic_path(kernel_tag)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -81,7 +112,8 @@ def read_traffic(kernel_tag):
         if ":" in line and not line.startswith("#"):
             k, _, v = line.partition(":")
             vals[k.strip()] = v.strip()
-    if vals.get("csrc_sha256") != csrc_sha256():
+    files = vals.get("sources", "").split()
+    if not files or vals.get("sources_sha256") != sources_sha256(files):
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
@@ -89,21 +121,12 @@ def read_traffic(kernel_tag):
         return None
 
 
-def csrc_sha256():
-    import hashlib
-    src = os.path.join(ROOT, "bit_weight_only_wq_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(src)):
-        h.update(open(os.path.join(src, f), "rb").read())
-    return h.hexdigest()
-
-
-def traffic_from(fetch_csv, write_csv, copy_mib=256):
+def traffic_from(fetch_csv, write_csv, copy_mib):
     """Per-launch HBM bytes of each wq kernel from two rocprofv3 --pmc CSVs.
 
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
-    counter reads for the calibration copy of copy_mib MiB (read once, written
-    once): factor = known bytes / counted bytes.
+    counter reads for the calibration kernel, an elementwise pass that reads
+    and writes copy_mib MiB: factor = known bytes / counted bytes.
     """
     import csv
     from collections import defaultdict
@@ -111,32 +134,70 @@ def traffic_from(fetch_csv, write_csv, copy_mib=256):
     def per_kernel(path, counter):
         vals = defaultdict(list)
         for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
-            vals[(r["Kernel_Name"], r["Grid_Size"])].append(float(r["Counter_Value"]) * 1024.0)
-        return vals
+            if r["Counter_Name"] == counter:
+                vals[(r["Kernel_Name"], r["Grid_Size"])].append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in vals.items()}
 
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
     write = per_kernel(write_csv, "WRITE_SIZE")
     known = copy_mib * (1 << 20)
 
     def calib(vals):
-        cands = [(k, sum(v) / len(v)) for k, v in vals.items()
-                 if "wq::" not in k[0] and sum(v) / len(v) > 0.5 * known]
-        if not cands:
-            return None
-        k, v = max(cands, key=lambda kv: kv[1])
-        return known / v
+        # The calibration kernel: torch's elementwise multiply (not a fill).
+        cands = [v for k, v in vals.items() if "wq::" not in k[0] and "Unary" in k[0]]
+        return known / max(cands) if cands and max(cands) > 0 else None
 
     fr, wr = calib(fetch), calib(write)
+    if fr is None or wr is None:
+        raise SystemExit("calibration kernel not found in the counter CSVs")
     out = {}
     for key in set(fetch) | set(write):
-        if "wq::" not in key[0]:
-            continue
-        f = sum(fetch.get(key, [0])) / max(1, len(fetch.get(key, [0])))
-        w = sum(write.get(key, [0])) / max(1, len(write.get(key, [0])))
-        out[key] = (f * (fr or 1.0), w * (wr or 1.0))
+        if "wq::" in key[0]:
+            out[key] = (fetch.get(key, 0.0) * fr, write.get(key, 0.0) * wr)
     return out, fr, wr
+
+
+def write_traffic_summaries(args):
+    """Print every wq kernel's calibrated traffic and write one summary file
+    per kernel family and grid size under profiles/."""
+    import bit_weight_only_wq_amd.roofline as rl
+    import wq_inputs
+    out, fr, wr = traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_calibration_mib)
+    cfg = wq_inputs.WORKLOADS[args.workload]
+    N, K, G, bits = cfg["N"], cfg["K"], cfg["group"], cfg["bits"]
+    batches = [b for b in cfg["batches"] if b <= 64] or [1]
+    for (name, grid), (f, w) in sorted(out.items()):
+        print(f"{name[:100]} grid={grid}: fetch {f / 1e6:.2f} MB, write {w / 1e6:.2f} MB")
+    for fam, frag in KERNEL_NAMES.items():
+        hits = [(k, v) for k, v in out.items() if frag in k[0]]
+        if fam == "quantize":
+            tags = [("wq_quantize_pack", rl.quantize_bytes(N, K, G, bits))]
+        else:
+            tags = [(f"wq_gemm_b{B}", rl.gemm_bytes(B, N, K, G, bits)) for B in batches]
+        for tag, algo in tags:
+            # A family's launches at one batch size share one kernel instance;
+            # match the summary to a batch by the kernel name's batch tile.
+            for (name, grid), (f, w) in hits:
+                if not args.traffic_match or not any(m in name and tag.endswith(t)
+                                                     for t, m in args.traffic_match):
+                    continue
+                path = traffic_path(f"{tag}_{args.workload}")
+                os.makedirs(os.path.dirname(path), exist_ok=True)
+                with open(path, "w") as fh:
+                    fh.write(f"# HBM traffic per launch of {tag} on {args.workload}\n")
+                    fh.write(f"# kernel: {name}\n")
+                    fh.write(f"# fetch: {args.fetch_cmd}\n# write: {args.write_cmd}\n")
+                    fh.write("# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over launches) "
+                             "scaled by known/counted bytes of a torch elementwise multiply "
+                             f"over {args.copy_calibration_mib} MiB\n")
+                    fh.write(f"fetch_scale: {fr:.6f}\nwrite_scale: {wr:.6f}\n")
+                    fh.write(f"fetch_bytes_per_launch: {f:.0f}\nwrite_bytes_per_launch: {w:.0f}\n")
+                    fh.write(f"hbm_bytes_per_launch: {f + w:.0f}\n")
+                    fh.write(f"algorithmic_bytes_per_launch: {algo}\n")
+                    fh.write(f"traffic_over_algorithmic: {(f + w) / algo:.4f}\n")
+                    fh.write(f"sources: {' '.join(KERNEL_SOURCES[fam])}\n")
+                    fh.write(f"sources_sha256: {sources_sha256(KERNEL_SOURCES[fam])}\n")
+                print("wrote", os.path.relpath(path, ROOT))
 
 
 def cpu_baseline(name, batches):
@@ -201,58 +262,69 @@ def run_step_bench(args):
     w_ptrs = [w.data_ptr() for w in Wd]
     xy = {B: (Xb[B].data_ptr(), Yb[B].data_ptr()) for B in batches}
 
-    def step(i, evs=None):
-        # Products first, each on its own pool slot; then the quantizer writes a
-        # slot that is next read two steps later (>1 GB of traffic in between).
-        if evs is not None:
-            evs[0].record(stream)
-        for j, B in enumerate(batches):
-            c, s, z = slot_ptrs[(nb * i + j) % P]
-            st = lib.wq_gemm_ex(xy[B][0], c, s, z, xy[B][1], B, K, N, G, bits, path_id, hs)
-            if st:
-                wq.check(st, "wq_gemm")
-            if evs is not None:
-                evs[j + 1].record(stream)
-        c, s, z = slot_ptrs[(nb * i + 2 * nb + 1) % P]
+    def gemm(j, B, slot):
+        c, s, z = slot_ptrs[slot % P]
+        st = lib.wq_gemm_ex(xy[B][0], c, s, z, xy[B][1], B, K, N, G, bits, path_id, hs)
+        if st:
+            wq.check(st, "wq_gemm")
+
+    def quant(i, slot):
+        c, s, z = slot_ptrs[slot % P]
         st = lib.wq_quantize_pack(w_ptrs[i % 2], N, K, G, bits, c, s, z, hs)
         if st:
             wq.check(st, "wq_quantize_pack")
-        if evs is not None:
-            evs[nb + 1].record(stream)
+
+    def step(i):
+        # Products first, each on its own pool slot; then the quantizer writes a
+        # slot that is next read two steps later (>1 GB of traffic in between).
+        for j, B in enumerate(batches):
+            gemm(j, B, nb * i + j)
+        quant(i, nb * i + 2 * nb + 1)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nb + 2)] for _ in range(args.steps)]
+    # Timed region 1: whole steps back to back, no events inside.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
 
-    per = {B: [] for B in batches}
-    per_q = []
-    for e in evs:
-        for j, B in enumerate(batches):
-            per[B].append(e[j].elapsed_time(e[j + 1]))
-        per_q.append(e[nb].elapsed_time(e[nb + 1]))
+    # Timed region 2: each kernel of the step launched `steps` times back to
+    # back (every launch on another pool slot), bracketed by one pair of events
+    # on the stream the library launches on; average duration per launch.
+    def burst(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        fn(0)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i + 1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    per = {B: burst(lambda i, j=j, B=B: gemm(j, B, i)) for j, B in enumerate(batches)}
+    per_q = burst(lambda i: quant(i, i + nb))
 
     step_bytes = rl.quantize_bytes(N, K, G, bits) + sum(rl.gemm_bytes(B, N, K, G, bits)
                                                        for B in batches)
     kernels = {}
     for B in batches:
         kernels[f"wq_gemm_B{B}"] = kernel_entry(
-            f"wq_gemm B={B}", rl.gemm_bytes(B, N, K, G, bits), rl.gemm_flops(B, N, K), per[B])
+            f"wq_gemm B={B}", rl.gemm_bytes(B, N, K, G, bits), rl.gemm_flops(B, N, K), [per[B]])
     kernels["wq_quantize_pack"] = kernel_entry(
-        "wq_quantize_pack", rl.quantize_bytes(N, K, G, bits), 0, per_q)
+        "wq_quantize_pack", rl.quantize_bytes(N, K, G, bits), 0, [per_q])
 
     head = kernels[f"wq_gemm_B{batches[0]}"]
     traffic = read_traffic(f"wq_gemm_b{batches[0]}_{args.workload}")
@@ -339,10 +411,7 @@ def run_sweep(args):
 def main():
     args = parse()
     if args.traffic_from:
-        out, fr, wr = traffic_from(*args.traffic_from)
-        for (name, grid), (f, w) in sorted(out.items()):
-            print(f"{name[:90]} grid={grid}: fetch {f / 1e6:.2f} MB, write {w / 1e6:.2f} MB "
-                  f"(copy scale fetch {fr}, write {wr})")
+        write_traffic_summaries(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
