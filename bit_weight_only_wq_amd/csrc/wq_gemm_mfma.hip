@@ -319,8 +319,8 @@ hipError_t launch_bt(const void* X, const void* codes, const void* scales, const
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((B + BT - 1) / BT), (unsigned)splits);
     float* part = nullptr;
     if (splits > 1) {
-        hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part),
-                                      (size_t)splits * B * N * sizeof(float), stream);
+        uint32_t* unused = nullptr;
+        hipError_t e = workspace_get(stream, 0, (size_t)splits * B * N * sizeof(float), &unused, &part);
         if (e != hipSuccess) return e;
     }
     gemm_mfma_kernel<BITS, BT, KS><<<grid, dim3(256), 0, stream>>>(
@@ -328,15 +328,11 @@ hipError_t launch_bt(const void* X, const void* codes, const void* scales, const
         static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
         static_cast<uint16_t*>(Y), part, B, N, K, G, sps);
     hipError_t e = hipGetLastError();
-    if (splits > 1) {
-        if (e == hipSuccess) {
-            const int64_t count = B * N;
-            split_reduce_kernel<<<dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream>>>(
-                part, static_cast<uint16_t*>(Y), count, (int)splits);
-            e = hipGetLastError();
-        }
-        hipError_t f = hipFreeAsync(part, stream);
-        if (e == hipSuccess) e = f;
+    if (splits > 1 && e == hipSuccess) {
+        const int64_t count = B * N;
+        split_reduce_kernel<<<dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream>>>(
+            part, static_cast<uint16_t*>(Y), count, (int)splits);
+        e = hipGetLastError();
     }
     return e;
 }
@@ -361,6 +357,8 @@ bool mfma_supports(int64_t K, int32_t group, int32_t bits) {
 hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales,
                             const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                             int32_t group, int32_t bits, int num_cus, hipStream_t stream) {
+    if (xr_supports(B, K, group, bits))
+        return launch_gemm_xr(X, codes, scales, zeros, Y, B, K, N, group, bits, num_cus, stream);
     if (bits == 4) return launch_bits<4>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
     return launch_bits<8>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
 }

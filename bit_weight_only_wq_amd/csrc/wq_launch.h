@@ -17,9 +17,21 @@ hipError_t launch_gemv(const void* X, const void* codes, const void* scales,
                        const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                        int32_t group, int32_t bits, int num_cus, hipStream_t stream);
 
+// Matrix-core family: the X-resident kernel for B <= 16 (xr_*), the tiled
+// kernel beyond.
+bool xr_supports(int64_t B, int64_t K, int32_t group, int32_t bits);
+hipError_t launch_gemm_xr(const void* X, const void* codes, const void* scales,
+                          const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
+                          int32_t group, int32_t bits, int num_cus, hipStream_t stream);
 bool mfma_supports(int64_t K, int32_t group, int32_t bits);
 hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales,
                             const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                             int32_t group, int32_t bits, int num_cus, hipStream_t stream);
+
+// Split-K workspace of the calling device and `stream`: counter_words zeroed
+// 32-bit counters (a kernel that uses them leaves them at zero) and part_bytes
+// of fp32 partials, reused by later calls on the same stream.
+hipError_t workspace_get(hipStream_t stream, size_t counter_words, size_t part_bytes,
+                         uint32_t** counters, float** part);
 
 }  // namespace wq

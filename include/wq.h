@@ -25,11 +25,14 @@
  *
  * Conventions shared by every entry point:
  *   - All array pointers are DEVICE pointers to row-major, contiguous buffers
- *     that the caller allocates, owns and frees.  The library keeps no state
- *     besides cached device properties.  The only memory it allocates is the
- *     fp32 split-K workspace of the MFMA path (B * N * 4 bytes per K split),
- *     taken and released in stream order (hipMallocAsync / hipFreeAsync on
- *     `stream`); a failure there is reported as WQ_ERR_HIP.
+ *     that the caller allocates, owns and frees.  The only memory the library
+ *     allocates itself is the fp32 split-K workspace of the MFMA path
+ *     (B * N * 4 bytes per K split): one buffer per (device, stream), taken in
+ *     stream order (hipMallocAsync on `stream`) the first time a call on that
+ *     stream needs it, grown the same way when a later call needs more, and
+ *     kept for reuse until the process ends.  Calls on one stream reuse it in
+ *     stream order; calls on different streams never share it.  A failure
+ *     there is reported as WQ_ERR_HIP.
  *   - `stream` is a hipStream_t (NULL means the default stream).  Work is
  *     enqueued on it and the call returns at once; the library never
  *     synchronizes.  Buffers must stay alive until the stream has run the work.
