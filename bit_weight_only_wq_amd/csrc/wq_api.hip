@@ -67,7 +67,9 @@ int64_t wq_num_groups(int64_t N, int64_t K, int32_t group) {
     return N * (K / group);
 }
 
-int32_t wq_gemv_max_batch(void) { return 4; }
+// Measured crossover on MI355X: the GEMV path wins at B <= 2, the matrix-core
+// kernels from B = 3 on.
+int32_t wq_gemv_max_batch(void) { return 2; }
 
 wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, int32_t bits,
                            void* codes, void* scales, void* zeros, void* stream) {
