@@ -81,10 +81,12 @@ def kernel_entry(name, nbytes, flops, ms_list, bound="hbm"):
 KERNEL_SOURCES = {
     "gemv": ["wq_gemv.hip", "wq_device.h"],
     "mfma": ["wq_gemm_mfma.hip", "wq_device.h"],
+    "xr": ["wq_gemm_xr.hip", "wq_device.h"],
     "quantize": ["wq_quantize.hip", "wq_device.h"],
 }
 # rocprofv3 kernel-name fragment of each family.
-KERNEL_NAMES = {"gemv": "gemv_kernel", "mfma": "gemm_mfma_kernel", "quantize": "quantize_"}
+KERNEL_NAMES = {"gemv": "gemv_kernel", "mfma": "gemm_mfma_kernel", "xr": "gemm_xr_kernel",
+                "quantize": "quantize_"}
 
 
 def sources_sha256(files):
