@@ -1,23 +1,29 @@
-// Skinny GEMM on the matrix cores (gfx950 MFMA) for batches past the GEMV regime:
+// Tiled product on the matrix cores (gfx950 MFMA) for batches past 16:
 // Y[B,N] = X[B,K] * dequant(W)[N,K]^T with fp16 operands and fp32 accumulation.
 //
 // Once 2B/w approaches the ridge ("Quantization & inference optimisation",
 // "Bandwidth, not compute") the product is a real dense contraction, so it
-// runs on v_mfma_f32_16x16x32_f16:
-//   - a block owns 64 weight rows (4 waves x 16 rows) and BT batch columns;
-//   - K is walked in stages of KS values; within a stage every lane streams one
-//     128-bit code chunk per 128-k round of its row (4 lanes x 16 bytes = 64
-//     contiguous bytes of each row per round), prefetched one stage ahead, and
-//     turns it in registers into A operands holding 1024 + q exactly in fp16;
-//   - the stage's X tile [BT x KS] is staged in LDS by the whole block
-//     (128-bit loads issued a stage ahead), permuted into the order the codes
-//     unpack in, with its per-round column sums; one barrier per stage;
-//   - the group header is applied per 128-k round and accumulator through
-//       sum_k (q - z) s x = s * (sum_k (1024 + q) x - (1024 + z) sum_k x)
-//     ("the kernel reconstructs an approximate float from the integer and the
-//     endpoints as it reads", "Quantization"), so the dequantized weight is
-//     never rounded to fp16;
-//   - per-row scales and zero points of the stage are staged in LDS as floats.
+// runs on v_mfma_f32_16x16x32_f16 with X as the A operand (16 batch rows) and
+// the weights as the B operand (16 weight rows):
+//   - a block owns 64*RB weight rows (4 waves x RB tiles of 16 rows) and BT
+//     batch columns and walks K in stages of KS values; a wave's RB row tiles
+//     share every X operand it reads from LDS;
+//   - every lane streams one 128-bit code chunk per 128-k round of its weight
+//     row (4 lanes x 16 bytes = 64 contiguous bytes of the row per round),
+//     two stages ahead in a ring of registers;
+//   - the stage's X tile [BT x KS] is staged in LDS by the whole block (loads
+//     issued a stage ahead), permuted into the order the codes unpack in; the
+//     stage's group headers of the block's 64 rows go to LDS beside it; one
+//     barrier per stage;
+//   - each chunk is dequantized in registers ("the kernel reconstructs an
+//     approximate float from the integer and the endpoints as it reads",
+//     "Quantization") to fp16 (q - z) * s / 2 and reused for all BT columns:
+//       (w & 0x000F000F) | 0x60006000 = (512 + q0/2, 512 + q4/2), exact
+//       (w & 0x00F000F0) | 0x50005000 = ( 32 + q1/2,  32 + q5/2), exact
+//     minus (512 + z/2) or (32 + z/2), times s, rounded once; the factor 1/2
+//     keeps every operand finite for any fp16 weights and is undone on the
+//     fp32 result.  The k order of an operand is (0,4,1,5,2,6,3,7) within each
+//     8 k (8-bit codes: (0,2,1,3) within each 4 k), and X is permuted to match.
 // Requires G % KR == 0 (KR = 128 k for 4-bit, 64 k for 8-bit).
 #include "wq_device.h"
 #include "wq_launch.h"
@@ -53,15 +59,6 @@ __device__ __forceinline__ uint4 permute8(uint4 in) {
     return o;
 }
 
-// Sum of 8 fp16 values in fp32 (products with 1.0 are exact).
-__device__ __forceinline__ float sum8(uint4 v) {
-    const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-    float s = __builtin_amdgcn_fdot2(as_h2(v.x), one, 0.0f, false);
-    s = __builtin_amdgcn_fdot2(as_h2(v.y), one, s, false);
-    s = __builtin_amdgcn_fdot2(as_h2(v.z), one, s, false);
-    return __builtin_amdgcn_fdot2(as_h2(v.w), one, s, false);
-}
-
 // A 32-bit constant held in a VGPR, so that each unpack step is one
 // v_and_or_b32 (gfx9 VOP3 instructions take no literal operand).
 __device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
@@ -70,82 +67,98 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
     return r;
 }
 
-// A operand of k-step j from a lane's 16-byte chunk: fp16 pairs 1024 + q.
+struct DqConsts {
+    uint32_t m_lo, m_hi, g_lo, g_hi;  // nibble/byte masks and exponent patterns
+};
+
+// B operand of k-step j of one lane's chunk: (q - z) * s / 2 in fp16, with
+// nz = (512 + z/2, 32 + z/2) and ss = (s, s).
 template <int BITS>
-__device__ __forceinline__ h8_t a_operand(const uint4& cw, int j, uint32_t mask) {
-    constexpr uint32_t MAGIC = 0x64006400u;
-    uint4 a;
+__device__ __forceinline__ h8_t dequant(const uint4& cw, int j, const DqConsts& c, h2_t nz, h2_t ss) {
+    const h2_t na = {nz.x, nz.x};
+    h2_t p0, p1, p2, p3;
     if constexpr (BITS == 4) {
+        const h2_t nb = {nz.y, nz.y};
         const uint32_t w = j == 0 ? cw.x : j == 1 ? cw.y : j == 2 ? cw.z : cw.w;
-        a.x = (w & mask) | MAGIC;
-        a.y = ((w >> 4) & mask) | MAGIC;
-        a.z = ((w >> 8) & mask) | MAGIC;
-        a.w = ((w >> 12) & mask) | MAGIC;
+        const uint32_t w8 = w >> 8;
+        p0 = (as_h2((w & c.m_lo) | c.g_lo) - na) * ss;
+        p1 = (as_h2((w & c.m_hi) | c.g_hi) - nb) * ss;
+        p2 = (as_h2((w8 & c.m_lo) | c.g_lo) - na) * ss;
+        p3 = (as_h2((w8 & c.m_hi) | c.g_hi) - nb) * ss;
     } else {
         const uint32_t w0 = j == 0 ? cw.x : cw.z;
         const uint32_t w1 = j == 0 ? cw.y : cw.w;
-        a.x = (w0 & mask) | MAGIC;
-        a.y = ((w0 >> 8) & mask) | MAGIC;
-        a.z = (w1 & mask) | MAGIC;
-        a.w = ((w1 >> 8) & mask) | MAGIC;
+        p0 = (as_h2((w0 & c.m_lo) | c.g_lo) - na) * ss;
+        p1 = (as_h2(((w0 >> 8) & c.m_lo) | c.g_lo) - na) * ss;
+        p2 = (as_h2((w1 & c.m_lo) | c.g_lo) - na) * ss;
+        p3 = (as_h2(((w1 >> 8) & c.m_lo) | c.g_lo) - na) * ss;
     }
+    const uint4 a = {as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
     return __builtin_bit_cast(h8_t, a);
 }
 
-// Grid: x = 64-row tiles, y = BT-column tiles, z = K splits.  Split z covers
-// stages [z*SPS, (z+1)*SPS); with one split the block writes Y (fp16), with
+// Grid: x = (64*RB)-row tiles, y = BT-column tiles, z = K splits.  Split z covers
+// stages [z*SPS, (z+1)*SPS) (SPS a multiple of 8); with one split the block writes Y (fp16), with
 // several it writes fp32 partials part[z][b][n] that split_reduce_kernel sums
 // in split order (deterministic).
-template <int BITS, int BT, int KS>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(
+template <int BITS, int BT, int KS, int RB, bool HV>
+__global__ __launch_bounds__(256, (BT == 64 && RB == 2) ? 3 : 1) void gemm_mfma_kernel(
     const uint16_t* __restrict__ X, const uint4* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, float* __restrict__ part, int64_t B, int64_t N, int64_t K,
     int32_t G, int64_t SPS) {
     typedef MfmaGeom<BITS> MG;
-    constexpr int NCB = BT / 16;                      // 16-column blocks
+    constexpr int NCB = BT / 16;                      // 16-column (batch) blocks
     constexpr int RPS = KS / MG::KR;                  // rounds per stage
     constexpr int XROW = KS + 8;                      // padded LDS row (halfs)
     constexpr int SEGS = KS / 8;                      // 16-byte X vectors per column
-    constexpr int SEGR = MG::KR / 8;                  // ... per column and round
     constexpr int NVEC = BT * SEGS;                   // X vectors per stage
     constexpr int VPT = NVEC >= 256 ? NVEC / 256 : 1; // X vectors per thread
     static_assert(NVEC % 256 == 0 || NVEC < 256, "X stage must tile the block");
 
     __shared__ __align__(16) uint16_t xs[2][BT][XROW];
-    __shared__ float xsum[2][RPS][BT];
-    __shared__ __align__(16) float2 hdr[2][RPS][64];  // (scale, 1024 + zero) per tile row
+    constexpr int BR = 64 * RB;                       // block rows
+    __shared__ uint32_t hdr[2][RPS][BR];   // (scale | zero << 16) fp16 bits per block row
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int r16 = lane & 15;
     const int g4 = lane >> 4;
-    const int64_t nb0 = (int64_t)blockIdx.x * 64;     // block's first row
-    const int64_t n0 = nb0 + wave * 16;               // wave's first row
+    const int64_t nb0 = (int64_t)blockIdx.x * BR;     // block's first row
+    const int64_t n0 = nb0 + wave * 16 * RB;          // wave's first row
     const int64_t b0 = (int64_t)blockIdx.y * BT;
-    const int64_t rowA = n0 + r16;
-    const uint4* rowc = codes + (rowA < N ? rowA : N - 1) * (K / MG::VALS);
+    // This lane's weight row in each of the wave's row tiles (B operand).
+    const uint4* rowc[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+        const int64_t rowB = n0 + 16 * t + r16;
+        rowc[t] = codes + (rowB < N ? rowB : N - 1) * (K / MG::VALS);
+    }
     const int64_t rounds = K / MG::KR;
     const int64_t st0 = (int64_t)blockIdx.z * SPS;
     const int64_t all_stages = (rounds + RPS - 1) / RPS;
     const int64_t st_end = st0 + SPS < all_stages ? st0 + SPS : all_stages;
     const int64_t ngrp = K / G;
-    const uint32_t cmask = vgpr_const(BITS == 4 ? 0x000F000Fu : 0x00FF00FFu);
+    const DqConsts cst = BITS == 4
+        ? DqConsts{vgpr_const(0x000F000Fu), vgpr_const(0x00F000F0u), vgpr_const(0x60006000u), vgpr_const(0x50005000u)}
+        : DqConsts{vgpr_const(0x00FF00FFu), 0u, vgpr_const(0x60006000u), 0u};
+    const h2_t zmul = {(_Float16)0.5f, (_Float16)0.5f};
+    const h2_t zadd = {(_Float16)512.0f, (_Float16)32.0f};
 
     // ---- global -> register loads of one stage --------------------------------
     // Every load is unconditional with a clamped address (rows past N, columns
-    // past B, rounds past the end reread valid data whose results are masked),
-    // so the compiler can count outstanding loads exactly and wait only for the
-    // ones a step needs.
+    // past B, rounds past the end reread valid data); X columns past B and k
+    // past K are zeroed at the LDS store, so clamped rounds add nothing.
     const uint32_t last_round = (uint32_t)(rounds - 1);
     const uint32_t rpg = (uint32_t)(G / MG::KR);      // rounds per group
-    auto load_codes = [&](int64_t st, uint4* cw) {
+    auto load_codes = [&](int64_t st, uint4* cw) {     // cw[r * RB + t]
 #pragma unroll
         for (int r = 0; r < RPS; ++r) {
             uint32_t rr = (uint32_t)(st * RPS + r);
             rr = rr < last_round ? rr : last_round;
-            cw[r] = rowc[(int64_t)rr * 4 + g4];
+#pragma unroll
+            for (int t = 0; t < RB; ++t) cw[r * RB + t] = rowc[t][(int64_t)rr * 4 + g4];
         }
     };
     auto load_x = [&](int64_t st, uint4* xr) {
@@ -159,132 +172,155 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
             xr[u] = *reinterpret_cast<const uint4*>(X + b * K + k);
         }
     };
-    // A round past the end keeps a zero scale, so the step that computes it
-    // (on clamped, finite data) adds nothing.
+    // Headers, HV (one group per round, 8 | groups per row, aligned arrays):
+    // each lane loads the 8 groups of a turn (8 rounds) of its own rows as
+    // two 128-bit loads per row tile, one turn ahead.  Otherwise the block
+    // stages each stage's headers in LDS.
+    int64_t hrow[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+        const int64_t rowB = n0 + 16 * t + r16;
+        hrow[t] = (rowB < N ? rowB : N - 1) * ngrp;
+    }
+    uint4 hsc[RB], hzc[RB], hsn[RB], hzn[RB];
+    auto load_hdr_turn = [&](int64_t round_start) {
+        int64_t ga = round_start;
+        ga = ga + 8 <= rounds ? ga : rounds - 8;
+#pragma unroll
+        for (int t = 0; t < RB; ++t) {
+            hsn[t] = *reinterpret_cast<const uint4*>(scales + hrow[t] + ga);
+            hzn[t] = *reinterpret_cast<const uint4*>(zeros + hrow[t] + ga);
+        }
+    };
     auto load_hdr = [&](int64_t st, uint32_t& hs, uint32_t& hz) {
-        const int row = tid & 63, r = (tid >> 6) % RPS;
+        if constexpr (HV) return;
+        const int row = tid % BR, r = (tid / BR) % RPS;
         const int64_t n = nb0 + row < N ? nb0 + row : N - 1;
-        const uint32_t rr0 = (uint32_t)(st * RPS + r);
-        const uint32_t rr = rr0 < last_round ? rr0 : last_round;
+        uint32_t rr = (uint32_t)(st * RPS + r);
+        rr = rr < last_round ? rr : last_round;
         const int64_t gi = n * ngrp + rr / rpg;
         hs = scales[gi];
         hz = zeros[gi];
-        if (rr0 > last_round) hs = 0u;
     };
     // ---- register -> LDS stores of one stage ----------------------------------
-    auto store_stage = [&](int buf, const uint4* xr, uint32_t hs, uint32_t hz) {
+    auto store_stage = [&](int64_t st, int buf, const uint4* xr, uint32_t hs, uint32_t hz) {
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
             const int v = tid + 256 * u;
             const int col = v / SEGS, seg = v % SEGS;
-            // Threads of one (column, round) are SEGR adjacent lanes.
-            const float s = group_sum<SEGR>(sum8(xr[u]));
-            if (v < NVEC) {
-                *reinterpret_cast<uint4*>(&xs[buf][col][seg * 8]) = permute8<BITS>(xr[u]);
-                if (seg % SEGR == 0) xsum[buf][seg / SEGR][col] = s;
-            }
+            const int64_t k = st * KS + seg * 8;
+            const uint4 x = (b0 + col < B && k < K && st < st_end) ? xr[u] : uint4{0u, 0u, 0u, 0u};
+            if (v < NVEC) *reinterpret_cast<uint4*>(&xs[buf][col][seg * 8]) = permute8<BITS>(x);
         }
-        if (tid < 64 * RPS)
-            hdr[buf][tid >> 6][tid & 63] =
-                make_float2(half_bits_to_float((uint16_t)hs), 1024.0f + half_bits_to_float((uint16_t)hz));
+        if (!HV && tid < BR * RPS) hdr[buf][tid / BR][tid % BR] = hs | (hz << 16);
     };
 
-    f4_t tot[NCB];
+    f4_t acc[RB][NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) tot[cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < RB; ++t)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[t][cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // ---- compute one stage from registers (codes) and LDS (X, header) ----------
-    // All rounds' MFMA chains are issued first, into separate accumulators, and
-    // the header corrections follow, so the matrix-core latency of one round
-    // overlaps the issue of the next instead of stalling each round.
-    auto compute = [&](int64_t st, int buf, const uint4* cw) {
-        float2 h[RPS][4];
-#pragma unroll
-        for (int r = 0; r < RPS; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) h[r][i] = hdr[buf][r][wave * 16 + 4 * g4 + i];  // (s, 1024 + z)
-        float xsv[RPS][NCB];
-#pragma unroll
-        for (int r = 0; r < RPS; ++r)
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) xsv[r][cb] = xsum[buf][r][cb * 16 + r16];
-        f4_t acc[RPS][NCB];
+    // Each k-step's dequantized codes feed all NCB column blocks, and each X
+    // operand read from LDS feeds all RB row tiles.
+    // kt: this stage's position in its turn of 8 rounds (HV header index).
+    auto compute = [&](int buf, const uint4* cw, int kt) {
 #pragma unroll
         for (int r = 0; r < RPS; ++r) {
+            h2_t nz[RB], ss[RB];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) acc[r][cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int t = 0; t < RB; ++t) {
+                uint32_t zb, sb;
+                if constexpr (HV) {
+                    const int i = (kt * RPS + r) & 7;
+                    const uint32_t ws = i < 4 ? (i < 2 ? hsc[t].x : hsc[t].y) : (i < 6 ? hsc[t].z : hsc[t].w);
+                    const uint32_t wz = i < 4 ? (i < 2 ? hzc[t].x : hzc[t].y) : (i < 6 ? hzc[t].z : hzc[t].w);
+                    const uint32_t sel = (i & 1) ? 0x07060706u : 0x05040504u;   // half i&1, twice
+                    sb = __builtin_amdgcn_perm(ws, ws, sel);
+                    zb = __builtin_amdgcn_perm(wz, wz, sel);
+                } else {
+                    const uint32_t h = hdr[buf][r][wave * 16 * RB + 16 * t + r16];
+                    zb = (h >> 16) | (h & 0xFFFF0000u);
+                    sb = (h & 0xFFFFu) | (h << 16);
+                }
+                nz[t] = as_h2(zb) * zmul + zadd;     // (512 + z/2, 32 + z/2)
+                ss[t] = as_h2(sb);
+            }
 #pragma unroll
             for (int j = 0; j < MG::KSTEPS; ++j) {
-                const h8_t a = a_operand<BITS>(cw[r], j, cmask);
+                h8_t bop[RB];
+#pragma unroll
+                for (int t = 0; t < RB; ++t) bop[t] = dequant<BITS>(cw[r * RB + t], j, cst, nz[t], ss[t]);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
-                    const h8_t bop = __builtin_bit_cast(
+                    const h8_t aop = __builtin_bit_cast(
                         h8_t, *reinterpret_cast<const uint4*>(
                                   &xs[buf][cb * 16 + r16][r * MG::KR + g4 * MG::VALS + 8 * j]));
-                    acc[r][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop, acc[r][cb], 0, 0, 0);
+#pragma unroll
+                    for (int t = 0; t < RB; ++t)
+                        acc[t][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[t], acc[t][cb], 0, 0, 0);
                 }
             }
         }
-        // Accumulator lane layout: rows 4*g4 + i, column r16 of each block.
-#pragma unroll
-        for (int r = 0; r < RPS; ++r)
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    tot[cb][i] = __builtin_fmaf(h[r][i].x, __builtin_fmaf(-h[r][i].y, xsv[r][cb], acc[r][cb][i]),
-                                                tot[cb][i]);
     };
 
     // ---- pipeline ----------------------------------------------------------------
-    // Codes run two stages ahead in a ring of three register sets; X and the
-    // header run one stage ahead through registers into the other LDS buffer.
-    // Issue order per stage (X, header, then codes) keeps the wait for X from
-    // also waiting on the codes just issued.
-    uint4 c0[RPS], c1[RPS], c2[RPS], xr[VPT];
-    uint32_t hs, hz;
+    // Codes run two stages ahead in a ring of four register sets; X (and, in
+    // the LDS header mode, the header) run one stage ahead through registers
+    // into the other LDS buffer; HV headers run one 8-round turn ahead.
+    uint4 cr[4][RPS * RB], xr[VPT];
+    uint32_t hs = 0u, hz = 0u;
+    if constexpr (HV) load_hdr_turn(st0 * RPS);
     load_x(st0, xr);
     load_hdr(st0, hs, hz);
-    load_codes(st0, c0);
-    load_codes(st0 + 1, c1);
-    store_stage(0, xr, hs, hz);
+    load_codes(st0, cr[0]);
+    load_codes(st0 + 1, cr[1]);
+    store_stage(st0, 0, xr, hs, hz);
     __syncthreads();
 
-    // Every step loads, computes and stores unconditionally (loads past the
-    // end are clamped and their rounds carry a zero scale): branch-free steps
-    // let the compiler wait only for the loads each step consumes.
-    auto step = [&](int64_t st, int buf, const uint4* cur, uint4* ahead2) {
-        load_x(st + 1, xr);
-        load_hdr(st + 1, hs, hz);
-        load_codes(st + 2, ahead2);
-        compute(st, buf, cur);
-        store_stage(buf ^ 1, xr, hs, hz);
-        __syncthreads();
-    };
-    for (int64_t st = st0; st < st_end; st += 6) {
-        step(st, 0, c0, c2);
-        if (st + 1 >= st_end) break;
-        step(st + 1, 1, c1, c0);
-        if (st + 2 >= st_end) break;
-        step(st + 2, 0, c2, c1);
-        if (st + 3 >= st_end) break;
-        step(st + 3, 1, c0, c2);
-        if (st + 4 >= st_end) break;
-        step(st + 4, 0, c1, c0);
-        if (st + 5 >= st_end) break;
-        step(st + 5, 1, c2, c1);
+    constexpr int STT = 8 / RPS;                      // stages per header turn
+    // The stage count is padded to whole 8-step bodies, so the loop has no
+    // exits inside it; padded stages meet zero X and add nothing.
+    for (int64_t st = st0; st < st_end; st += 8) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if constexpr (HV) {
+                if (k % STT == 0) {
+#pragma unroll
+                    for (int t = 0; t < RB; ++t) {
+                        hsc[t] = hsn[t];
+                        hzc[t] = hzn[t];
+                    }
+                    load_hdr_turn((st + k) * RPS + 8);
+                }
+            }
+            load_x(st + k + 1, xr);
+            load_hdr(st + k + 1, hs, hz);
+            load_codes(st + k + 2, cr[(k + 2) & 3]);
+            compute(k & 1, cr[k & 3], k % STT);
+            store_stage(st + k + 1, (k & 1) ^ 1, xr, hs, hz);
+            __syncthreads();
+        }
     }
 
+    // Accumulator lane layout: batch rows 4*g4 + i of column block cb, weight
+    // row r16 of tile t; the dequantized operand carried a factor 1/2.
     float* pz = part ? part + (int64_t)blockIdx.z * B * N : nullptr;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        const int64_t col = b0 + cb * 16 + r16;
+    for (int t = 0; t < RB; ++t) {
+        const int64_t row = n0 + 16 * t + r16;
+        if (row >= N) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t row = n0 + 4 * g4 + i;
-            if (row < N && col < B) {
-                if (pz) pz[col * N + row] = tot[cb][i];
-                else Y[col * N + row] = float_to_half_bits_rne(tot[cb][i]);
+        for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t col = b0 + cb * 16 + 4 * g4 + i;
+                if (col < B) {
+                    const float v = 2.0f * acc[t][cb][i];
+                    if (pz) pz[col * N + row] = v;
+                    else Y[col * N + row] = float_to_half_bits_rne(v);
+                }
             }
         }
     }
@@ -301,32 +337,43 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     Y[i] = float_to_half_bits_rne(s);
 }
 
-template <int BITS, int BT, int KS>
+template <int BITS, int BT, int KS, int RB>
 hipError_t launch_bt(const void* X, const void* codes, const void* scales, const void* zeros,
                      void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int num_cus,
                      hipStream_t stream) {
     constexpr int RPS = KS / MfmaGeom<BITS>::KR;
-    const int64_t tiles = ((N + 63) / 64) * ((B + BT - 1) / BT);
+    constexpr int BR = 64 * RB;
+    const int64_t tiles = ((N + BR - 1) / BR) * ((B + BT - 1) / BT);
     const int64_t stages = (K / MfmaGeom<BITS>::KR + RPS - 1) / RPS;
-    // Split K until about three blocks per compute unit are in flight, keeping
+    // Split K until about two blocks per compute unit are in flight, keeping
     // at least two stages per split so that loads overlap compute.
-    int64_t want = (3 * (int64_t)num_cus + tiles - 1) / tiles;
+    int64_t want = (2 * (int64_t)num_cus + tiles - 1) / tiles;
     int64_t max_split = stages / 2 > 0 ? stages / 2 : 1;
     if (want > max_split) want = max_split;
     if (want < 1) want = 1;
-    const int64_t sps = (stages + want - 1) / want;
+    int64_t sps = (stages + want - 1) / want;
+    sps = (sps + 7) / 8 * 8;                          // whole 8-step loop bodies
     const int64_t splits = (stages + sps - 1) / sps;
-    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((B + BT - 1) / BT), (unsigned)splits);
+    const dim3 grid((unsigned)((N + BR - 1) / BR), (unsigned)((B + BT - 1) / BT), (unsigned)splits);
     float* part = nullptr;
     if (splits > 1) {
         uint32_t* unused = nullptr;
         hipError_t e = workspace_get(stream, 0, (size_t)splits * B * N * sizeof(float), &unused, &part);
         if (e != hipSuccess) return e;
     }
-    gemm_mfma_kernel<BITS, BT, KS><<<grid, dim3(256), 0, stream>>>(
-        static_cast<const uint16_t*>(X), static_cast<const uint4*>(codes),
-        static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
-        static_cast<uint16_t*>(Y), part, B, N, K, G, sps);
+    const bool hv = G == MfmaGeom<BITS>::KR && (K / G) % 8 == 0 &&
+                    reinterpret_cast<uintptr_t>(scales) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(zeros) % 16 == 0;
+    if (hv)
+        gemm_mfma_kernel<BITS, BT, KS, RB, true><<<grid, dim3(256), 0, stream>>>(
+            static_cast<const uint16_t*>(X), static_cast<const uint4*>(codes),
+            static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
+            static_cast<uint16_t*>(Y), part, B, N, K, G, sps);
+    else
+        gemm_mfma_kernel<BITS, BT, KS, RB, false><<<grid, dim3(256), 0, stream>>>(
+            static_cast<const uint16_t*>(X), static_cast<const uint4*>(codes),
+            static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
+            static_cast<uint16_t*>(Y), part, B, N, K, G, sps);
     hipError_t e = hipGetLastError();
     if (splits > 1 && e == hipSuccess) {
         const int64_t count = B * N;
@@ -337,14 +384,21 @@ hipError_t launch_bt(const void* X, const void* codes, const void* scales, const
     return e;
 }
 
+// Tall matrices give every compute unit enough 128-row tiles: two row tiles
+// per wave halve the LDS reads per weight.  Shorter ones keep 64-row tiles.
 template <int BITS>
 hipError_t launch_bits(const void* X, const void* codes, const void* scales, const void* zeros,
                        void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int cus,
                        hipStream_t st) {
     constexpr int KR = MfmaGeom<BITS>::KR;
-    if (B <= 16) return launch_bt<BITS, 16, 2 * KR>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
-    if (B <= 32) return launch_bt<BITS, 32, 2 * KR>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
-    return launch_bt<BITS, 64, 2 * KR>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+    const bool tall = N >= 64 * (int64_t)cus;
+    if (B <= 16) return launch_bt<BITS, 16, 2 * KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+    if (B <= 32) {
+        if (tall) return launch_bt<BITS, 32, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+        return launch_bt<BITS, 32, 2 * KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+    }
+    if (tall) return launch_bt<BITS, 64, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+    return launch_bt<BITS, 64, 2 * KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
 }
 
 }  // namespace
