@@ -18,6 +18,7 @@ same step.
 
     python bench.py [--steps 20] [--warmup 5] [--no-cpu]
     python bench.py --sweep     # batch sweep across the ridge (K=N=8192), table only
+    python bench.py --decode-set   # 7B-class decode step (224 products, B=32), table only
 """
 
 from __future__ import annotations
@@ -47,6 +48,8 @@ def parse():
     p.add_argument("--workload", default=WORKLOAD)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--sweep", action="store_true", help="batch sweep on K=N=8192 (table)")
+    p.add_argument("--decode-set", action="store_true",
+                   help="7B-class decode step, 224 products at B=32 (table)")
     p.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after timing, copy this many MiB device-to-device once (a "
@@ -410,6 +413,91 @@ def run_sweep(args):
     return rows
 
 
+def run_decode_set(args):
+    """The 7B-class decode step: 32 layers x (q, k, v, o, gate, up, down) at
+    B = 32, int4 group 128 and 8-bit per-channel.  Every matrix has its own
+    packed weights in HBM (3.4 GB at int4, 6.5 GB at 8 bits), so nothing is
+    served from a cache; weights are drawn on the GPU, N(0, 0.02), fp16."""
+    import torch
+
+    import bit_weight_only_wq_amd as wq
+    import wq_inputs
+    from bit_weight_only_wq_amd import roofline as rl
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    B = wq_inputs.DECODE_SET_BATCH
+    out = []
+    for bits, label in ((4, "int4 g128"), (8, "int8 per-channel")):
+        mats = []
+        for layer in range(wq_inputs.DECODE_SET_LAYERS):
+            for _, N, K in wq_inputs.DECODE_SET_SHAPES:
+                G = 128 if bits == 4 else K
+                W = (torch.randn((N, K), generator=gen, device=dev) * wq_inputs.DECODE_SET_SIGMA).half()
+                mats.append((N, K, G) + tuple(wq.quantize_pack(W, G, bits)))
+                del W
+        Xs = {K: torch.randn((B, K), generator=gen, device=dev).half()
+              for K in {k for _, _, k in wq_inputs.DECODE_SET_SHAPES}}
+        Ys = {N: torch.empty((B, N), dtype=torch.float16, device=dev)
+              for N in {n for _, n, _ in wq_inputs.DECODE_SET_SHAPES}}
+        torch.cuda.synchronize()
+
+        lib = wq.load()
+        stream = torch.cuda.current_stream(dev)
+        hs = stream.cuda_stream
+        calls = [(Xs[K].data_ptr(), c.data_ptr(), s.data_ptr(), z.data_ptr(), Ys[N].data_ptr(),
+                  B, K, N, G) for N, K, G, c, s, z in mats]
+
+        def step_on(h):
+            for x, c, s, z, y, b, k, n, g in calls:
+                st = lib.wq_gemm(x, c, s, z, y, b, k, n, g, bits, h)
+                if st:
+                    wq.check(st, "wq_gemm")
+
+        def step():
+            step_on(hs)
+
+        def timed(fn, reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        for _ in range(2):
+            step()
+        ms_eager = timed(step, 5)
+        # The same 224 launches replayed from a HIP graph: no host launch gaps.
+        # The capture stream's workspace is created by eager calls first, so
+        # capture records kernels only.
+        cap = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cap):
+            step_on(cap.cuda_stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            step_on(cap.cuda_stream)
+        graph.replay()
+        ms = timed(graph.replay, 5)
+        nbytes = sum(rl.gemm_bytes(B, N, K, G, bits) for N, K, G, *_ in mats)
+        flops = sum(rl.gemm_flops(B, N, K) for N, K, *_ in mats)
+        row = {"decode_set": label, "matrices": len(mats), "B": B, "ms_per_step": round(ms, 4),
+               "ms_per_step_eager": round(ms_eager, 4),
+               "GBps": round(nbytes / ms / 1e6, 1), "TFLOPs": round(flops / ms / 1e9, 2),
+               "bytes_per_step": int(nbytes)}
+        print(json.dumps(row), flush=True)
+        out.append(row)
+        del mats
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -421,6 +509,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         run_sweep(args)
+        return
+    if args.decode_set:
+        run_decode_set(args)
         return
     out, batches = run_step_bench(args)
     if args.copy_calibration_mib:
