@@ -386,6 +386,8 @@ hipError_t launch_bt(const void* X, const void* codes, const void* scales, const
 
 // Tall matrices give every compute unit enough 128-row tiles: two row tiles
 // per wave halve the LDS reads per weight.  Shorter ones keep 64-row tiles.
+// Past 16 columns every variant stages one 128-k round per step, which keeps
+// enough K-splits for short matrices (measured on the 7B-class shapes).
 template <int BITS>
 hipError_t launch_bits(const void* X, const void* codes, const void* scales, const void* zeros,
                        void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int cus,
@@ -395,10 +397,10 @@ hipError_t launch_bits(const void* X, const void* codes, const void* scales, con
     if (B <= 16) return launch_bt<BITS, 16, 2 * KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
     if (B <= 32) {
         if (tall) return launch_bt<BITS, 32, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
-        return launch_bt<BITS, 32, 2 * KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+        return launch_bt<BITS, 32, KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
     }
     if (tall) return launch_bt<BITS, 64, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
-    return launch_bt<BITS, 64, 2 * KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+    return launch_bt<BITS, 64, KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
 }
 
 }  // namespace

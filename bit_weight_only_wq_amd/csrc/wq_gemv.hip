@@ -131,8 +131,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(
         const int64_t g = tl + (int64_t)TG * i;
         hidx[i] = (int)(g < ngrp ? g : ngrp - 1);
     }
+    // Every load is unconditional (passes past the end reread the last row,
+    // chunks and header entries past the row's end reread its last ones), so
+    // the compiler can count the loads in flight exactly and the next pass's
+    // loads stay outstanding while the current pass computes.
     auto load_pass = [&](int64_t pass, uint4* w, uint32_t* hs, uint32_t* hz) {
-        if (pass >= passes) return;
         int64_t n = pass * RPB + rs;
         n = n < N ? n : N - 1;
         const uint4* rowc = codes + n * C;
@@ -140,11 +143,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(
         const uint16_t* rowz = zeros + n * ngrp;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            if (TG * i < C) w[i] = load_stream(rowc + cidx[i]);
-            if ((int64_t)TG * i < ngrp) {
-                hs[i] = rows[hidx[i]];
-                hz[i] = rowz[hidx[i]];
-            }
+            w[i] = load_stream(rowc + cidx[i]);
+            hs[i] = rows[hidx[i]];
+            hz[i] = rowz[hidx[i]];
         }
     };
 
