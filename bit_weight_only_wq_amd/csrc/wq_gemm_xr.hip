@@ -1,13 +1,14 @@
-// Matrix-core product for small batches (B <= 16) with the activations held in
+// Matrix-core product for small batches (B <= 32) with the activations held in
 // LDS: Y[B,N] = X[B,K] * dequant(W)[N,K]^T.
 //
 // A decode step reads every weight once for the whole batch ("Quantization &
 // inference optimisation", "Bandwidth, not compute"), so the kernel is built
 // around one continuous stream of packed codes, like the GEMV path:
-//   - a block (16 waves, one per compute unit) copies a K-slice of X (all B
-//     rows, up to 128 KB) into LDS once, permuted into the order the codes
-//     unpack in, together with two weighted column sums per 128-k round, and
-//     never synchronizes again;
+//   - a block (one per compute unit: 16 waves, or 8 when B > 16 puts two
+//     16-column blocks in each wave) copies a K-slice of X (all B rows, up to
+//     128 KB) into LDS once, permuted into the order the codes unpack in,
+//     together with two weighted column sums per 128-k round, and never
+//     synchronizes again;
 //   - every wave then owns whole 16-row tiles of that slice and streams their
 //     128-bit code chunks through a ring of registers that runs six to seven
 //     rounds ahead, across tile boundaries; group headers arrive eight rounds at a
@@ -42,7 +43,6 @@ namespace wq {
 
 namespace {
 
-constexpr int XR_WAVES = 16;     // waves per block (one block per compute unit)
 constexpr int XR_SLOTS = 8;      // register ring of code chunks, refilled two rounds at a time
 
 // How a wave gets the group headers of its rows.
@@ -51,6 +51,10 @@ enum XrHeader {
     XR_HDR_TURN = 1,    // one group per round: 8 groups per 128-bit load
     XR_HDR_ROW = 2      // one group per row: loaded once per tile
 };
+
+// Waves per block (one block per compute unit): 16 while the registers of one
+// 16-column block fit 128 per lane, 8 with two column blocks.
+constexpr int xr_waves(int btx) { return btx > 16 ? 8 : 16; }
 
 template <int BITS, int BTX>
 struct XrGeom {
@@ -61,6 +65,7 @@ struct XrGeom {
     static constexpr int KSL = 65536 / BTX;        // X slice length (halves): 128 KB of LDS
     static constexpr int ROW = KSL + 8;            // padded LDS row: rows land on distinct banks
     static constexpr int RMAX = KSL / KR;          // rounds per slice at most
+    static constexpr int WAVES = xr_waves(BTX);
 };
 
 __device__ __forceinline__ uint32_t vreg(uint32_t v) {
@@ -149,12 +154,13 @@ __device__ __forceinline__ float half_of(const uint4& v, int i) {
 // round r is (r * rpg_magic) >> 32 = floor(r / (G / KR)), exact for r < 2^16
 // with rpg_magic = ceil(2^32 / (G / KR)).
 template <int BITS, int BTX, int HM>
-__global__ __launch_bounds__(1024) void gemm_xr_kernel(
+__global__ __launch_bounds__(xr_waves(BTX) * 64) void gemm_xr_kernel(
     const uint16_t* __restrict__ X, const uint4* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, float* __restrict__ part, int64_t B, int64_t N, int64_t K,
     int64_t ngrp, uint64_t rpg_magic, int32_t RS) {
     typedef XrGeom<BITS, BTX> XG;
+    constexpr int NCB = (BTX + 15) / 16;                   // 16-column blocks
     __shared__ __align__(16) uint16_t xs[BTX * XG::ROW];
     __shared__ __align__(16) float cneg1[XG::RMAX][BTX];   // -C1 per (round, column)
     __shared__ __align__(16) float csum2[XG::RMAX][BTX];   //  C2 per (round, column)
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(1024) void gemm_xr_kernel(
     const int64_t rounds = K / XG::KR;
     const int64_t round0 = (int64_t)blockIdx.y * RS;          // first round of the slice
     const int64_t ntiles = (N + 15) / 16;
-    const int64_t stride = (int64_t)gridDim.x * XR_WAVES;
+    const int64_t stride = (int64_t)gridDim.x * XG::WAVES;
     const int64_t t0 = (int64_t)wave * gridDim.x + blockIdx.x;
     const int64_t chunks_per_row = K / XG::VALS;
 
@@ -185,13 +191,13 @@ __global__ __launch_bounds__(1024) void gemm_xr_kernel(
     // loads go out before the ring's, so waiting for them leaves the code
     // stream in flight.
     constexpr int VROW = XG::KSL / 8;                              // vectors per LDS row
-    constexpr int FILL = BTX * VROW / (XR_WAVES * 64);             // vectors per thread
+    constexpr int FILL = BTX * VROW / (XG::WAVES * 64);             // vectors per thread
     const int vec_used = RS * XG::SEGR;                            // vectors of this slice
     const int64_t k0 = round0 * XG::KR;
     uint4 xv[FILL];
 #pragma unroll
     for (int u = 0; u < FILL; ++u) {
-        const int v = tid + u * XR_WAVES * 64;
+        const int v = tid + u * XG::WAVES * 64;
         const int col = v / VROW, seg = v % VROW;
         const int64_t k = k0 + (int64_t)seg * 8;
         const bool ok = col < B && seg < vec_used && k < K;
@@ -246,7 +252,7 @@ __global__ __launch_bounds__(1024) void gemm_xr_kernel(
     // ---- X slice -> LDS, with its per-round column sums ---------------------
 #pragma unroll
     for (int u = 0; u < FILL; ++u) {
-        const int v = tid + u * XR_WAVES * 64;
+        const int v = tid + u * XG::WAVES * 64;
         const int col = v / VROW, seg = v % VROW;
         const int64_t k = k0 + (int64_t)seg * 8;
         const uint4 x = col < B && seg < vec_used && k < K ? xv[u] : uint4{0u, 0u, 0u, 0u};
@@ -269,24 +275,43 @@ __global__ __launch_bounds__(1024) void gemm_xr_kernel(
 
     const Consts cst = BITS == 4 ? Consts{vreg(0x000F000Fu), vreg(0x00F000F0u), vreg(0x64006400u), vreg(0x54005400u)}
                                  : Consts{vreg(0x00FF00FFu), 0u, vreg(0x64006400u), 0u};
-    // A operand: batch row r16 (mod BTX), 8 k at the lane group's offset.
-    // Accumulator lane layout: batch rows 4*g4 + i (mod BTX), weight row r16.
-    const uint16_t* xa = &xs[(r16 % BTX) * XG::ROW + g4 * XG::VALS];
-    const int cbase = (4 * g4) % BTX;
-
-    f4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto compute = [&](int slot, int lr, float s, float z) {
-        f4_t acc = *reinterpret_cast<const f4_t*>(&cneg1[lr][cbase]);
-        const f4_t c2 = *reinterpret_cast<const f4_t*>(&csum2[lr][cbase]);
+    // A operand of column block cb: batch row cb*16 + r16 (mod BTX), 8 k at the
+    // lane group's offset.  Accumulator lane layout: batch rows
+    // cb*16 + 4*g4 + i (mod BTX), weight row r16.  The unpacked codes of a
+    // k-step feed every column block.
+    const uint16_t* xa[NCB];
+    int cbase[NCB];
 #pragma unroll
-        for (int j = 0; j < XG::KSTEPS; ++j) {
-            const h8_t a = __builtin_bit_cast(
-                h8_t, *reinterpret_cast<const uint4*>(xa + lr * XG::KR + 8 * j));
-            const h8_t b = unpack<BITS>(cw[slot], j, cst);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    for (int cb = 0; cb < NCB; ++cb) {
+        xa[cb] = &xs[((cb * 16 + r16) % BTX) * XG::ROW + g4 * XG::VALS];
+        cbase[cb] = (cb * 16 + 4 * g4) % BTX;
+    }
+
+    f4_t tot[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) tot[cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](int slot, int lr, float s, float z) {
+        f4_t acc[NCB], c2[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            acc[cb] = *reinterpret_cast<const f4_t*>(&cneg1[lr][cbase[cb]]);
+            c2[cb] = *reinterpret_cast<const f4_t*>(&csum2[lr][cbase[cb]]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tot[i] = __builtin_fmaf(s, __builtin_fmaf(-z, c2[i], acc[i]), tot[i]);
+        for (int j = 0; j < XG::KSTEPS; ++j) {
+            const h8_t b = unpack<BITS>(cw[slot], j, cst);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const h8_t a = __builtin_bit_cast(
+                    h8_t, *reinterpret_cast<const uint4*>(xa[cb] + lr * XG::KR + 8 * j));
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[cb], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                tot[cb][i] = __builtin_fmaf(s, __builtin_fmaf(-z, c2[cb][i], acc[cb][i]), tot[cb][i]);
     };
     // Header of step k of a turn (values for round it*8 + k).
     auto hdr_s = [&](int k) -> float {
@@ -353,23 +378,26 @@ __global__ __launch_bounds__(1024) void gemm_xr_kernel(
         }
         const int64_t row = t * 16 + r16;
         const int bmax = (int)(B < BTX ? B : BTX);
-        const bool mine = row < N && 4 * g4 < BTX;
-        if (!part) {
-            if (mine) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const bool mine = row < N && cb * 16 + 4 * g4 < BTX;
+            if (!part) {
+                if (mine) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int col = cb * 16 + 4 * g4 + i;
+                        if (col < bmax) Y[col * N + row] = float_to_half_bits_rne(tot[cb][i]);
+                    }
+                }
+            } else if (mine) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int col = 4 * g4 + i;
-                    if (col < bmax) Y[col * N + row] = float_to_half_bits_rne(tot[i]);
+                    const int col = cb * 16 + 4 * g4 + i;
+                    if (col < bmax) part[((int64_t)blockIdx.y * B + col) * N + row] = tot[cb][i];
                 }
             }
-        } else if (mine) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = 4 * g4 + i;
-                if (col < bmax) part[((int64_t)blockIdx.y * B + col) * N + row] = tot[i];
-            }
+            tot[cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
         }
-        tot = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
         pc = nc;
         ph = nh;
         nc = codes + tile_row(t + 2 * stride) * chunks_per_row + g4;
@@ -404,7 +432,7 @@ hipError_t launch_xr_hm(const void* X, const void* codes, const void* scales, co
     // Slices: as few as LDS allows, more when the tiles alone cannot give every
     // compute unit's waves work (each slice keeps at least one ring turn).
     int64_t slices = (rounds + XG::RMAX - 1) / XG::RMAX;
-    const int64_t want_items = (int64_t)num_cus * XR_WAVES / 2;
+    const int64_t want_items = (int64_t)num_cus * XG::WAVES / 2;
     if (ntiles * slices < want_items) {
         const int64_t s = (want_items + ntiles - 1) / ntiles;
         const int64_t smax = (rounds + XR_SLOTS - 1) / XR_SLOTS;
@@ -427,7 +455,7 @@ hipError_t launch_xr_hm(const void* X, const void* codes, const void* scales, co
         hipError_t e = workspace_get(stream, 0, (size_t)slices * B * N * sizeof(float), &unused, &part);
         if (e != hipSuccess) return e;
     }
-    gemm_xr_kernel<BITS, BTX, HM><<<grid, dim3(XR_WAVES * 64), 0, stream>>>(
+    gemm_xr_kernel<BITS, BTX, HM><<<grid, dim3(XG::WAVES * 64), 0, stream>>>(
         static_cast<const uint16_t*>(X), static_cast<const uint4*>(codes),
         static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
         static_cast<uint16_t*>(Y), part, B, N, K, K / G, magic, (int32_t)rs);
@@ -459,9 +487,12 @@ hipError_t launch_xr_bt(const void* X, const void* codes, const void* scales, co
 }  // namespace
 
 bool xr_supports(int64_t B, int64_t K, int32_t group, int32_t bits) {
-    if (B < 1 || B > 16 || (bits != 4 && bits != 8)) return false;
+    if (B < 1 || B > 32 || (bits != 4 && bits != 8)) return false;
     const int kr = bits == 4 ? XrGeom<4, 16>::KR : XrGeom<8, 16>::KR;
-    return group % kr == 0 && K % kr == 0 && K / kr < 65536;
+    if (group % kr != 0 || K % kr != 0 || K / kr >= 65536) return false;
+    // Past 16 columns a slice holds 2048 k; beyond four slices the partial
+    // sums cost more than the tiled kernel's staging (measured at K = 11008).
+    return B <= 16 || K <= 4 * XrGeom<4, 32>::KSL;
 }
 
 hipError_t launch_gemm_xr(const void* X, const void* codes, const void* scales,
@@ -469,10 +500,12 @@ hipError_t launch_gemm_xr(const void* X, const void* codes, const void* scales,
                           int32_t group, int32_t bits, int num_cus, hipStream_t stream) {
     if (bits == 4) {
         if (B <= 8) return launch_xr_bt<4, 8>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
-        return launch_xr_bt<4, 16>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+        if (B <= 16) return launch_xr_bt<4, 16>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+        return launch_xr_bt<4, 32>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
     }
     if (B <= 8) return launch_xr_bt<8, 8>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
-    return launch_xr_bt<8, 16>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+    if (B <= 16) return launch_xr_bt<8, 16>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+    return launch_xr_bt<8, 32>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
 }
 
 }  // namespace wq

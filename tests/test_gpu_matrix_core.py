@@ -1,6 +1,6 @@
 """GPU parity of the matrix-core kernels on the cases their tiling makes special.
 
-The small-batch matrix-core kernel (3 <= B <= 16) keeps a K-slice of X in
+The small-batch matrix-core kernel (3 <= B <= 32) keeps a K-slice of X in
 LDS, so these tests cover: K that is not a multiple of the slice (rounds past
 K inside the last slice), several slices added in slice order, each way of
 reading group headers (one group per 128-k round, several rounds per group,
@@ -33,7 +33,7 @@ def packed(W, group, bits):
 @pytest.mark.parametrize("K,group,bits", [(4480, 128, 4), (11008, 128, 4), (8192, 256, 4),
                                           (16384, 128, 4), (4480, 4480, 8), (11008, 64, 8),
                                           (4096, 512, 8)])
-@pytest.mark.parametrize("B", [3, 8, 9, 16])
+@pytest.mark.parametrize("B", [3, 8, 9, 16, 17, 32])
 def test_ragged_slices_and_header_modes(K, group, bits, B):
     device()
     rng = np.random.default_rng(K + 7 * B + bits)
@@ -47,7 +47,7 @@ def test_ragged_slices_and_header_modes(K, group, bits, B):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("B", [4, 16, 40])
+@pytest.mark.parametrize("B", [4, 16, 24, 40])
 def test_extreme_groups(bits, B):
     """Crafted groups (saturated zero points, subnormal and +-65504 values,
     constant groups) stacked into rows: every operand stays finite."""
