@@ -7,8 +7,9 @@
 //     visits (chunk c, c+TG, c+2TG, ... of the row), read with one 128-bit
 //     load each; TG consecutive threads cover a row, so a wave's loads are
 //     contiguous;
-//   - the matching X values live in registers for the whole kernel, already
-//     permuted into the order the codes unpack in, so X is read once;
+//   - the matching X values live in LDS for the whole kernel, already
+//     permuted into the order the codes unpack in, so X is read from HBM once
+//     per block;
 //   - codes become fp16 (1024 + q) with one AND-OR per pair ("the kernel
 //     reconstructs an approximate float from the integer and the endpoints as
 //     it reads", "Quantization"), and v_dot2_f32_f16 accumulates in fp32;
@@ -322,6 +323,202 @@ __global__ __launch_bounds__(256) void gemv_kernel(
     }
 }
 
+// ---- one batch row ---------------------------------------------------------
+// B = 1 with whole rows inside one wave (TG <= 64) and an even group count per
+// row: the same arithmetic as gemv_kernel, with less work around it.
+//   - the group headers of a row arrive as 32-bit words (two scales or two
+//     zeros each, HL words per thread) instead of one 16-bit load per entry;
+//   - with TG == 64 the row is uniform across the wave, so the code loads take
+//     a scalar row base and a fixed per-lane offset;
+//   - chunks past a row's end read an all-zero X record (index C) instead of
+//     being masked in every pass, and the records hold -K0, so a chunk costs
+//     its unpack, its dot products and three FMAs.
+template <int BITS, int TG, int CPT, int HL>
+__global__ __launch_bounds__(256) void gemv_row_kernel(
+    const uint16_t* __restrict__ X, const uint4* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
+    uint16_t* __restrict__ Y, int64_t N, int64_t K, int32_t G) {
+    typedef ChunkGeom<BITS> CG;
+    constexpr int QPC = CG::PAIRS / 4;          // uint4 of X pairs per chunk
+    constexpr int REC = QPC + 1;                // uint4 per X record
+    constexpr int RPB = 256 / TG;               // rows per block pass
+    constexpr uint32_t MAGIC = 0x64006400u;
+    // LDS: C + 1 X records, then (scale, zero) of every group of the block's
+    // RPB rows.
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x;
+    const int tl = tid % TG;
+    const int rs = TG == 64 ? __builtin_amdgcn_readfirstlane(tid / TG) : tid / TG;
+    const int C = (int)(K / CG::VALS);
+    const int ngrp = (int)(K / G);
+    const int cpg = G / CG::VALS;
+    const int S = ngrp / 2;                     // header words per array and row
+    const int64_t passes = (N + RPB - 1) / RPB;
+    uint4* xrec = reinterpret_cast<uint4*>(smem);
+    const uint32_t m_lo = vgpr_const(BITS == 4 ? 0x000F000Fu : 0x00FF00FFu);
+    const uint32_t m_hi = vgpr_const(0x00F000F0u);
+
+    // Per chunk: byte offset in the row, LDS byte address of its X record,
+    // and its group.
+    uint32_t coff[CPT], xaddr[CPT], gix[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tl + TG * i;
+        const bool ok = c < C;
+        const int cc = ok ? c : C - 1;
+        coff[i] = (uint32_t)cc * 16u;
+        xaddr[i] = (uint32_t)(ok ? c : C) * (uint32_t)(REC * 16);
+        gix[i] = (uint32_t)(cc / cpg);
+    }
+    // Header word h of this thread: word w of the row's 2S words (scales
+    // first, then zeros; threads past the end repeat the last word), its byte
+    // offset from the row's first scale, and where its two values go in hdr.
+    int64_t hoff[HL];
+    int hst[HL];
+#pragma unroll
+    for (int h = 0; h < HL; ++h) {
+        int w = tl + TG * h;
+        w = w < 2 * S ? w : 2 * S - 1;
+        const bool isz = w >= S;
+        const int wm = isz ? w - S : w;
+        hoff[h] = (isz ? (int64_t)(reinterpret_cast<const char*>(zeros) -
+                                   reinterpret_cast<const char*>(scales))
+                       : (int64_t)0) +
+                  (int64_t)wm * 4;
+        hst[h] = 4 * wm + (isz ? 1 : 0);
+    }
+
+    // Every load is unconditional (passes past the end reread the last row),
+    // so the next pass stays in flight while the current one computes.
+    auto load_pass = [&](int64_t pass, uint4* w, uint32_t* hw) {
+        int64_t n = pass * RPB + rs;
+        n = n < N ? n : N - 1;
+        const char* rowc = reinterpret_cast<const char*>(codes + n * C);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) w[i] = load_stream(reinterpret_cast<const uint4*>(rowc + coff[i]));
+        const char* rowh = reinterpret_cast<const char*>(scales + n * ngrp);
+#pragma unroll
+        for (int h = 0; h < HL; ++h) hw[h] = *reinterpret_cast<const uint32_t*>(rowh + hoff[h]);
+    };
+
+    int64_t pass = blockIdx.x;
+    uint4 wA[CPT], wB[CPT];
+    uint32_t hA[HL], hB[HL];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) wA[i] = wB[i] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int h = 0; h < HL; ++h) hA[h] = hB[h] = 0u;
+    load_pass(pass, wA, hA);
+
+    // ---- X records in LDS, plus the zero record C ---------------------------
+    for (int e = tid; e <= C; e += 256) {
+        uint16_t xv[CG::VALS];
+        if (e < C) {
+            const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)e * CG::VALS);
+#pragma unroll
+            for (int v = 0; v < CG::VALS / 8; ++v) {
+                const uint4 u = src[v];
+                const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    xv[8 * v + 2 * q] = (uint16_t)(ww[q] & 0xFFFFu);
+                    xv[8 * v + 2 * q + 1] = (uint16_t)(ww[q] >> 16);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < CG::VALS; ++v) xv[v] = 0;
+        }
+        uint32_t pr[CG::PAIRS];
+        float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int p = 0; p < CG::PAIRS_PER_WORD; ++p) {
+                int a, bb;
+                pair_positions<BITS>(j, p, a, bb);
+                pr[j * CG::PAIRS_PER_WORD + p] = (uint32_t)xv[a] | ((uint32_t)xv[bb] << 16);
+                const float t = half_bits_to_float(xv[a]) + half_bits_to_float(xv[bb]);
+                if (BITS == 4 && (p & 1)) sb += t;
+                else sa += t;
+            }
+        uint4* rec = xrec + (size_t)e * REC;
+#pragma unroll
+        for (int r = 0; r < QPC; ++r)
+            rec[r] = make_uint4(pr[4 * r], pr[4 * r + 1], pr[4 * r + 2], pr[4 * r + 3]);
+        const float k0 = 1024.0f * sa + 64.0f * sb;
+        rec[QPC] = make_uint4(__builtin_bit_cast(uint32_t, -k0), __builtin_bit_cast(uint32_t, sa + sb), 0u, 0u);
+    }
+    __syncthreads();
+
+    float2* hrow = reinterpret_cast<float2*>(smem + (size_t)(C + 1) * REC * 16) + (size_t)rs * ngrp;
+    float* hf = reinterpret_cast<float*>(hrow);
+    auto compute_pass = [&](int64_t ps, const uint4* w, const uint32_t* hw) {
+        const int64_t n = ps * RPB + rs;
+#pragma unroll
+        for (int h = 0; h < HL; ++h) {
+            hf[hst[h]] = half_bits_to_float((uint16_t)(hw[h] & 0xFFFFu));
+            hf[hst[h] + 2] = half_bits_to_float((uint16_t)(hw[h] >> 16));
+        }
+        wave_lds_sync();
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const float2 sz = hrow[gix[i]];
+            // Opaque address: keeps the record reads in the pass loop and after
+            // the previous chunk's math (bounds the registers in flight).
+            uint32_t xa = xaddr[i];
+            asm volatile("" : "+v"(xa) : "v"(acc));
+            const uint4* rec = reinterpret_cast<const uint4*>(smem + xa);
+            const uint4 kx = rec[QPC];
+            float pa = __builtin_bit_cast(float, kx.x);
+            const float xt = __builtin_bit_cast(float, kx.y);
+            float pb = 0.0f;
+            const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t sh = ww[j] >> 8;
+                if constexpr (BITS == 4) {
+                    const h2_t q04 = as_h2((ww[j] & m_lo) | MAGIC);
+                    const h2_t q15 = as_h2((ww[j] & m_hi) | MAGIC);
+                    const h2_t q26 = as_h2((sh & m_lo) | MAGIC);
+                    const h2_t q37 = as_h2((sh & m_hi) | MAGIC);
+                    const uint4 xv = rec[j];
+                    pa = __builtin_amdgcn_fdot2(q04, as_h2(xv.x), pa, false);
+                    pb = __builtin_amdgcn_fdot2(q15, as_h2(xv.y), pb, false);
+                    pa = __builtin_amdgcn_fdot2(q26, as_h2(xv.z), pa, false);
+                    pb = __builtin_amdgcn_fdot2(q37, as_h2(xv.w), pb, false);
+                } else {
+                    const h2_t q02 = as_h2((ww[j] & m_lo) | MAGIC);
+                    const h2_t q13 = as_h2((sh & m_lo) | MAGIC);
+                    const uint4 xv = rec[j >> 1];
+                    pa = __builtin_amdgcn_fdot2(q02, as_h2((j & 1) ? xv.z : xv.x), pa, false);
+                    pa = __builtin_amdgcn_fdot2(q13, as_h2((j & 1) ? xv.w : xv.y), pa, false);
+                }
+            }
+            float t = pa;
+            if constexpr (BITS == 4) t = __builtin_fmaf(pb, 0.0625f, t);
+            t = __builtin_fmaf(-sz.y, xt, t);
+            acc = __builtin_fmaf(sz.x, t, acc);
+        }
+        acc = group_sum<TG>(acc);
+        if (tl == 0 && n < N) Y[n] = float_to_half_bits_rne(acc);
+        wave_lds_sync();
+    };
+
+    const int64_t step = gridDim.x;
+    while (pass < passes) {
+        load_pass(pass + step, wB, hB);
+        compute_pass(pass, wA, hA);
+        pass += step;
+        if (pass >= passes) break;
+        load_pass(pass + step, wA, hA);
+        compute_pass(pass, wB, hB);
+        pass += step;
+    }
+}
+
 struct GemvChoice {
     int nb, tg, cpt;
 };
@@ -423,6 +620,74 @@ hipError_t by_shape(const GemvChoice& ch, const void* X, const void* codes, cons
     return hipErrorInvalidValue;
 }
 
+// LDS of the one-row kernel: X records (C + 1 of them, the last zero) and
+// the group headers of the 256 / TG rows of a block pass.
+size_t row_lds_bytes(int64_t K, int32_t G, int32_t bits, int tg) {
+    return (size_t)(K / (128 / bits) + 1) * x_lds_per_chunk(bits) +
+           (size_t)(256 / tg) * (size_t)(K / G) * sizeof(float2);
+}
+
+template <int BITS, int TG, int CPT, int HL>
+hipError_t launch_row(const void* X, const void* codes, const void* scales, const void* zeros,
+                      void* Y, int64_t K, int64_t N, int32_t G, int num_cus, hipStream_t stream) {
+    constexpr int RPB = 256 / TG;
+    const size_t lds = row_lds_bytes(K, G, BITS, TG);
+    static thread_local size_t cached_lds = (size_t)-1;
+    static thread_local int cached_per_cu = 1;
+    if (cached_lds != lds) {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, gemv_row_kernel<BITS, TG, CPT, HL>, 256, lds) !=
+                hipSuccess || v <= 0)
+            v = 1;
+        cached_lds = lds;
+        cached_per_cu = v;
+    }
+    const int64_t passes = (N + RPB - 1) / RPB;
+    const int64_t cap = (int64_t)num_cus * cached_per_cu;
+    gemv_row_kernel<BITS, TG, CPT, HL><<<dim3((unsigned)(passes < cap ? passes : cap)), dim3(256), lds, stream>>>(
+        static_cast<const uint16_t*>(X), static_cast<const uint4*>(codes),
+        static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
+        static_cast<uint16_t*>(Y), N, K, G);
+    return hipGetLastError();
+}
+
+template <int BITS, int TG, int CPT>
+hipError_t row_by_hl(int hl, const void* X, const void* codes, const void* scales, const void* zeros,
+                     void* Y, int64_t K, int64_t N, int32_t G, int cus, hipStream_t st) {
+    if (hl == 1) return launch_row<BITS, TG, CPT, 1>(X, codes, scales, zeros, Y, K, N, G, cus, st);
+    if constexpr (CPT >= 2)
+        if (hl == 2) return launch_row<BITS, TG, CPT, 2>(X, codes, scales, zeros, Y, K, N, G, cus, st);
+    if constexpr (CPT >= 4)
+        if (hl == 4) return launch_row<BITS, TG, CPT, 4>(X, codes, scales, zeros, Y, K, N, G, cus, st);
+    return hipErrorInvalidValue;
+}
+
+template <int BITS, int TG>
+hipError_t row_by_cpt(int cpt, int hl, const void* X, const void* codes, const void* scales,
+                      const void* zeros, void* Y, int64_t K, int64_t N, int32_t G, int cus,
+                      hipStream_t st) {
+    switch (cpt) {
+        case 1: return row_by_hl<BITS, TG, 1>(hl, X, codes, scales, zeros, Y, K, N, G, cus, st);
+        case 2: return row_by_hl<BITS, TG, 2>(hl, X, codes, scales, zeros, Y, K, N, G, cus, st);
+        case 4: return row_by_hl<BITS, TG, 4>(hl, X, codes, scales, zeros, Y, K, N, G, cus, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// The one-row kernel applies when a row fits one wave, its group count is
+// even and the header arrays allow 32-bit loads.  HL = header words per thread.
+bool row_path(int64_t B, int64_t K, int32_t G, const GemvChoice& ch, const void* scales,
+              const void* zeros, int& hl) {
+    if (B != 1 || ch.tg > 64) return false;
+    const int64_t ngrp = K / G;
+    if (ngrp % 2 != 0 || reinterpret_cast<uintptr_t>(scales) % 4 != 0 ||
+        reinterpret_cast<uintptr_t>(zeros) % 4 != 0)
+        return false;
+    const int64_t need = (ngrp + ch.tg - 1) / ch.tg;   // 2 * (ngrp / 2) words over TG threads
+    hl = need <= 1 ? 1 : need <= 2 ? 2 : 4;
+    return hl <= ch.cpt;
+}
+
 }  // namespace
 
 bool gemv_supports(int64_t K, int32_t bits) {
@@ -435,6 +700,24 @@ hipError_t launch_gemv(const void* X, const void* codes, const void* scales,
                        int32_t group, int32_t bits, int num_cus, hipStream_t stream) {
     GemvChoice ch;
     if (!choose(B, K, bits, ch)) return hipErrorInvalidValue;
+    int hl = 0;
+    if (row_path(B, K, group, ch, scales, zeros, hl)) {
+        const int cus = num_cus;
+        if (bits == 4) {
+            switch (ch.tg) {
+                case 16: return row_by_cpt<4, 16>(ch.cpt, hl, X, codes, scales, zeros, Y, K, N, group, cus, stream);
+                case 32: return row_by_cpt<4, 32>(ch.cpt, hl, X, codes, scales, zeros, Y, K, N, group, cus, stream);
+                case 64: return row_by_cpt<4, 64>(ch.cpt, hl, X, codes, scales, zeros, Y, K, N, group, cus, stream);
+            }
+        } else {
+            switch (ch.tg) {
+                case 16: return row_by_cpt<8, 16>(ch.cpt, hl, X, codes, scales, zeros, Y, K, N, group, cus, stream);
+                case 32: return row_by_cpt<8, 32>(ch.cpt, hl, X, codes, scales, zeros, Y, K, N, group, cus, stream);
+                case 64: return row_by_cpt<8, 64>(ch.cpt, hl, X, codes, scales, zeros, Y, K, N, group, cus, stream);
+            }
+        }
+        return hipErrorInvalidValue;
+    }
     if (bits == 4)
         return by_shape<4>(ch, X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
     return by_shape<8>(ch, X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
