@@ -70,6 +70,30 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// Buffer resource word 3 for raw (unformatted, unswizzled) gfx9 buffers.
+constexpr int kBufferWord3 = 0x00020000;
+
+// 128-bit streaming load through a buffer resource (nt cache policy).
+__device__ __forceinline__ uint4 load_stream_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 2);
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// Sum over aligned groups of W lanes (W in {16, 32, 64}), complete in the last
+// lane of each group: row sums by DPP within 16 lanes, then row broadcasts
+// (lane 15 of a row into the next row, lane 31 into rows 2 and 3) instead of
+// cross-row shuffles through LDS.
+template <int W>
+__device__ __forceinline__ float group_total_last(float v) {
+    v = group_sum<16>(v);
+    if constexpr (W >= 32)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+    if constexpr (W >= 64)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+    return v;
+}
+
 // X lives in LDS for the whole kernel as one record per (batch row, chunk):
 //   QPC uint4   the chunk's fp16 X pairs in the order its codes unpack;
 //   float2      (K0, xT): xT = sum of the chunk's X, and K0 the constant that
@@ -354,7 +378,10 @@ __global__ __launch_bounds__(256) void gemv_row_kernel(
     const int ngrp = (int)(K / G);
     const int cpg = G / CG::VALS;
     const int S = ngrp / 2;                     // header words per array and row
-    const int64_t passes = (N + RPB - 1) / RPB;
+    // Row and pass indices fit 32 bits (the launcher checks N), which keeps
+    // their compares on the scalar unit.
+    const int Nr = (int)N;
+    const int passes = (Nr + RPB - 1) / RPB;
     uint4* xrec = reinterpret_cast<uint4*>(smem);
     const uint32_t m_lo = vgpr_const(BITS == 4 ? 0x000F000Fu : 0x00FF00FFu);
     const uint32_t m_hi = vgpr_const(0x00F000F0u);
@@ -389,20 +416,32 @@ __global__ __launch_bounds__(256) void gemv_row_kernel(
         hst[h] = 4 * wm + (isz ? 1 : 0);
     }
 
-    // Every load is unconditional (passes past the end reread the last row),
-    // so the next pass stays in flight while the current one computes.
-    auto load_pass = [&](int64_t pass, uint4* w, uint32_t* hw) {
-        int64_t n = pass * RPB + rs;
-        n = n < N ? n : N - 1;
-        const char* rowc = reinterpret_cast<const char*>(codes + n * C);
+    // Every load is issued unconditionally, so the next pass stays in flight
+    // while the current one computes.  With TG == 64 a wave owns one row, and
+    // its codes are read through a buffer resource: scalar base, per-lane
+    // 32-bit offsets, and a record count of zero for rows past the end, which
+    // then read zeros without touching memory.  Narrower groups (several rows
+    // per wave) reread the last row instead.
+    auto load_pass = [&](int pass, uint4* w, uint32_t* hw) {
+        int n = pass * RPB + rs;
+        const bool live = n < Nr;
+        n = live ? n : Nr - 1;
+        if constexpr (TG == 64) {
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint4*>(codes + (int64_t)n * C), (short)0, live ? C * 16 : 0, kBufferWord3);
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) w[i] = load_stream(reinterpret_cast<const uint4*>(rowc + coff[i]));
-        const char* rowh = reinterpret_cast<const char*>(scales + n * ngrp);
+            for (int i = 0; i < CPT; ++i) w[i] = load_stream_buf(rsrc, coff[i]);
+        } else {
+            const char* rowc = reinterpret_cast<const char*>(codes + (int64_t)n * C);
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) w[i] = load_stream(reinterpret_cast<const uint4*>(rowc + coff[i]));
+        }
+        const char* rowh = reinterpret_cast<const char*>(scales + (int64_t)n * ngrp);
 #pragma unroll
         for (int h = 0; h < HL; ++h) hw[h] = *reinterpret_cast<const uint32_t*>(rowh + hoff[h]);
     };
 
-    int64_t pass = blockIdx.x;
+    int pass = blockIdx.x;
     uint4 wA[CPT], wB[CPT];
     uint32_t hA[HL], hB[HL];
 #pragma unroll
@@ -454,8 +493,8 @@ __global__ __launch_bounds__(256) void gemv_row_kernel(
 
     float2* hrow = reinterpret_cast<float2*>(smem + (size_t)(C + 1) * REC * 16) + (size_t)rs * ngrp;
     float* hf = reinterpret_cast<float*>(hrow);
-    auto compute_pass = [&](int64_t ps, const uint4* w, const uint32_t* hw) {
-        const int64_t n = ps * RPB + rs;
+    auto compute_pass = [&](int ps, const uint4* w, const uint32_t* hw) {
+        const int n = ps * RPB + rs;
 #pragma unroll
         for (int h = 0; h < HL; ++h) {
             hf[hst[h]] = half_bits_to_float((uint16_t)(hw[h] & 0xFFFFu));
@@ -466,11 +505,11 @@ __global__ __launch_bounds__(256) void gemv_row_kernel(
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const float2 sz = hrow[gix[i]];
-            // Opaque address: keeps the record reads in the pass loop and after
-            // the previous chunk's math (bounds the registers in flight).
-            uint32_t xa = xaddr[i];
-            asm volatile("" : "+v"(xa) : "v"(acc));
-            const uint4* rec = reinterpret_cast<const uint4*>(smem + xa);
+            // The address is made opaque in place: the record reads stay in
+            // the pass loop, after the previous chunk's math (which bounds the
+            // registers in flight), at no instruction cost.
+            asm volatile("" : "+v"(xaddr[i]) : "v"(acc));
+            const uint4* rec = reinterpret_cast<const uint4*>(smem + xaddr[i]);
             const uint4 kx = rec[QPC];
             float pa = __builtin_bit_cast(float, kx.x);
             const float xt = __builtin_bit_cast(float, kx.y);
@@ -502,18 +541,23 @@ __global__ __launch_bounds__(256) void gemv_row_kernel(
             t = __builtin_fmaf(-sz.y, xt, t);
             acc = __builtin_fmaf(sz.x, t, acc);
         }
-        acc = group_sum<TG>(acc);
-        if (tl == 0 && n < N) Y[n] = float_to_half_bits_rne(acc);
+        acc = group_total_last<TG>(acc);
+        if (tl == TG - 1 && n < Nr) Y[n] = float_to_half_bits_rne(acc);
         wave_lds_sync();
     };
 
-    const int64_t step = gridDim.x;
+    // The scheduling barriers keep each pass's loads ahead of the previous
+    // pass's math (the header staging would otherwise be hoisted above them
+    // and wait for every load in flight).
+    const int step = gridDim.x;
     while (pass < passes) {
         load_pass(pass + step, wB, hB);
+        __builtin_amdgcn_sched_barrier(0);
         compute_pass(pass, wA, hA);
         pass += step;
         if (pass >= passes) break;
         load_pass(pass + step, wA, hA);
+        __builtin_amdgcn_sched_barrier(0);
         compute_pass(pass, wB, hB);
         pass += step;
     }
@@ -676,9 +720,9 @@ hipError_t row_by_cpt(int cpt, int hl, const void* X, const void* codes, const v
 
 // The one-row kernel applies when a row fits one wave, its group count is
 // even and the header arrays allow 32-bit loads.  HL = header words per thread.
-bool row_path(int64_t B, int64_t K, int32_t G, const GemvChoice& ch, const void* scales,
-              const void* zeros, int& hl) {
-    if (B != 1 || ch.tg > 64) return false;
+bool row_path(int64_t B, int64_t K, int64_t N, int32_t G, const GemvChoice& ch,
+              const void* scales, const void* zeros, int& hl) {
+    if (B != 1 || ch.tg > 64 || N >= ((int64_t)1 << 31) - 256) return false;
     const int64_t ngrp = K / G;
     if (ngrp % 2 != 0 || reinterpret_cast<uintptr_t>(scales) % 4 != 0 ||
         reinterpret_cast<uintptr_t>(zeros) % 4 != 0)
@@ -701,7 +745,7 @@ hipError_t launch_gemv(const void* X, const void* codes, const void* scales,
     GemvChoice ch;
     if (!choose(B, K, bits, ch)) return hipErrorInvalidValue;
     int hl = 0;
-    if (row_path(B, K, group, ch, scales, zeros, hl)) {
+    if (row_path(B, K, N, group, ch, scales, zeros, hl)) {
         const int cus = num_cus;
         if (bits == 4) {
             switch (ch.tg) {
