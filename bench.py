@@ -88,7 +88,7 @@ KERNEL_SOURCES = {
     "quantize": ["wq_quantize.hip", "wq_device.h"],
 }
 # rocprofv3 kernel-name fragment of each family.
-KERNEL_NAMES = {"gemv": "gemv_kernel", "mfma": "gemm_mfma_kernel", "xr": "gemm_xr_kernel",
+KERNEL_NAMES = {"gemv": "gemv_", "mfma": "gemm_mfma_kernel", "xr": "gemm_xr_kernel",
                 "quantize": "quantize_"}
 
 
