@@ -417,7 +417,9 @@ def run_decode_set(args):
     """The 7B-class decode step: 32 layers x (q, k, v, o, gate, up, down) at
     B = 32, int4 group 128 and 8-bit per-channel.  Every matrix has its own
     packed weights in HBM (3.4 GB at int4, 6.5 GB at 8 bits), so nothing is
-    served from a cache; weights are drawn on the GPU, N(0, 0.02), fp16."""
+    served from a cache; weights are drawn on the GPU, N(0, 0.02), fp16.
+    The step is timed as one wq_gemm_grouped call per layer (the headline)
+    and as one wq_gemm call per matrix, each eagerly and from a HIP graph."""
     import torch
 
     import bit_weight_only_wq_amd as wq
@@ -439,24 +441,38 @@ def run_decode_set(args):
                 del W
         Xs = {K: torch.randn((B, K), generator=gen, device=dev).half()
               for K in {k for _, _, k in wq_inputs.DECODE_SET_SHAPES}}
-        Ys = {N: torch.empty((B, N), dtype=torch.float16, device=dev)
-              for N in {n for _, n, _ in wq_inputs.DECODE_SET_SHAPES}}
+        # One output per matrix of a layer (grouped products need distinct
+        # outputs); layers reuse them in stream order.
+        per_layer = len(wq_inputs.DECODE_SET_SHAPES)
+        Ys = [torch.empty((B, N), dtype=torch.float16, device=dev)
+              for _, N, _ in wq_inputs.DECODE_SET_SHAPES]
         torch.cuda.synchronize()
 
         lib = wq.load()
         stream = torch.cuda.current_stream(dev)
         hs = stream.cuda_stream
-        calls = [(Xs[K].data_ptr(), c.data_ptr(), s.data_ptr(), z.data_ptr(), Ys[N].data_ptr(),
-                  B, K, N, G) for N, K, G, c, s, z in mats]
+        calls = [(Xs[K].data_ptr(), c.data_ptr(), s.data_ptr(), z.data_ptr(),
+                  Ys[i % per_layer].data_ptr(), B, K, N, G)
+                 for i, (N, K, G, c, s, z) in enumerate(mats)]
+        from bit_weight_only_wq_amd._lib import GemmItem
+        layers = []
+        for l0 in range(0, len(calls), per_layer):
+            arr = (GemmItem * per_layer)()
+            for j, (x, c, s, z, y, b, k, n, g) in enumerate(calls[l0:l0 + per_layer]):
+                arr[j] = GemmItem(x, c, s, z, y, b, k, n, g, bits)
+            layers.append(arr)
 
-        def step_on(h):
+        def single_on(h):
             for x, c, s, z, y, b, k, n, g in calls:
                 st = lib.wq_gemm(x, c, s, z, y, b, k, n, g, bits, h)
                 if st:
                     wq.check(st, "wq_gemm")
 
-        def step():
-            step_on(hs)
+        def grouped_on(h):
+            for arr in layers:
+                st = lib.wq_gemm_grouped(arr, per_layer, h)
+                if st:
+                    wq.check(st, "wq_gemm_grouped")
 
         def timed(fn, reps):
             e0 = torch.cuda.Event(enable_timing=True)
@@ -469,26 +485,34 @@ def run_decode_set(args):
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
 
+        def graph_ms(step_on):
+            # Replayed from a HIP graph: no host launch gaps.  The capture
+            # stream's workspace is created by eager calls first, so capture
+            # records kernels only.
+            cap = torch.cuda.Stream()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(cap):
+                step_on(cap.cuda_stream)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=cap):
+                step_on(cap.cuda_stream)
+            graph.replay()
+            return timed(graph.replay, 5)
+
         for _ in range(2):
-            step()
-        ms_eager = timed(step, 5)
-        # The same 224 launches replayed from a HIP graph: no host launch gaps.
-        # The capture stream's workspace is created by eager calls first, so
-        # capture records kernels only.
-        cap = torch.cuda.Stream()
-        torch.cuda.synchronize()
-        with torch.cuda.stream(cap):
-            step_on(cap.cuda_stream)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=cap):
-            step_on(cap.cuda_stream)
-        graph.replay()
-        ms = timed(graph.replay, 5)
+            single_on(hs)
+            grouped_on(hs)
+        ms_single_eager = timed(lambda: single_on(hs), 5)
+        ms_eager = timed(lambda: grouped_on(hs), 5)
+        ms_single = graph_ms(single_on)
+        ms = graph_ms(grouped_on)
         nbytes = sum(rl.gemm_bytes(B, N, K, G, bits) for N, K, G, *_ in mats)
         flops = sum(rl.gemm_flops(B, N, K) for N, K, *_ in mats)
         row = {"decode_set": label, "matrices": len(mats), "B": B, "ms_per_step": round(ms, 4),
                "ms_per_step_eager": round(ms_eager, 4),
+               "ms_per_step_one_call_per_matrix": round(ms_single, 4),
+               "ms_per_step_one_call_per_matrix_eager": round(ms_single_eager, 4),
                "GBps": round(nbytes / ms / 1e6, 1), "TFLOPs": round(flops / ms / 1e9, 2),
                "bytes_per_step": int(nbytes)}
         print(json.dumps(row), flush=True)

@@ -76,6 +76,46 @@ def quantize_pack(W, group: int = 128, bits: int = 4, out=None):
     return codes, scales, zeros
 
 
+def gemm_grouped(items):
+    """Several products in one call: items is a sequence of
+    (X, codes, scales, zeros, N, K, group, bits[, out]) tuples; returns the Y
+    tensors in order (each exactly what gemm() gives for its item)."""
+    import ctypes
+    import torch
+    from ._lib import GemmItem
+    lib = load()
+    arr = (GemmItem * max(len(items), 1))()
+    outs = []
+    dev = None
+    for i, it in enumerate(items):
+        X, codes, scales, zeros, N, K, group, bits = it[:8]
+        out = it[8] if len(it) > 8 else None
+        if X.dim() != 2:
+            raise ValueError("X must be 2-D [B, K]")
+        B = X.shape[0]
+        _need(X, torch.float16, (B, K), "X")
+        _need(codes, torch.uint8, (N, K * bits // 8), "codes")
+        _need(scales, torch.float16, (N, K // group), "scales")
+        _need(zeros, torch.float16, (N, K // group), "zeros")
+        if dev is None:
+            dev = X.device
+        elif X.device != dev:
+            raise ValueError("all items must be on one device")
+        if out is None:
+            out = torch.empty((B, N), dtype=torch.float16, device=X.device)
+        else:
+            _need(out, torch.float16, (B, N), "out")
+        outs.append(out)
+        arr[i] = GemmItem(X.data_ptr(), codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                          out.data_ptr(), B, K, N, group, bits)
+    if not items:
+        return outs
+    with torch.cuda.device(dev):
+        st = lib.wq_gemm_grouped(arr, len(items), _stream_handle(dev))
+    check(st, "wq_gemm_grouped")
+    return outs
+
+
 def gemm(X, codes, scales, zeros, N: int, K: int, group: int = 128, bits: int = 4,
          path: str = "auto", out=None):
     """Y fp16 [B, N] = X fp16 [B, K] times the dequantized [N, K] matrix, transposed."""

@@ -22,10 +22,19 @@ WQ_PATH_MFMA = 2
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
+
+
+class GemmItem(ctypes.Structure):
+    """wq_gemm_item: the arguments of one wq_gemm call."""
+    _fields_ = [("X", _P), ("codes", _P), ("scales", _P), ("zeros", _P), ("Y", _P),
+                ("B", _I64), ("K", _I64), ("N", _I64), ("group", _I32), ("bits", _I32)]
+
+
 SIGNATURES = {
     "wq_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _P, _P, _P]),
     "wq_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P]),
     "wq_gemm_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
+    "wq_gemm_grouped": (ctypes.c_int, [ctypes.POINTER(GemmItem), _I32, _P]),
     "wq_gemv_max_batch": (_I32, []),
     "wq_codes_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
     "wq_num_groups": (_I64, [_I64, _I64, _I32]),

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <new>
+
 #include "wq.h"
 #include "wq_launch.h"
 
@@ -94,10 +96,12 @@ wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, i
                      "wq_quantize_pack launch");
 }
 
-wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales, const void* zeros,
-                     void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
-                     int32_t path, void* stream) {
-    g_last_error[0] = '\0';
+// Validates one product and picks its kernel family (path on return); does
+// not enqueue anything.  A no-op product (B == 0 or N == 0) returns WQ_OK with
+// path = -1.
+static wq_status check_gemm(const void* X, const void* codes, const void* scales,
+                            const void* zeros, const void* Y, int64_t B, int64_t K, int64_t N,
+                            int32_t group, int32_t bits, int32_t& path) {
     if (B < 0 || N < 0 || K < 1 || group < 1)
         return fail(WQ_ERR_INVALID_ARG, "wq_gemm: need B >= 0, N >= 0, K >= 1, group >= 1 (B=%lld K=%lld)", B, K);
     if (K % group != 0)
@@ -111,7 +115,10 @@ wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales, const
     if (K % vals != 0 || group % vals != 0)
         return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: K=%lld and group=%lld must be multiples of the 16-byte chunk",
                     K, group);
-    if (B == 0 || N == 0) return WQ_OK;
+    if (B == 0 || N == 0) {
+        path = -1;
+        return WQ_OK;
+    }
     if (!X || !codes || !scales || !zeros || !Y)
         return fail(WQ_ERR_INVALID_ARG, "wq_gemm: null pointer");
     if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(Y, 2))
@@ -129,13 +136,86 @@ wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales, const
     if (use == WQ_PATH_MFMA && !mfma_ok)
         return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: MFMA path needs group %% %lld == 0 (group=%lld)",
                     bits == 4 ? 128 : 64, group);
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    path = use;
+    return WQ_OK;
+}
+
+static wq_status run_gemm(const void* X, const void* codes, const void* scales, const void* zeros,
+                          void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                          int32_t use, hipStream_t st) {
     if (use == WQ_PATH_MFMA)
         return check_hip(wq::launch_gemm_mfma(X, codes, scales, zeros, Y, B, K, N, group, bits,
                                               num_cus(), st),
                          "wq_gemm (mfma) launch");
     return check_hip(wq::launch_gemv(X, codes, scales, zeros, Y, B, K, N, group, bits, num_cus(), st),
                      "wq_gemm (gemv) launch");
+}
+
+wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales, const void* zeros,
+                     void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                     int32_t path, void* stream) {
+    g_last_error[0] = '\0';
+    int32_t use = path;
+    const wq_status st = check_gemm(X, codes, scales, zeros, Y, B, K, N, group, bits, use);
+    if (st != WQ_OK || use < 0) return st;
+    return run_gemm(X, codes, scales, zeros, Y, B, K, N, group, bits, use, static_cast<hipStream_t>(stream));
+}
+
+wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream) {
+    g_last_error[0] = '\0';
+    if (count < 0 || (count > 0 && !items))
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm_grouped: count=%lld, items=%lld (null)", count,
+                    (long long)(items != nullptr));
+    // Validate everything before enqueuing anything.
+    int32_t paths_small[64];
+    int32_t* paths = count <= 64 ? paths_small : new (std::nothrow) int32_t[count];
+    if (!paths) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_grouped: out of host memory (count=%lld)", count);
+    struct Release {
+        int32_t* p;
+        int32_t* small;
+        ~Release() { if (p != small) delete[] p; }
+    } release{paths, paths_small};
+    for (int32_t i = 0; i < count; ++i) {
+        const wq_gemm_item& it = items[i];
+        paths[i] = WQ_PATH_AUTO;
+        const wq_status st = check_gemm(it.X, it.codes, it.scales, it.zeros, it.Y, it.B, it.K, it.N,
+                                        it.group, it.bits, paths[i]);
+        if (st != WQ_OK) {
+            char msg[sizeof(g_last_error)];
+            snprintf(msg, sizeof(msg), "%s", g_last_error);
+            snprintf(g_last_error, sizeof(g_last_error), "item %d: %s", (int)i, msg);
+            return st;
+        }
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // X-resident products of one (B, bits) go out together, in item order;
+    // every other product is one wq_gemm.
+    wq::XrProduct group_buf[64];
+    for (int32_t i = 0; i < count; ++i) {
+        const wq_gemm_item& it = items[i];
+        if (paths[i] < 0) continue;
+        const bool xr = paths[i] == WQ_PATH_MFMA && wq::xr_supports(it.B, it.K, it.group, it.bits);
+        if (!xr) {
+            const wq_status s2 = run_gemm(it.X, it.codes, it.scales, it.zeros, it.Y, it.B, it.K, it.N,
+                                          it.group, it.bits, paths[i], st);
+            if (s2 != WQ_OK) return s2;
+            continue;
+        }
+        // Collect the not yet issued X-resident items of this (B, bits).
+        int n = 0;
+        for (int32_t j = i; j < count && n < 64; ++j) {
+            const wq_gemm_item& o = items[j];
+            if (paths[j] != WQ_PATH_MFMA || o.B != it.B || o.bits != it.bits ||
+                !wq::xr_supports(o.B, o.K, o.group, o.bits))
+                continue;
+            group_buf[n++] = wq::XrProduct{o.X, o.codes, o.scales, o.zeros, o.Y, o.K, o.N, o.group};
+            paths[j] = -1;  // issued
+        }
+        const wq_status s2 = check_hip(wq::launch_gemm_xr_many(group_buf, n, it.B, it.bits, num_cus(), st),
+                                       "wq_gemm_grouped (x-resident) launch");
+        if (s2 != WQ_OK) return s2;
+    }
+    return WQ_OK;
 }
 
 wq_status wq_gemm(const void* X, const void* codes, const void* scales, const void* zeros,

@@ -68,6 +68,47 @@ struct XrGeom {
     static constexpr int WAVES = xr_waves(BTX);
 };
 
+// One product of a launch, and the launch: up to XR_MAX_ITEMS products of
+// one batch size, bit width and header mode, passed by value (the kernel
+// reads the table from its argument segment with scalar loads).
+constexpr int XR_MAX_ITEMS = 8;
+
+struct XrItem {
+    const uint16_t* X;
+    const uint4* codes;
+    const uint16_t* scales;
+    const uint16_t* zeros;
+    uint16_t* Y;
+    float* part;          // fp32 partials [slices][B][N], or null with one slice
+    int64_t N, K, ngrp;
+    uint64_t rpg_magic;
+    int32_t RS;           // rounds per slice
+    int32_t per_slice;    // blocks per slice
+    int32_t slices;
+    int32_t block0;       // first block of this product
+};
+
+struct XrLaunch {
+    XrItem it[XR_MAX_ITEMS];
+    int64_t B;
+    int32_t count;
+};
+
+// The reduction of a launch: every product with several slices, its outputs
+// numbered from t0 in one flat index space.
+struct XrReduceItem {
+    const float* part;
+    uint16_t* Y;
+    int64_t count;        // B * N
+    int64_t t0;
+    int32_t slices;
+};
+
+struct XrReduce {
+    XrReduceItem it[XR_MAX_ITEMS];
+    int32_t count;
+};
+
 __device__ __forceinline__ uint32_t vreg(uint32_t v) {
     uint32_t r;
     asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
@@ -146,20 +187,36 @@ __device__ __forceinline__ float half_of(const uint4& v, int i) {
     return (i & 1) ? (float)as_h2(w).y : (float)as_h2(w).x;
 }
 
-// Grid: x = blocks sharing one K-slice, y = K-slice.  Slice y covers rounds
-// [y*RS, (y+1)*RS) (RS a multiple of XR_SLOTS; rounds past K meet zero X in
-// LDS and add nothing).  Tiles are 16 weight rows; wave w of block x owns
-// tiles w*gridDim.x + x + i*stride, so every block has work.  With several
-// slices, part receives fp32 partials [slice][b][n].  ngrp = K / G; for XR_HDR_ROUND the group of
-// round r is (r * rpg_magic) >> 32 = floor(r / (G / KR)), exact for r < 2^16
-// with rpg_magic = ceil(2^32 / (G / KR)).
+// Grid: one dimension over the products of the launch.  Product i owns blocks
+// [block0, block0 + per_slice * slices); its block b works on K-slice
+// b / per_slice, which covers rounds [slice*RS, (slice+1)*RS) (RS a multiple
+// of XR_SLOTS; rounds past K meet zero X in LDS and add nothing), as block
+// x = b % per_slice of that slice.  Tiles are 16 weight rows; wave w of
+// block x owns tiles w*per_slice + x + i*stride, so every block has work.
+// With several slices, part receives fp32 partials [slice][b][n].  For
+// XR_HDR_ROUND the group of round r is (r * rpg_magic) >> 32 =
+// floor(r / (G / KR)), exact for r < 2^16 with rpg_magic = ceil(2^32 / (G / KR)).
 template <int BITS, int BTX, int HM>
-__global__ __launch_bounds__(xr_waves(BTX) * 64) void gemm_xr_kernel(
-    const uint16_t* __restrict__ X, const uint4* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
-    uint16_t* __restrict__ Y, float* __restrict__ part, int64_t B, int64_t N, int64_t K,
-    int64_t ngrp, uint64_t rpg_magic, int32_t RS) {
+__global__ __launch_bounds__(xr_waves(BTX) * 64) void gemm_xr_kernel(const XrLaunch L) {
     typedef XrGeom<BITS, BTX> XG;
+    // This block's product (a uniform scan of the launch table).
+    int item = 0;
+#pragma unroll
+    for (int j = 1; j < XR_MAX_ITEMS; ++j)
+        if (j < L.count && (int)blockIdx.x >= L.it[j].block0) item = j;
+    const XrItem& P = L.it[item];
+    const uint16_t* __restrict__ X = P.X;
+    const uint4* __restrict__ codes = P.codes;
+    const uint16_t* __restrict__ scales = P.scales;
+    const uint16_t* __restrict__ zeros = P.zeros;
+    uint16_t* __restrict__ Y = P.Y;
+    float* __restrict__ part = P.part;
+    const int64_t B = L.B, N = P.N, K = P.K, ngrp = P.ngrp;
+    const uint64_t rpg_magic = P.rpg_magic;
+    const int32_t RS = P.RS;
+    const int lb = (int)blockIdx.x - P.block0;
+    const int slice = lb / P.per_slice;
+    const int bx = lb - slice * P.per_slice;
     constexpr int NCB = (BTX + 15) / 16;                   // 16-column blocks
     __shared__ __align__(16) uint16_t xs[BTX * XG::ROW];
     __shared__ __align__(16) float cneg1[XG::RMAX][BTX];   // -C1 per (round, column)
@@ -171,10 +228,10 @@ __global__ __launch_bounds__(xr_waves(BTX) * 64) void gemm_xr_kernel(
     const int r16 = lane & 15;
     const int g4 = lane >> 4;
     const int64_t rounds = K / XG::KR;
-    const int64_t round0 = (int64_t)blockIdx.y * RS;          // first round of the slice
+    const int64_t round0 = (int64_t)slice * RS;               // first round of the slice
     const int64_t ntiles = (N + 15) / 16;
-    const int64_t stride = (int64_t)gridDim.x * XG::WAVES;
-    const int64_t t0 = (int64_t)wave * gridDim.x + blockIdx.x;
+    const int64_t stride = (int64_t)P.per_slice * XG::WAVES;
+    const int64_t t0 = (int64_t)wave * P.per_slice + bx;
     const int64_t chunks_per_row = K / XG::VALS;
 
     // Weight row r16 of tile t, clamped to N - 1 (tiles past the end reread
@@ -393,7 +450,7 @@ __global__ __launch_bounds__(xr_waves(BTX) * 64) void gemm_xr_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int col = cb * 16 + 4 * g4 + i;
-                    if (col < bmax) part[((int64_t)blockIdx.y * B + col) * N + row] = tot[cb][i];
+                    if (col < bmax) part[((int64_t)slice * B + col) * N + row] = tot[cb][i];
                 }
             }
             tot[cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -411,27 +468,32 @@ __global__ __launch_bounds__(xr_waves(BTX) * 64) void gemm_xr_kernel(
     }
 }
 
-// Y = fp16(sum over slices of part[z]), slices added in order 0, 1, 2, ...
-__global__ __launch_bounds__(256) void xr_reduce_kernel(const float* __restrict__ part,
-                                                        uint16_t* __restrict__ Y, int64_t count,
-                                                        int slices) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count) return;
-    float s = part[i];
-    for (int z = 1; z < slices; ++z) s += part[(int64_t)z * count + i];
-    Y[i] = float_to_half_bits_rne(s);
+// Y = fp16(sum over slices of part[z]), slices added in order 0, 1, 2, ...,
+// for every product of the table (one flat index space over their outputs).
+__global__ __launch_bounds__(256) void xr_reduce_kernel(const XrReduce R) {
+    // Products start on 256-thread boundaries, so the product is uniform per block.
+    const int64_t g0 = (int64_t)blockIdx.x * 256;
+    int item = 0;
+#pragma unroll
+    for (int j = 1; j < XR_MAX_ITEMS; ++j)
+        if (j < R.count && g0 >= R.it[j].t0) item = j;
+    const XrReduceItem& P = R.it[item];
+    const int64_t i = g0 - P.t0 + threadIdx.x;
+    if (i >= P.count) return;
+    float s = P.part[i];
+    for (int z = 1; z < P.slices; ++z) s += P.part[(int64_t)z * P.count + i];
+    P.Y[i] = float_to_half_bits_rne(s);
 }
 
-template <int BITS, int BTX, int HM>
-hipError_t launch_xr_hm(const void* X, const void* codes, const void* scales, const void* zeros,
-                        void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int num_cus,
-                        hipStream_t stream) {
+// Slices, rounds per slice and blocks per slice of one product.  Slices: as
+// few as LDS allows, more when the tiles alone cannot give every compute
+// unit's waves work (each slice keeps at least one ring turn).
+template <int BITS, int BTX>
+bool xr_plan(int64_t K, int64_t N, int num_cus, int64_t& slices, int64_t& rs, int64_t& per_slice) {
     typedef XrGeom<BITS, BTX> XG;
     const int64_t rounds = K / XG::KR;
     const int64_t ntiles = (N + 15) / 16;
-    // Slices: as few as LDS allows, more when the tiles alone cannot give every
-    // compute unit's waves work (each slice keeps at least one ring turn).
-    int64_t slices = (rounds + XG::RMAX - 1) / XG::RMAX;
+    slices = (rounds + XG::RMAX - 1) / XG::RMAX;
     const int64_t want_items = (int64_t)num_cus * XG::WAVES / 2;
     if (ntiles * slices < want_items) {
         const int64_t s = (want_items + ntiles - 1) / ntiles;
@@ -439,49 +501,120 @@ hipError_t launch_xr_hm(const void* X, const void* codes, const void* scales, co
         slices = s < smax ? s : smax;
         if (slices < 1) slices = 1;
     }
-    int64_t rs = (rounds + slices - 1) / slices;
+    rs = (rounds + slices - 1) / slices;
     rs = (rs + XR_SLOTS - 1) / XR_SLOTS * XR_SLOTS;
-    if (rs > XG::RMAX) return hipErrorInvalidValue;
+    if (rs > XG::RMAX) return false;
     slices = (rounds + rs - 1) / rs;
-    int64_t per_slice = ((int64_t)num_cus + slices - 1) / slices;
+    per_slice = ((int64_t)num_cus + slices - 1) / slices;
     if (per_slice > ntiles) per_slice = ntiles;
     if (per_slice < 1) per_slice = 1;
-    const dim3 grid((unsigned)per_slice, (unsigned)slices);
-    const uint64_t rpg = (uint64_t)(G / XG::KR);
-    const uint64_t magic = ((1ull << 32) + rpg - 1) / rpg;
-    float* part = nullptr;
-    if (slices > 1) {
+    return true;
+}
+
+// How a product's kernel reads its group headers.
+template <int BITS, int BTX>
+int xr_mode(const XrProduct& p) {
+    typedef XrGeom<BITS, BTX> XG;
+    const int64_t ngrp = p.K / p.group;
+    const bool aligned16 = (reinterpret_cast<uintptr_t>(p.scales) % 16 == 0) &&
+                           (reinterpret_cast<uintptr_t>(p.zeros) % 16 == 0);
+    if (ngrp == 1) return XR_HDR_ROW;
+    if (p.group == XG::KR && ngrp % 8 == 0 && aligned16) return XR_HDR_TURN;
+    return XR_HDR_ROUND;
+}
+
+// One launch for up to XR_MAX_ITEMS products of one header mode, plus one
+// reduction launch for those of them that have several K-slices.  The fp32
+// partials of all of them share the stream's workspace.
+template <int BITS, int BTX, int HM>
+hipError_t launch_xr_items(const XrProduct* const* prods, int n, int64_t B, int num_cus,
+                           hipStream_t stream) {
+    typedef XrGeom<BITS, BTX> XG;
+    XrLaunch L{};
+    XrReduce R{};
+    size_t part_off[XR_MAX_ITEMS] = {};
+    size_t part_total = 0;
+    int64_t blocks = 0;
+    for (int i = 0; i < n; ++i) {
+        const XrProduct& p = *prods[i];
+        int64_t slices = 0, rs = 0, per_slice = 0;
+        if (!xr_plan<BITS, BTX>(p.K, p.N, num_cus, slices, rs, per_slice)) return hipErrorInvalidValue;
+        XrItem& it = L.it[i];
+        it.X = static_cast<const uint16_t*>(p.X);
+        it.codes = static_cast<const uint4*>(p.codes);
+        it.scales = static_cast<const uint16_t*>(p.scales);
+        it.zeros = static_cast<const uint16_t*>(p.zeros);
+        it.Y = static_cast<uint16_t*>(p.Y);
+        it.part = nullptr;
+        it.N = p.N;
+        it.K = p.K;
+        it.ngrp = p.K / p.group;
+        const uint64_t rpg = (uint64_t)(p.group / XG::KR);
+        it.rpg_magic = ((1ull << 32) + rpg - 1) / rpg;
+        it.RS = (int32_t)rs;
+        it.per_slice = (int32_t)per_slice;
+        it.slices = (int32_t)slices;
+        it.block0 = (int32_t)blocks;
+        blocks += per_slice * slices;
+        if (slices > 1) {
+            part_off[i] = part_total;
+            part_total += ((size_t)slices * B * p.N * sizeof(float) + 255) / 256 * 256;
+        }
+    }
+    L.B = B;
+    L.count = n;
+    if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    float* base = nullptr;
+    if (part_total > 0) {
         uint32_t* unused = nullptr;
-        hipError_t e = workspace_get(stream, 0, (size_t)slices * B * N * sizeof(float), &unused, &part);
+        const hipError_t e = workspace_get(stream, 0, part_total, &unused, &base);
         if (e != hipSuccess) return e;
     }
-    gemm_xr_kernel<BITS, BTX, HM><<<grid, dim3(XG::WAVES * 64), 0, stream>>>(
-        static_cast<const uint16_t*>(X), static_cast<const uint4*>(codes),
-        static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
-        static_cast<uint16_t*>(Y), part, B, N, K, K / G, magic, (int32_t)rs);
+    int64_t t = 0;
+    for (int i = 0; i < n; ++i) {
+        XrItem& it = L.it[i];
+        if (it.slices > 1) {
+            it.part = reinterpret_cast<float*>(reinterpret_cast<char*>(base) + part_off[i]);
+            XrReduceItem& r = R.it[R.count++];
+            r.part = it.part;
+            r.Y = it.Y;
+            r.count = B * it.N;
+            r.t0 = t;
+            r.slices = it.slices;
+            t += (r.count + 255) / 256 * 256;
+        }
+    }
+    gemm_xr_kernel<BITS, BTX, HM><<<dim3((unsigned)blocks), dim3(XG::WAVES * 64), 0, stream>>>(L);
     hipError_t e = hipGetLastError();
-    if (slices > 1 && e == hipSuccess) {
-        const int64_t count = B * N;
-        xr_reduce_kernel<<<dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream>>>(
-            part, static_cast<uint16_t*>(Y), count, (int)slices);
+    if (R.count > 0 && e == hipSuccess) {
+        xr_reduce_kernel<<<dim3((unsigned)(t / 256)), dim3(256), 0, stream>>>(R);
         e = hipGetLastError();
     }
     return e;
 }
 
+// Products of one batch size and bit width, grouped by header mode into
+// launches of at most XR_MAX_ITEMS products (in the given order within a mode).
 template <int BITS, int BTX>
-hipError_t launch_xr_bt(const void* X, const void* codes, const void* scales, const void* zeros,
-                        void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int num_cus,
+hipError_t launch_xr_bt(const XrProduct* prods, int count, int64_t B, int num_cus,
                         hipStream_t stream) {
-    typedef XrGeom<BITS, BTX> XG;
-    const int64_t ngrp = K / G;
-    const bool aligned16 = (reinterpret_cast<uintptr_t>(scales) % 16 == 0) &&
-                           (reinterpret_cast<uintptr_t>(zeros) % 16 == 0);
-    if (ngrp == 1)
-        return launch_xr_hm<BITS, BTX, XR_HDR_ROW>(X, codes, scales, zeros, Y, B, K, N, G, num_cus, stream);
-    if (G == XG::KR && ngrp % 8 == 0 && aligned16)
-        return launch_xr_hm<BITS, BTX, XR_HDR_TURN>(X, codes, scales, zeros, Y, B, K, N, G, num_cus, stream);
-    return launch_xr_hm<BITS, BTX, XR_HDR_ROUND>(X, codes, scales, zeros, Y, B, K, N, G, num_cus, stream);
+    for (int hm = 0; hm < 3; ++hm) {
+        const XrProduct* sel[XR_MAX_ITEMS];
+        int n = 0;
+        for (int i = 0; i <= count; ++i) {
+            const bool take = i < count && xr_mode<BITS, BTX>(prods[i]) == hm;
+            if (take) sel[n++] = &prods[i];
+            if (n == XR_MAX_ITEMS || (i == count && n > 0)) {
+                hipError_t e = hipSuccess;
+                if (hm == XR_HDR_ROUND) e = launch_xr_items<BITS, BTX, XR_HDR_ROUND>(sel, n, B, num_cus, stream);
+                else if (hm == XR_HDR_TURN) e = launch_xr_items<BITS, BTX, XR_HDR_TURN>(sel, n, B, num_cus, stream);
+                else e = launch_xr_items<BITS, BTX, XR_HDR_ROW>(sel, n, B, num_cus, stream);
+                if (e != hipSuccess) return e;
+                n = 0;
+            }
+        }
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -495,17 +628,24 @@ bool xr_supports(int64_t B, int64_t K, int32_t group, int32_t bits) {
     return B <= 16 || K <= 4 * XrGeom<4, 32>::KSL;
 }
 
+hipError_t launch_gemm_xr_many(const XrProduct* prods, int count, int64_t B, int32_t bits,
+                               int num_cus, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    if (bits == 4) {
+        if (B <= 8) return launch_xr_bt<4, 8>(prods, count, B, num_cus, stream);
+        if (B <= 16) return launch_xr_bt<4, 16>(prods, count, B, num_cus, stream);
+        return launch_xr_bt<4, 32>(prods, count, B, num_cus, stream);
+    }
+    if (B <= 8) return launch_xr_bt<8, 8>(prods, count, B, num_cus, stream);
+    if (B <= 16) return launch_xr_bt<8, 16>(prods, count, B, num_cus, stream);
+    return launch_xr_bt<8, 32>(prods, count, B, num_cus, stream);
+}
+
 hipError_t launch_gemm_xr(const void* X, const void* codes, const void* scales,
                           const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                           int32_t group, int32_t bits, int num_cus, hipStream_t stream) {
-    if (bits == 4) {
-        if (B <= 8) return launch_xr_bt<4, 8>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
-        if (B <= 16) return launch_xr_bt<4, 16>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
-        return launch_xr_bt<4, 32>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
-    }
-    if (B <= 8) return launch_xr_bt<8, 8>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
-    if (B <= 16) return launch_xr_bt<8, 16>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
-    return launch_xr_bt<8, 32>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+    const XrProduct p{X, codes, scales, zeros, Y, K, N, group};
+    return launch_gemm_xr_many(&p, 1, B, bits, num_cus, stream);
 }
 
 }  // namespace wq

@@ -23,6 +23,20 @@ bool xr_supports(int64_t B, int64_t K, int32_t group, int32_t bits);
 hipError_t launch_gemm_xr(const void* X, const void* codes, const void* scales,
                           const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                           int32_t group, int32_t bits, int num_cus, hipStream_t stream);
+// Several X-resident products of one batch size and bit width (each must
+// satisfy xr_supports): products sharing a header mode go into one launch of
+// up to eight, with one reduction launch for their K-slices.
+struct XrProduct {
+    const void* X;
+    const void* codes;
+    const void* scales;
+    const void* zeros;
+    void* Y;
+    int64_t K, N;
+    int32_t group;
+};
+hipError_t launch_gemm_xr_many(const XrProduct* prods, int count, int64_t B, int32_t bits,
+                               int num_cus, hipStream_t stream);
 bool mfma_supports(int64_t K, int32_t group, int32_t bits);
 hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales,
                             const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,

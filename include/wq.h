@@ -119,6 +119,37 @@ wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales,
                      const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                      int32_t group, int32_t bits, int32_t path, void* stream);
 
+/* The arguments of one wq_gemm call, for wq_gemm_grouped. */
+typedef struct wq_gemm_item {
+    const void* X;
+    const void* codes;
+    const void* scales;
+    const void* zeros;
+    void* Y;
+    int64_t B, K, N;
+    int32_t group, bits;
+} wq_gemm_item;
+
+/*
+ * Several products of a decode step (every weight matrix of a layer, say)
+ * enqueued together: each item's Y is exactly what wq_gemm (WQ_PATH_AUTO)
+ * would write for it, bit for bit.  The decode step reads each matrix once
+ * per token ("Quantization & inference optimisation", "Bandwidth, not
+ * compute"); small matrices then spend much of their time in launch ramp and
+ * split-K reduction, which grouping shares out.  Items that take the
+ * X-resident matrix-core kernel (3 <= B <= 32) and share B and bits run up to
+ * eight products per launch (one launch per group-header layout), plus one
+ * reduction launch; every other item runs as its own wq_gemm, in item order.
+ *
+ * items   host array of `count` items, read during the call and not kept
+ * count   >= 0 (0 is a no-op)
+ * Every item is validated as by wq_gemm before anything is enqueued; the
+ * first invalid item's status is returned (wq_last_error names the item) and
+ * nothing runs.  An item's Y must not overlap any item's inputs or another
+ * item's Y.  Items share the stream's split-K workspace.
+ */
+wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream);
+
 /* Largest batch that WQ_PATH_AUTO sends to the GEMV path when the MFMA path
  * can take the shape. */
 int32_t wq_gemv_max_batch(void);
@@ -139,7 +170,7 @@ const char* wq_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int32_t wq_version(void);
 
-#define WQ_VERSION 100
+#define WQ_VERSION 101
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = wq.load()
-    assert lib.wq_version() == 100
+    assert lib.wq_version() == 101
     for st in range(5):
         assert lib.wq_status_string(st)
     assert lib.wq_status_string(99) == b"unknown status"
@@ -98,3 +98,24 @@ def test_quantize_validation_errors():
 def test_binding_raises_on_error():
     with pytest.raises(wq.WQError):
         _lib.check(_gemm(K=250), "wq_gemm")
+
+
+def _item(B=4, K=256, N=64, group=128, bits=4, X=FAKE, C=FAKE, S=FAKE, Z=FAKE, Y=FAKE):
+    return _lib.GemmItem(X, C, S, Z, Y, B, K, N, group, bits)
+
+
+def test_grouped_validates_every_item_first():
+    """An invalid item anywhere makes the whole call fail before any launch;
+    the error names the item."""
+    lib = wq.load()
+    for bad, st in [(dict(K=200), _lib.WQ_ERR_INVALID_ARG), (dict(bits=3), _lib.WQ_ERR_UNSUPPORTED),
+                    (dict(X=FAKE + 2), _lib.WQ_ERR_MISALIGNED), (dict(Y=0), _lib.WQ_ERR_INVALID_ARG)]:
+        arr = (_lib.GemmItem * 3)(_item(), _item(B=32), _item(**bad))
+        assert lib.wq_gemm_grouped(arr, 3, None) == st
+        assert b"item 2" in lib.wq_last_error()
+    assert lib.wq_gemm_grouped(None, 2, None) == _lib.WQ_ERR_INVALID_ARG
+    assert lib.wq_gemm_grouped(None, -1, None) == _lib.WQ_ERR_INVALID_ARG
+    assert lib.wq_gemm_grouped(None, 0, None) == _lib.WQ_OK
+    # No-op items (B == 0 or N == 0) are valid and enqueue nothing.
+    arr = (_lib.GemmItem * 2)(_item(B=0), _item(N=0))
+    assert lib.wq_gemm_grouped(arr, 2, None) == _lib.WQ_OK
