@@ -511,6 +511,27 @@ bool xr_plan(int64_t K, int64_t N, int num_cus, int64_t& slices, int64_t& rs, in
     return true;
 }
 
+// Plan of a product launched together with others.  Their blocks run side by
+// side, so the other products supply the parallelism that extra K-slices give
+// a single product: every product keeps the fewest slices LDS allows, and its
+// blocks per slice are sized so that each wave of the whole launch gets about
+// `per_wave` tiles (this amortizes a block's X staging over more rounds).
+template <int BITS, int BTX>
+bool xr_plan_grouped(int64_t K, int64_t N, int64_t per_wave, int64_t& slices, int64_t& rs,
+                     int64_t& per_slice) {
+    typedef XrGeom<BITS, BTX> XG;
+    const int64_t rounds = K / XG::KR;
+    const int64_t ntiles = (N + 15) / 16;
+    slices = (rounds + XG::RMAX - 1) / XG::RMAX;
+    rs = (rounds + slices - 1) / slices;
+    rs = (rs + XR_SLOTS - 1) / XR_SLOTS * XR_SLOTS;
+    if (rs > XG::RMAX) return false;
+    slices = (rounds + rs - 1) / rs;
+    per_slice = (ntiles + XG::WAVES * per_wave - 1) / (XG::WAVES * per_wave);
+    if (per_slice < 1) per_slice = 1;
+    return true;
+}
+
 // How a product's kernel reads its group headers.
 template <int BITS, int BTX>
 int xr_mode(const XrProduct& p) {
@@ -535,10 +556,27 @@ hipError_t launch_xr_items(const XrProduct* const* prods, int n, int64_t B, int 
     size_t part_off[XR_MAX_ITEMS] = {};
     size_t part_total = 0;
     int64_t blocks = 0;
+    // Several products: tiles per wave from the launch's total (see
+    // xr_plan_grouped); one product keeps the single-product plan.
+    int64_t per_wave = 1;
+    if (n > 1) {
+        int64_t items = 0;
+        for (int i = 0; i < n; ++i) {
+            int64_t slices = 0, rs = 0, per_slice = 0;
+            if (!xr_plan_grouped<BITS, BTX>(prods[i]->K, prods[i]->N, 1, slices, rs, per_slice))
+                return hipErrorInvalidValue;
+            items += (prods[i]->N + 15) / 16 * slices;
+        }
+        const int64_t slots = (int64_t)num_cus * XG::WAVES;
+        per_wave = (items + slots - 1) / slots;
+        if (per_wave < 1) per_wave = 1;
+    }
     for (int i = 0; i < n; ++i) {
         const XrProduct& p = *prods[i];
         int64_t slices = 0, rs = 0, per_slice = 0;
-        if (!xr_plan<BITS, BTX>(p.K, p.N, num_cus, slices, rs, per_slice)) return hipErrorInvalidValue;
+        const bool ok = n > 1 ? xr_plan_grouped<BITS, BTX>(p.K, p.N, per_wave, slices, rs, per_slice)
+                              : xr_plan<BITS, BTX>(p.K, p.N, num_cus, slices, rs, per_slice);
+        if (!ok) return hipErrorInvalidValue;
         XrItem& it = L.it[i];
         it.X = static_cast<const uint16_t*>(p.X);
         it.codes = static_cast<const uint4*>(p.codes);

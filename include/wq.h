@@ -132,14 +132,17 @@ typedef struct wq_gemm_item {
 
 /*
  * Several products of a decode step (every weight matrix of a layer, say)
- * enqueued together: each item's Y is exactly what wq_gemm (WQ_PATH_AUTO)
- * would write for it, bit for bit.  The decode step reads each matrix once
- * per token ("Quantization & inference optimisation", "Bandwidth, not
- * compute"); small matrices then spend much of their time in launch ramp and
- * split-K reduction, which grouping shares out.  Items that take the
- * X-resident matrix-core kernel (3 <= B <= 32) and share B and bits run up to
- * eight products per launch (one launch per group-header layout), plus one
- * reduction launch; every other item runs as its own wq_gemm, in item order.
+ * enqueued together; each item computes what wq_gemm (WQ_PATH_AUTO) computes
+ * for it.  The decode step reads each matrix once per token ("Quantization &
+ * inference optimisation", "Bandwidth, not compute"); small matrices then
+ * spend much of their time in launch ramp, X staging and split-K reduction,
+ * which grouping shares out.  Items that take the X-resident matrix-core
+ * kernel (3 <= B <= 32) and share B and bits run up to eight products per
+ * launch (one launch per group-header layout), plus one reduction launch;
+ * every other item runs as its own wq_gemm, in item order.  A launch of
+ * several products splits K into fewer slices than single calls do, so their
+ * fp32 sums may differ from wq_gemm's in the last bits (same tolerance);
+ * results are deterministic for a given list of items.
  *
  * items   host array of `count` items, read during the call and not kept
  * count   >= 0 (0 is a no-op)

@@ -1,5 +1,6 @@
-"""GPU parity of wq_gemm_grouped: every item's output is bit-identical to a
-separate wq_gemm call on the same inputs, and matches the CPU oracle.
+"""GPU parity of wq_gemm_grouped: every item matches the CPU oracle and a
+separate wq_gemm call on the same inputs (to the product tolerance: grouped
+launches slice K differently), and repeated grouped calls agree bit for bit.
 
 Grouping puts the X-resident products of one batch size and bit width into
 shared launches (up to eight per launch, one launch per group-header layout,
@@ -37,14 +38,30 @@ def single(item):
     return wq.gemm(X, c, s, z, N=N, K=K, group=group, bits=bits)
 
 
-def assert_bitwise(outs, items):
+def assert_matches_single(outs, items):
+    """Each grouped output is within the product tolerance of a single call,
+    and a second grouped call reproduces every output bit for bit."""
     torch.cuda.synchronize()
-    for i, (y, it) in enumerate(zip(outs, items)):
-        ref = single(it)
-        torch.cuda.synchronize()
-        a = y.cpu().numpy().view(np.uint16)
-        b = ref.cpu().numpy().view(np.uint16)
-        assert np.array_equal(a, b), f"item {i}: B={it[0].shape[0]} N={it[4]} K={it[5]} G={it[6]} b={it[7]}"
+    again = wq.gemm_grouped(items)
+    torch.cuda.synchronize()
+    for i, (y, y2, it) in enumerate(zip(outs, again, items)):
+        what = f"item {i}: B={it[0].shape[0]} N={it[4]} K={it[5]} G={it[6]} b={it[7]}"
+        a = y.cpu().numpy()
+        assert np.array_equal(a.view(np.uint16), y2.cpu().numpy().view(np.uint16)), what
+        ref = single(it).cpu().numpy().astype(np.float64)
+        if ref.size:
+            assert_close(a.astype(np.float64), ref, what)
+
+
+def assert_matches_oracle(outs, items, hosts, rng, nrows=40):
+    """Sampled rows of every item against the oracle (rows are independent,
+    so the oracle quantizes and multiplies only those)."""
+    for i, (y, it, (X, W)) in enumerate(zip(outs, items, hosts)):
+        N, K, G, bits = it[4], it[5], it[6], it[7]
+        rows = np.sort(rng.choice(N, min(nrows, N), replace=False))
+        c, s, z = oracle.quantize(W[rows], G, bits)
+        ref = oracle.gemm(X, c, s, z, len(rows), K, G, bits)
+        assert_close(y.cpu().numpy().astype(np.float64)[:, rows], ref, f"item {i} vs oracle")
 
 
 def test_mixed_items_match_single_calls():
@@ -64,27 +81,30 @@ def test_mixed_items_match_single_calls():
         (5, 90, 1024, 128, 4),      # x-resident, 8-column tile
         (24, 210, 4096, 128, 4),    # x-resident, two column blocks per wave
     ]
-    items = [make_item(rng, *sp) for sp in specs]
+    made = [make_item(rng, *sp, host=True) for sp in specs]
+    items = [m[0] for m in made]
     note(f"grouped mixed: {len(items)} items")
     outs = wq.gemm_grouped(items)
-    assert_bitwise(outs, items)
+    assert_matches_single(outs, items)
+    assert_matches_oracle(outs, items, [m[1] for m in made], rng)
 
 
 def test_more_than_eight_grouped_products():
     """Eleven products of one kind take two grouped launches."""
     device()
     rng = np.random.default_rng(22)
-    items = [make_item(rng, 12, 64 + 37 * i, 2048 + 1024 * (i % 3), 128, 4) for i in range(11)]
+    made = [make_item(rng, 12, 64 + 37 * i, 2048 + 1024 * (i % 3), 128, 4, host=True) for i in range(11)]
+    items = [m[0] for m in made]
     note("grouped: 11 products at B=12")
     outs = wq.gemm_grouped(items)
-    assert_bitwise(outs, items)
+    assert_matches_single(outs, items)
+    assert_matches_oracle(outs, items, [m[1] for m in made], rng)
 
 
 @pytest.mark.parametrize("bits,group", [(4, 128), (8, None)])
 def test_decode_layer_at_b32(bits, group):
     """The seven matrices of a 7B-class layer (int4 g128 or 8-bit per-channel)
-    at B = 32 in one call; four of them are also checked against the oracle
-    on sampled rows."""
+    at B = 32 in one call, each checked against the oracle on sampled rows."""
     device()
     rng = np.random.default_rng(23 + bits)
     shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]
@@ -96,18 +116,8 @@ def test_decode_layer_at_b32(bits, group):
         hosts.append(h)
     note(f"grouped decode layer b={bits}")
     outs = wq.gemm_grouped(items)
-    assert_bitwise(outs, items)
-    for idx in (0, 3, 4, 6):
-        X, W = hosts[idx]
-        N, K = shapes[idx]
-        G = group if group else K
-        # Rows are independent: the oracle quantizes and multiplies only the
-        # sampled ones.
-        rows = np.sort(rng.choice(N, 48, replace=False))
-        c, s, z = oracle.quantize(W[rows], G, bits)
-        ref = oracle.gemm(X, c, s, z, len(rows), K, G, bits)
-        y = outs[idx].cpu().numpy().astype(np.float64)[:, rows]
-        assert_close(y, ref, f"layer item {idx}")
+    assert_matches_single(outs, items)
+    assert_matches_oracle(outs, items, hosts, rng, nrows=48)
 
 
 def test_empty_and_noop_items():
@@ -119,4 +129,6 @@ def test_empty_and_noop_items():
     empty = (X[:0], c, s, z, N, K, G, b)
     outs = wq.gemm_grouped([empty, it])
     assert outs[0].shape == (0, N)
-    assert_bitwise(outs[1:], [it])
+    torch.cuda.synchronize()
+    # A lone x-resident product keeps the single-call plan: bit-identical.
+    assert np.array_equal(outs[1].cpu().numpy().view(np.uint16), single(it).cpu().numpy().view(np.uint16))
