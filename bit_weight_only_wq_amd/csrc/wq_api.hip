@@ -194,7 +194,7 @@ wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream
     for (int32_t i = 0; i < count; ++i) {
         const wq_gemm_item& it = items[i];
         if (paths[i] < 0) continue;
-        const bool xr = paths[i] == WQ_PATH_MFMA && wq::xr_supports(it.B, it.K, it.group, it.bits);
+        const bool xr = paths[i] == WQ_PATH_MFMA && wq::xr_groupable(it.B, it.K, it.group, it.bits);
         if (!xr) {
             const wq_status s2 = run_gemm(it.X, it.codes, it.scales, it.zeros, it.Y, it.B, it.K, it.N,
                                           it.group, it.bits, paths[i], st);
@@ -206,11 +206,12 @@ wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream
         for (int32_t j = i; j < count && n < 64; ++j) {
             const wq_gemm_item& o = items[j];
             if (paths[j] != WQ_PATH_MFMA || o.B != it.B || o.bits != it.bits ||
-                !wq::xr_supports(o.B, o.K, o.group, o.bits))
+                !wq::xr_groupable(o.B, o.K, o.group, o.bits))
                 continue;
             group_buf[n++] = wq::XrProduct{o.X, o.codes, o.scales, o.zeros, o.Y, o.K, o.N, o.group};
             paths[j] = -1;  // issued
         }
+        // (A product left alone in a launch keeps the single-call kernel.)
         const wq_status s2 = check_hip(wq::launch_gemm_xr_many(group_buf, n, it.B, it.bits, num_cus(), st),
                                        "wq_gemm_grouped (x-resident) launch");
         if (s2 != WQ_OK) return s2;

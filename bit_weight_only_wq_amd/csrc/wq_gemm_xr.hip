@@ -644,7 +644,12 @@ hipError_t launch_xr_bt(const XrProduct* prods, int count, int64_t B, int num_cu
             if (take) sel[n++] = &prods[i];
             if (n == XR_MAX_ITEMS || (i == count && n > 0)) {
                 hipError_t e = hipSuccess;
-                if (hm == XR_HDR_ROUND) e = launch_xr_items<BITS, BTX, XR_HDR_ROUND>(sel, n, B, num_cus, stream);
+                const XrProduct& p0 = *sel[0];
+                if (n == 1 && !xr_supports(B, p0.K, p0.group, BITS))
+                    // Alone in its launch: the single-call choice of kernel.
+                    e = launch_gemm_mfma(p0.X, p0.codes, p0.scales, p0.zeros, p0.Y, B, p0.K, p0.N,
+                                         p0.group, BITS, num_cus, stream);
+                else if (hm == XR_HDR_ROUND) e = launch_xr_items<BITS, BTX, XR_HDR_ROUND>(sel, n, B, num_cus, stream);
                 else if (hm == XR_HDR_TURN) e = launch_xr_items<BITS, BTX, XR_HDR_TURN>(sel, n, B, num_cus, stream);
                 else e = launch_xr_items<BITS, BTX, XR_HDR_ROW>(sel, n, B, num_cus, stream);
                 if (e != hipSuccess) return e;
@@ -656,6 +661,12 @@ hipError_t launch_xr_bt(const XrProduct* prods, int count, int64_t B, int num_cu
 }
 
 }  // namespace
+
+bool xr_groupable(int64_t B, int64_t K, int32_t group, int32_t bits) {
+    if (B < 1 || B > 32 || (bits != 4 && bits != 8)) return false;
+    const int kr = bits == 4 ? XrGeom<4, 16>::KR : XrGeom<8, 16>::KR;
+    return group % kr == 0 && K % kr == 0 && K / kr < 65536;
+}
 
 bool xr_supports(int64_t B, int64_t K, int32_t group, int32_t bits) {
     if (B < 1 || B > 32 || (bits != 4 && bits != 8)) return false;

@@ -20,12 +20,16 @@ hipError_t launch_gemv(const void* X, const void* codes, const void* scales,
 // Matrix-core family: the X-resident kernel for B <= 32 (xr_*), the tiled
 // kernel beyond.
 bool xr_supports(int64_t B, int64_t K, int32_t group, int32_t bits);
+// Shapes the X-resident kernel can take at all (a superset of xr_supports:
+// beyond it, it is chosen only when other products share the launch).
+bool xr_groupable(int64_t B, int64_t K, int32_t group, int32_t bits);
 hipError_t launch_gemm_xr(const void* X, const void* codes, const void* scales,
                           const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                           int32_t group, int32_t bits, int num_cus, hipStream_t stream);
 // Several X-resident products of one batch size and bit width (each must
-// satisfy xr_supports): products sharing a header mode go into one launch of
-// up to eight, with one reduction launch for their K-slices.
+// satisfy xr_groupable): products sharing a header mode go into one launch of
+// up to eight, with one reduction launch for their K-slices; a product alone
+// in its launch that xr_supports rejects runs on the tiled kernel instead.
 struct XrProduct {
     const void* X;
     const void* codes;

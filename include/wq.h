@@ -136,10 +136,10 @@ typedef struct wq_gemm_item {
  * for it.  The decode step reads each matrix once per token ("Quantization &
  * inference optimisation", "Bandwidth, not compute"); small matrices then
  * spend much of their time in launch ramp, X staging and split-K reduction,
- * which grouping shares out.  Items that take the X-resident matrix-core
- * kernel (3 <= B <= 32) and share B and bits run up to eight products per
- * launch (one launch per group-header layout), plus one reduction launch;
- * every other item runs as its own wq_gemm, in item order.  A launch of
+ * which grouping shares out.  Items with 3 <= B <= 32 that the matrix-core
+ * path takes and that share B and bits run on the X-resident kernel, up to
+ * eight products per launch (one launch per group-header layout), plus one
+ * reduction launch; every other item runs as its own wq_gemm, in item order.  A launch of
  * several products splits K into fewer slices than single calls do, so their
  * fp32 sums may differ from wq_gemm's in the last bits (same tolerance);
  * results are deterministic for a given list of items.
