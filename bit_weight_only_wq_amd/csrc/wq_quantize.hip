@@ -91,11 +91,25 @@ __device__ __forceinline__ typename Packed8<BITS>::type encode8(const float* x, 
         near |= __builtin_fabsf(t - k[i]) > h.thr;
     }
     if (__builtin_amdgcn_ballot_w64(near) != 0) {
-        // Rare (wave-uniform) exact path: outside [-Z-2, M-Z+2] every value
-        // clamps to code 0 or M anyway.
+        // Exact path (taken when a lane of the wave lies near a half-integer;
+        // exact ties x/s = k + 1/2 are common with fp16 x and s).  With
+        // kl = floor(t) and t within 2^-20 of x/s, round-half-even(x/s) is kl
+        // below kl + 1/2, kl + 1 above it, and the even one of the two on it;
+        // the side is the sign of r = x - (kl + 1/2) s, computed exactly by
+        // one fma (every operand is a short multiple of 2^-25, so r is zero
+        // only when x/s is exactly kl + 1/2).  Outside [-Z-2, M-Z+2] every
+        // value clamps to code 0 or M anyway, so t is clamped there first.
         const float lo = -h.Z - 2.0f, hi = M - h.Z + 2.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) k[i] = rne_div_exact(x[i], h.s, h.rcp, lo, hi);
+        for (int i = 0; i < 8; ++i) {
+            const float t = __builtin_amdgcn_fmed3f(x[i] * h.rcp, lo, hi);
+            const float kl = __builtin_floorf(t);
+            const float r = __builtin_fmaf(-(kl + 0.5f), h.s, x[i]);
+            const float half = kl * 0.5f;
+            const bool odd = __builtin_rintf(half) != half;
+            const bool inc = (r > 0.0f) | ((r == 0.0f) & odd);   // no short-circuit branches
+            k[i] = inc ? kl + 1.0f : kl;
+        }
     }
     float q[8];
 #pragma unroll
