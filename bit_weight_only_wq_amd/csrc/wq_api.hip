@@ -82,8 +82,8 @@ wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, i
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: K=%lld is not a multiple of group=%lld", K, group);
     if (bits < 1 || bits > 8)
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: bits=%lld out of range", bits);
-    if (bits != 4 && bits != 8)
-        return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: GPU codec takes bits 4 or 8 (got %lld)", bits);
+    if (bits < 2)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: the codec takes bits 2..8 (got %lld)", bits);
     if (group % 8 != 0)
         return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: group=%lld must be a multiple of 8", group);
     if (N == 0) return WQ_OK;

@@ -64,10 +64,14 @@ __device__ __forceinline__ GroupHeader make_header(float mn, float mx, int M) {
     return h;
 }
 
-// Codes of 8 values packed into 4 bytes (4-bit, even position in the low
-// nibble) or 8 bytes (8-bit), little-endian.
+// Codes of 8 values packed into BITS bytes: the little-endian bit stream
+// (code i at bits [i*BITS, i*BITS+BITS)).  4-bit: one word, even position in
+// the low nibble; 8-bit: one byte per code; other widths: the low 8*BITS bits
+// of a 64-bit value.
 template <int BITS>
-struct Packed8;
+struct Packed8 {
+    typedef uint64_t type;
+};
 template <>
 struct Packed8<4> {
     typedef uint32_t type;
@@ -123,7 +127,7 @@ __device__ __forceinline__ typename Packed8<BITS>::type encode8(const float* x, 
             od = __builtin_amdgcn_cvt_pk_u8_f32(q[2 * j + 1], j, od);
         }
         return ev | (od << 4);
-    } else {
+    } else if constexpr (BITS == 8) {
         uint2 w = make_uint2(0u, 0u);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -131,14 +135,47 @@ __device__ __forceinline__ typename Packed8<BITS>::type encode8(const float* x, 
             w.y = __builtin_amdgcn_cvt_pk_u8_f32(q[4 + j], j, w.y);
         }
         return w;
+    } else {
+        uint64_t v = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v |= (uint64_t)(uint32_t)q[i] << (i * BITS);
+        return v;
     }
+}
+
+// Byte j (0 <= j < BITS) of a packed 8-code chunk.
+template <int BITS>
+__device__ __forceinline__ uint32_t chunk_byte(const typename Packed8<BITS>::type& p, int j) {
+    if constexpr (BITS == 4) return (p >> (8 * j)) & 0xFFu;
+    else if constexpr (BITS == 8) return ((j < 4 ? p.x : p.y) >> (8 * (j & 3))) & 0xFFu;
+    else return (uint32_t)(p >> (8 * j)) & 0xFFu;
 }
 
 // Store the packed codes of CPL consecutive 8-value chunks with one vector
 // store (4*CPL bytes at 4 bits, 8*CPL bytes at 8 bits).
 template <int BITS, int CPL>
 __device__ __forceinline__ void store_codes(uint8_t* dst, const typename Packed8<BITS>::type* p) {
-    if constexpr (BITS == 4) {
+    if constexpr (BITS != 4 && BITS != 8) {
+        // CPL*BITS bytes: the chunks' bytes in order.  Whole 32-bit words when
+        // the lane's share is a multiple of 4 bytes (then also 4-byte
+        // aligned), single bytes otherwise.
+        constexpr int NB = CPL * BITS;
+        if constexpr (NB % 4 == 0) {
+#pragma unroll
+            for (int w = 0; w < NB / 4; ++w) {
+                uint32_t v = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int byte = 4 * w + b;
+                    v |= chunk_byte<BITS>(p[byte / BITS], byte % BITS) << (8 * b);
+                }
+                reinterpret_cast<uint32_t*>(dst)[w] = v;
+            }
+        } else {
+#pragma unroll
+            for (int byte = 0; byte < NB; ++byte) dst[byte] = (uint8_t)chunk_byte<BITS>(p[byte / BITS], byte % BITS);
+        }
+    } else if constexpr (BITS == 4) {
         if constexpr (CPL == 4) *reinterpret_cast<uint4*>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
         else if constexpr (CPL == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(p[0], p[1]);
         else *reinterpret_cast<uint32_t*>(dst) = p[0];
@@ -193,7 +230,7 @@ __global__ __launch_bounds__(256) void quantize_team_kernel(
 // pass 1 reduces min/max over the group, pass 2 re-reads and encodes.
 template <int BITS>
 __global__ __launch_bounds__(256) void quantize_wave_kernel(
-    const uint16_t* __restrict__ W, typename Packed8<BITS>::type* __restrict__ codes,
+    const uint16_t* __restrict__ W, uint8_t* __restrict__ codes,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ngroups,
     int64_t G) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -216,7 +253,8 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
         float x[8];
         uint4 raw;
         load8(W + (c0 + j) * 8, x, raw);
-        codes[c0 + j] = encode8<BITS>(x, h);
+        const typename Packed8<BITS>::type p = encode8<BITS>(x, h);
+        store_codes<BITS, 1>(codes + (c0 + j) * BITS, &p);
     }
     if (lane == 0) {
         scales[g] = h.sbits;
@@ -236,7 +274,6 @@ hipError_t launch_team(const uint16_t* w, uint8_t* c, uint16_t* s, uint16_t* z, 
 template <int BITS>
 hipError_t launch_bits(const void* W, int64_t N, int64_t K, int32_t G, void* codes,
                        void* scales, void* zeros, hipStream_t stream) {
-    typedef typename Packed8<BITS>::type P;
     const uint16_t* w = static_cast<const uint16_t*>(W);
     uint8_t* c = static_cast<uint8_t*>(codes);
     uint16_t* s = static_cast<uint16_t*>(scales);
@@ -255,8 +292,7 @@ hipError_t launch_bits(const void* W, int64_t N, int64_t K, int32_t G, void* cod
         default: {
             const int64_t ngroups = nv / G;
             const dim3 grid((unsigned)((ngroups + 3) / 4));
-            quantize_wave_kernel<BITS><<<grid, dim3(256), 0, stream>>>(
-                w, static_cast<P*>(codes), s, z, ngroups, G);
+            quantize_wave_kernel<BITS><<<grid, dim3(256), 0, stream>>>(w, c, s, z, ngroups, G);
             return hipGetLastError();
         }
     }
@@ -267,8 +303,16 @@ hipError_t launch_bits(const void* W, int64_t N, int64_t K, int32_t G, void* cod
 hipError_t launch_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
                                 int32_t bits, void* codes, void* scales, void* zeros,
                                 hipStream_t stream) {
-    if (bits == 4) return launch_bits<4>(W, N, K, group, codes, scales, zeros, stream);
-    return launch_bits<8>(W, N, K, group, codes, scales, zeros, stream);
+    switch (bits) {
+        case 2: return launch_bits<2>(W, N, K, group, codes, scales, zeros, stream);
+        case 3: return launch_bits<3>(W, N, K, group, codes, scales, zeros, stream);
+        case 4: return launch_bits<4>(W, N, K, group, codes, scales, zeros, stream);
+        case 5: return launch_bits<5>(W, N, K, group, codes, scales, zeros, stream);
+        case 6: return launch_bits<6>(W, N, K, group, codes, scales, zeros, stream);
+        case 7: return launch_bits<7>(W, N, K, group, codes, scales, zeros, stream);
+        case 8: return launch_bits<8>(W, N, K, group, codes, scales, zeros, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace wq

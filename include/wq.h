@@ -85,8 +85,9 @@ typedef enum {
  * scales  fp16 [N, K/group]           output (group index fastest)
  * zeros   fp16 [N, K/group]           output
  * N >= 0 (N == 0 is a no-op), K >= 1, group >= 1, K % group == 0.
- * bits in {4, 8}; group % 8 == 0; codes 16-byte aligned; scales/zeros
- * 2-byte aligned.
+ * bits in 2..8 (wq_gemm reads 4 and 8); group % 8 == 0, so every 8 codes
+ * fill exactly `bits` bytes; codes 16-byte aligned; scales/zeros 2-byte
+ * aligned.
  */
 wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
                            int32_t bits, void* codes, void* scales, void* zeros,

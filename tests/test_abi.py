@@ -87,7 +87,7 @@ def test_empty_calls_are_no_ops():
 def test_quantize_validation_errors():
     assert _quant(K=250) == _lib.WQ_ERR_INVALID_ARG
     assert _quant(bits=0) == _lib.WQ_ERR_INVALID_ARG
-    assert _quant(bits=3) == _lib.WQ_ERR_UNSUPPORTED
+    assert _quant(bits=1) == _lib.WQ_ERR_UNSUPPORTED
     assert _quant(group=4, K=256) == _lib.WQ_ERR_UNSUPPORTED
     assert _quant(W=0) == _lib.WQ_ERR_INVALID_ARG
     assert _quant(W=FAKE + 2) == _lib.WQ_ERR_MISALIGNED

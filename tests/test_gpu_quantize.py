@@ -1,6 +1,9 @@
 """GPU parity of wq_quantize_pack against the CPU oracle: codes, packed bytes,
 scales and zero points must be bit-exact, on crafted corner-case groups, random
-shapes, the full-size workloads and part of the 7B decode-step weight set."""
+shapes, the full-size workloads and part of the 7B decode-step weight set.
+Every code width 2..8 is covered (the little-endian bit stream per row), with
+group sizes that take each kernel and each store width (whole 32-bit words,
+single bytes)."""
 
 import numpy as np
 import pytest
@@ -29,14 +32,17 @@ def check_quantize(W, group, bits, what):
     return codes, scales, zeros
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+ALL_BITS = [2, 3, 4, 5, 6, 7, 8]
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("group", [8, 16, 32, 64, 128, 256, 512, 96, 1024, 1536])
 def test_crafted_groups(bits, group):
     W = crafted_groups(group, bits, seed=group)
     check_quantize(W, group, bits, "crafted")
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("N,K,group", [(1, 8, 8), (3, 64, 32), (65, 512, 128), (7, 4096, 4096),
                                        (5, 11008, 11008), (33, 896, 32), (2, 1152, 384)])
 def test_random_shapes(bits, N, K, group):
@@ -45,7 +51,7 @@ def test_random_shapes(bits, N, K, group):
     check_quantize(W, group, bits, "random")
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", ALL_BITS)
 def test_fixpoint_on_grid(bits):
     W, q, s, z = on_grid_matrix(16, 256, 32, bits)
     codes, scales, zeros = check_quantize(W, 32, bits, "on-grid")
