@@ -9,11 +9,18 @@ What it computes (see oracle.c for the step-by-step citations):
       group-wise asymmetric quantization along K in exact integer arithmetic,
       following the codec of "What actually happens when you quantize a KV
       cache" §3 steps 3-5 and §4.
+  quantize(W, group, bits, scheme="sym" | "sym_tensor")
+      symmetric absolute-maximum quantization ("Quantization & inference
+      optimisation", "Quantize a matrix by hand" and "Per-channel, and what it
+      buys"), one scale per group (group = K: per output channel) or one per
+      tensor, stored in the same layout with zero point 2^(b-1).
   dequantize(...)           -> W_hat float64 [N, K] = (q - z) * s
   gemm(X, ...)              -> Y_ref float64 [B, N] = X W_hat^T in double.
 
 Parity status: the quantizer and packer are pinned by the worked groups of
-that page and by an exact-rational brute force; the GEMM is pinned only by
+that page and by an exact-rational brute force; the symmetric variant by the
+per-tensor/per-channel error table of "Quantize a matrix by hand", the
+symmetric step of the KV-cache page's worked group and the same brute force; the GEMM is pinned only by
 special cases (on-grid weights against a library matmul, single-row dot
 products), since the pages print no GEMM outputs.
 """
@@ -50,17 +57,19 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
         lib = ctypes.CDLL(_LIB)
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         i32 = ctypes.c_int32
         lib.oracle_quantize.argtypes = [p, i64, i64, i32, i32, p, p, p]
+        lib.oracle_quantize_sym.argtypes = [p, i64, i64, i32, i32, i32, p, p, p]
         lib.oracle_dequantize.argtypes = [p, p, p, i64, i64, i32, i32, p]
         lib.oracle_gemm.argtypes = [p, p, p, p, i64, i64, i64, i32, i32, p]
         lib.oracle_gemm_rows.argtypes = [p, p, p, p, i64, i64, i64, i32, i32, p, i64, p]
-        for f in (lib.oracle_quantize, lib.oracle_dequantize, lib.oracle_gemm,
+        for f in (lib.oracle_quantize, lib.oracle_quantize_sym, lib.oracle_dequantize,
+                  lib.oracle_gemm,
                   lib.oracle_gemm_rows):
             f.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -82,8 +91,17 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def quantize(W: np.ndarray, group: int, bits: int):
-    """W fp16 [N, K] -> (codes u8 [N, K*bits//8], scales fp16 [N, K//group], zeros fp16)."""
+SCHEMES = ("asym", "sym", "sym_tensor")
+
+
+def quantize(W: np.ndarray, group: int, bits: int, scheme: str = "asym"):
+    """W fp16 [N, K] -> (codes u8 [N, K*bits//8], scales fp16 [N, K//group], zeros fp16).
+
+    scheme "asym": min/max per group; "sym": absolute maximum per group;
+    "sym_tensor": one absolute maximum over the whole matrix.
+    """
+    if scheme not in SCHEMES:
+        raise ValueError(f"oracle: unknown scheme {scheme!r}")
     W = np.ascontiguousarray(W, dtype=np.float16)
     N, K = W.shape
     if K % group or (K * bits) % 8:
@@ -91,8 +109,14 @@ def quantize(W: np.ndarray, group: int, bits: int):
     codes = np.zeros((N, K * bits // 8), dtype=np.uint8)
     scales = np.zeros((N, K // group), dtype=np.float16)
     zeros = np.zeros((N, K // group), dtype=np.float16)
-    _check(_load().oracle_quantize(_ptr(W), N, K, group, bits, _ptr(codes),
-                                   _ptr(scales), _ptr(zeros)))
+    lib = _load()
+    if scheme == "asym":
+        rc = lib.oracle_quantize(_ptr(W), N, K, group, bits, _ptr(codes), _ptr(scales),
+                                 _ptr(zeros))
+    else:
+        rc = lib.oracle_quantize_sym(_ptr(W), N, K, group, bits, int(scheme == "sym_tensor"),
+                                     _ptr(codes), _ptr(scales), _ptr(zeros))
+    _check(rc)
     return codes, scales, zeros
 
 

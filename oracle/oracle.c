@@ -1,6 +1,7 @@
 /*
- * CPU oracle for group-wise asymmetric low-bit weight quantization and the
- * dequantize-then-multiply decode product.
+ * CPU oracle for group-wise low-bit weight quantization (asymmetric min/max,
+ * and the symmetric absolute-maximum variant) and the dequantize-then-multiply
+ * decode product.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
  * call this file: only the tests, the smoke check and the CPU-baseline leg of
@@ -40,6 +41,15 @@
  *     [k*b, k*b+b) of the row, which is the pages' "even channel in the low
  *     nibble" at b = 4 and one byte per code at b = 8;
  *   - NaN and Inf weights are rejected.
+ *
+ * Symmetric variant (oracle_quantize_sym), readings:
+ *   - the scale is max|x| / (2^(b-1) - 1), the exact quotient rounded once to
+ *     fp16 as above; an all-zero scope gets scale 1.0;
+ *   - the signed integer clamps to [-2^(b-1), 2^(b-1) - 1] (the pages' clamp
+ *     keeps the extra negative level) and is stored offset by 2^(b-1), with
+ *     that offset as the fp16 zero point;
+ *   - one scale per tensor is stored as that scale repeated in every group
+ *     header, so every scope shares one layout.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -250,6 +260,94 @@ int oracle_quantize(const uint16_t *W, int64_t N, int64_t K, int32_t group,
                 fp16_to_units(src[i], &xu[i]);
             quantize_group(xu, group, bits, q, &scales[n * ngroups + g],
                            &zeros[n * ngroups + g]);
+            for (i = 0; i < group; i++)
+                put_code(codes + n * row_bytes, g * group + i, bits, q[i]);
+        }
+        free(xu);
+        free(q);
+    }
+    return err;
+}
+
+/*
+ * Symmetric absolute-maximum quantization of one group ([QIO] "Quantize a
+ * matrix by hand" and "Per-channel, and what it buys"; [SMU]
+ * "Quantization: rounding the weights"):
+ *   qmax = 2^(b-1) - 1
+ *   s = A / qmax, A = max |x| over the scale's scope   stored in fp16
+ *   q = clamp(round(x / s), -qmax - 1, qmax)
+ * The signed q is stored as the code q + 2^(b-1) with the zero point 2^(b-1)
+ * (exact in fp16), so (code - zero) * s is the page's q * s and the
+ * asymmetric decoder reads it unchanged.  A is passed in: the group's own
+ * maximum, or the whole matrix's for one scale per tensor.
+ */
+static void quantize_group_sym(const int64_t *x, int64_t G, int bits, int64_t A,
+                               unsigned *q, uint16_t *scale_bits, uint16_t *zero_bits)
+{
+    const int64_t qmax = ((int64_t)1 << (bits - 1)) - 1;
+    const int64_t half = (int64_t)1 << (bits - 1);
+    int64_t S = 0, i;
+    int ovf;
+    uint16_t sb = fp16_nearest_ratio(A, qmax, &ovf);
+    if (sb == 0)
+        sb = 0x3C00;                     /* all-zero scope (or a few subnormal steps): s = 1.0 */
+    fp16_to_units(sb, &S);
+    for (i = 0; i < G; i++) {
+        int64_t c = rne_div(x[i], S);
+        if (c < -qmax - 1) c = -qmax - 1;
+        if (c > qmax) c = qmax;
+        q[i] = (unsigned)(c + half);
+    }
+    *scale_bits = sb;
+    *zero_bits = zero_point_to_fp16(half);
+}
+
+/*
+ * Symmetric variant of oracle_quantize: same layout and packing.  per_tensor
+ * = 0 takes A per group (group = K is one scale per output channel);
+ * per_tensor = 1 takes one A over the whole matrix and repeats its scale in
+ * every group header.
+ */
+int oracle_quantize_sym(const uint16_t *W, int64_t N, int64_t K, int32_t group,
+                        int32_t bits, int32_t per_tensor, uint8_t *codes,
+                        uint16_t *scales, uint16_t *zeros)
+{
+    const int64_t row_bytes = K * bits / 8;
+    const int64_t ngroups = K / group;
+    int64_t n, Aall = 0;
+    int err = check_shape(N, K, group, bits);
+    if (err)
+        return err;
+    for (n = 0; n < N * K; n++) {
+        int64_t u;
+        if (fp16_to_units(W[n], &u) != 0)
+            return ORACLE_ENONFINITE;
+        if (u < 0) u = -u;
+        if (u > Aall) Aall = u;
+    }
+    memset(codes, 0, (size_t)(N * row_bytes));
+    err = ORACLE_OK;
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; n++) {
+        int64_t *xu = (int64_t *)malloc(sizeof(int64_t) * (size_t)group);
+        unsigned *q = (unsigned *)malloc(sizeof(unsigned) * (size_t)group);
+        int64_t g, i;
+        if (!xu || !q) {
+            err = ORACLE_ENOMEM;
+            free(xu);
+            free(q);
+            continue;
+        }
+        for (g = 0; g < ngroups; g++) {
+            const uint16_t *src = W + n * K + g * group;
+            int64_t A = 0;
+            for (i = 0; i < group; i++) {
+                fp16_to_units(src[i], &xu[i]);
+                if (xu[i] > A) A = xu[i];
+                if (-xu[i] > A) A = -xu[i];
+            }
+            quantize_group_sym(xu, group, bits, per_tensor ? Aall : A, q,
+                               &scales[n * ngroups + g], &zeros[n * ngroups + g]);
             for (i = 0; i < group; i++)
                 put_code(codes + n * row_bytes, g * group + i, bits, q[i]);
         }

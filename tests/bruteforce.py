@@ -1,8 +1,9 @@
-"""Exact-rational brute force of the group-wise asymmetric quantizer.
+"""Exact-rational brute force of the group-wise quantizers.
 
 Written straight from the formulas of "What actually happens when you quantize
-a KV cache" (§3 steps 3-5, §4) with ``fractions.Fraction``; it pins the C
-oracle on tiny inputs.  It shares nothing with the oracle: fp16 rounding here
+a KV cache" (§3 steps 3-5, §4) for the asymmetric codec, and of "Quantization &
+inference optimisation" ("Quantize a matrix by hand") for the symmetric one,
+with ``fractions.Fraction``; it pins the C oracle on tiny inputs.  It shares nothing with the oracle: fp16 rounding here
 is a nearest-neighbour search over the full sorted list of finite fp16 values,
 where the oracle constructs the significand arithmetically.
 
@@ -10,7 +11,10 @@ Readings (identical in meaning to the oracle's, arrived at independently):
 round half to even; scale rounded once to fp16 and used thereafter; a scale
 that rounds to 0 becomes 1.0; zero point stored in fp16, saturating at 65504;
 zero point 0 stored as +0.0; codes from the stored zero point; codes packed as
-a little-endian bit stream per row.
+a little-endian bit stream per row.  Symmetric: s = max|x| / (2^(b-1) - 1)
+rounded once to fp16 (1.0 if that is 0), signed integers clamped to
+[-2^(b-1), 2^(b-1) - 1] and stored offset by 2^(b-1), which is the stored zero
+point; one scale per tensor is that scale in every group header.
 """
 
 from __future__ import annotations
@@ -99,6 +103,41 @@ def quantize(W16: np.ndarray, group: int, bits: int):
         row_codes = []
         for g in range(K // group):
             q, s, z = quantize_group([int(v) for v in wb[n, g * group:(g + 1) * group]], bits)
+            row_codes += q
+            sb[n, g], zb[n, g] = s, z
+        codes[n] = np.frombuffer(pack_row(row_codes, bits), dtype=np.uint8)
+    return codes, sb, zb
+
+
+def quantize_group_sym(xbits, bits, amax=None):
+    """Symmetric group: (codes, scale_bits, zero_bits).  amax overrides the
+    group's own absolute maximum (one scale for the whole tensor)."""
+    half = 2 ** (bits - 1)
+    x = [fp16_value(b) for b in xbits]
+    A = max(abs(v) for v in x) if amax is None else amax
+    sb = nearest_fp16_bits(A / (half - 1))
+    if sb == 0:
+        sb = 0x3C00
+    s = fp16_value(sb)
+    codes = [int(min(max(round_half_even(v / s), -half), half - 1)) + half for v in x]
+    return codes, sb, nearest_fp16_bits(Fraction(half))
+
+
+def quantize_sym(W16: np.ndarray, group: int, bits: int, per_tensor: bool = False):
+    """Symmetric counterpart of quantize(): same outputs and layout."""
+    N, K = W16.shape
+    wb = W16.view(np.uint16)
+    amax = None
+    if per_tensor:
+        amax = max((abs(fp16_value(int(v))) for v in wb.ravel()), default=Fraction(0))
+    codes = np.zeros((N, K * bits // 8), dtype=np.uint8)
+    sb = np.zeros((N, K // group), dtype=np.uint16)
+    zb = np.zeros((N, K // group), dtype=np.uint16)
+    for n in range(N):
+        row_codes = []
+        for g in range(K // group):
+            q, s, z = quantize_group_sym([int(v) for v in wb[n, g * group:(g + 1) * group]],
+                                         bits, amax)
             row_codes += q
             sb[n, g], zb[n, g] = s, z
         codes[n] = np.frombuffer(pack_row(row_codes, bits), dtype=np.uint8)

@@ -311,3 +311,184 @@ def test_workloads_have_no_degenerate_groups():
         W, _ = wq_inputs.workload_arrays(name, rows=512)
         g = W.reshape(W.shape[0], -1, cfg["group"]).astype(np.float64)
         assert np.all(g.max(-1) > g.min(-1))
+
+
+# --------------------------------------------------------------------------
+# Symmetric absolute-maximum variant
+# --------------------------------------------------------------------------
+
+def _sym_signed(codes, K, bits):
+    return _unpack(codes, K, bits) - 2 ** (bits - 1)
+
+
+def test_symmetric_step_of_worked_group(oracle_mod):
+    """"What actually happens when you quantize a KV cache", §3 step 3 (the
+    comparison with a symmetric grid): max(|min|, |max|) / 7 = 0.124 for the
+    worked group, and the asymmetric step is 38% finer."""
+    g = read_golden("kvq_worked_group.txt")
+    x = np.array([float(v) for v in g["x"].split()], dtype=F16)[None, :]
+    codes, scales, zeros = oracle_mod.quantize(x, 8, 4, scheme="sym")
+    s_sym = float(scales[0, 0])
+    assert round(s_sym, 3) == float(g["symmetric_step"])
+    assert _bits(zeros)[0, 0] == 0x4800  # zero point 8 = 2^(b-1)
+    s_asym = float(oracle_mod.quantize(x, 8, 4)[1][0, 0])
+    assert round(100 * (1 - s_asym / s_sym)) == 38
+    # The largest magnitude maps to +qmax; reconstruction is q * s.
+    q = _sym_signed(codes, 8, 4)[0]
+    assert q[2] == 7 and q.min() >= -8
+    xhat = oracle_mod.dequantize(codes, scales, zeros, 1, 8, 8, 4)[0]
+    assert np.array_equal(xhat, q * s_sym)
+
+
+def _page_matrix():
+    torch = pytest.importorskip("torch")
+    gen = torch.Generator().manual_seed(0)
+    W = torch.randn(512, 512, generator=gen) * 0.02
+    W[7] *= 25.0
+    W[200] *= 12.0
+    return W.numpy()
+
+
+def test_symmetric_table_matches_page(oracle_mod):
+    """"Quantization & inference optimisation": the matrix of "Quantize a
+    matrix by hand" and the error table of "Per-channel, and what it buys".
+
+    Per-channel is one group per row (group = K); per-tensor is one absolute
+    maximum over the matrix.  The page works in fp32; here W and the scale are
+    stored in fp16, which moves the printed 4-decimal figures by at most about
+    1e-4, so each must agree within 2e-4.  A wrong qmax (2^b - 1), a maximum
+    taken over columns, or a per-tensor/per-channel mix-up misses by far more.
+    """
+    g = read_golden("qio_symmetric_table.txt")
+    W32 = _page_matrix()
+    # The recipe reproduces the page's input statistics.
+    assert round(float(np.abs(W32).max()), 4) == float(g["abs_max"])
+    assert round(float(W32.std(ddof=1)), 4) == float(g["std"])
+    W = W32.astype(F16)
+    x = W.astype(np.float64)
+    assert int((np.abs(x) > 0.2).sum()) == int(g["loud_count"])
+
+    def errors(bits, scheme):
+        codes, scales, zeros = oracle_mod.quantize(W, 512, bits, scheme=scheme)
+        Q = oracle_mod.dequantize(codes, scales, zeros, 512, 512, 512, bits)
+        rel = np.sqrt(((Q - x) ** 2).mean()) / np.sqrt((x ** 2).mean())
+        return Q, rel, np.abs(Q - x).max()
+
+    for entry in g["table"].split("|"):
+        bits, name, rel_p, max_p = entry.split()
+        scheme = "sym_tensor" if name == "per-tensor" else "sym"
+        _, rel, mx = errors(int(bits), scheme)
+        assert abs(rel - float(rel_p)) <= 2e-4, (bits, name, rel)
+        assert abs(mx - float(max_p)) <= 2e-4, (bits, name, mx)
+    # "Where the error actually lands": per-row errors at int8 per-tensor.
+    Q, _, _ = errors(8, "sym_tensor")
+    row = np.sqrt(((Q - x) ** 2).mean(1)) / np.sqrt((x ** 2).mean(1))
+    assert abs(np.median(row) - float(g["row_err_median"])) <= 2e-4
+    assert abs(row[0] - float(g["row_err_row0"])) <= 2e-4
+    assert abs(row[7] - float(g["row_err_row7"])) <= 2e-4
+
+
+@pytest.mark.parametrize("scheme", ["sym", "sym_tensor"])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_symmetric_matches_bruteforce(oracle_mod, bits, scheme):
+    rng = np.random.default_rng(200 + bits)
+    per_tensor = scheme == "sym_tensor"
+    for group, K in [(8, 16), (16, 32), (8, 64), (64, 64)]:
+        W = (rng.standard_normal((3, K)) * rng.choice([0.02, 1.0, 300.0])).astype(F16)
+        codes, scales, zeros = oracle_mod.quantize(W, group, bits, scheme=scheme)
+        bc, bs, bz = bruteforce.quantize_sym(W, group, bits, per_tensor)
+        assert np.array_equal(codes, bc)
+        assert np.array_equal(_bits(scales), bs)
+        assert np.array_equal(_bits(zeros), bz)
+    for group in (8, 32):
+        W = crafted_groups(group, bits)
+        codes, scales, zeros = oracle_mod.quantize(W, group, bits, scheme=scheme)
+        bc, bs, bz = bruteforce.quantize_sym(W, group, bits, per_tensor)
+        assert np.array_equal(_bits(scales), bs)
+        assert np.array_equal(_bits(zeros), bz)
+        assert np.array_equal(codes, bc)
+
+
+def test_symmetric_two_bit_levels(oracle_mod):
+    """"Serving many users at once", "Quantization: rounding the weights":
+    at 2 bits the levels are -2, -1, 0, 1 times the scale (group of 32)."""
+    rng = np.random.default_rng(9)
+    W = (rng.standard_normal((16, 256)) * 0.02).astype(F16)
+    codes, scales, zeros = oracle_mod.quantize(W, 32, 2, scheme="sym")
+    q = _sym_signed(codes, 256, 2)
+    assert set(np.unique(q).tolist()) <= {-2, -1, 0, 1}
+    assert np.all(zeros.astype(np.float64) == 2.0)
+    # With s = max|x| (qmax = 1) every group's largest magnitude decodes to +-s.
+    xg = _group_view(W.astype(np.float64), 32)
+    s = scales.astype(np.float64)
+    assert np.allclose(np.abs(xg).max(-1), s, rtol=2.0 ** -11)
+
+
+@pytest.mark.parametrize("bits,group,scheme", [(4, 128, "sym"), (8, 4096, "sym"),
+                                               (3, 64, "sym"), (4, 128, "sym_tensor")])
+def test_symmetric_error_bound(oracle_mod, bits, group, scheme):
+    """Closed form: |x - q s| <= s/2 unless q is clamped; the clamp can only
+    fire when the fp16 scale fell below A / qmax, and then the error is at
+    most A - qmax s + s/2 (A the scope's absolute maximum)."""
+    W, _ = wq_inputs.workload_arrays("mlp7b_up_k4096_n11008_g128", rows=128)
+    codes, scales, zeros = oracle_mod.quantize(W, group, bits, scheme=scheme)
+    N, K = W.shape
+    half = 2 ** (bits - 1)
+    q = _sym_signed(codes, K, bits)
+    x = W.astype(np.float64)
+    s = np.repeat(scales.astype(np.float64), group, axis=1)
+    err = np.abs(x - q * s)
+    inner = (q > -half) & (q < half - 1)
+    assert np.all(err[inner] <= s[inner] / 2)
+    if scheme == "sym_tensor":
+        A = np.full_like(x, np.abs(x).max())
+        assert np.all(scales == scales.flat[0])
+    else:
+        A = np.repeat(np.abs(_group_view(x, group)).max(-1), group, axis=1)
+    assert np.all(err <= s / 2 + np.maximum(A - (half - 1) * s, 0))
+    # Dequantization is q * s exactly.
+    assert np.array_equal(oracle_mod.dequantize(codes, scales, zeros, N, K, group, bits), q * s)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_symmetric_fixpoint_on_grid(oracle_mod, bits):
+    """Weights q * s with s = 2^e, |q| <= qmax and some |q| = qmax round-trip
+    exactly (a -qmax - 1 would make the absolute maximum, and so the scale,
+    larger)."""
+    rng = np.random.default_rng(11)
+    half = 2 ** (bits - 1)
+    N, K, G = 6, 128, 32
+    s = 2.0 ** rng.integers(-14, -6, (N, K // G))
+    q = rng.integers(-half + 1, half, (N, K // G, G))
+    q[:, :, 0] = half - 1
+    W = (q * s[:, :, None]).reshape(N, K).astype(F16)
+    codes, scales, zeros = oracle_mod.quantize(W, G, bits, scheme="sym")
+    assert np.array_equal(scales.astype(np.float64), s)
+    assert np.array_equal(_sym_signed(codes, K, bits), q.reshape(N, K))
+
+
+def test_symmetric_degenerate_scopes(oracle_mod):
+    W = np.zeros((2, 16), dtype=F16)
+    W[1, 3] = -0.0
+    for scheme in ("sym", "sym_tensor"):
+        codes, scales, zeros = oracle_mod.quantize(W, 8, 4, scheme=scheme)
+        assert np.all(_bits(scales) == 0x3C00)
+        assert np.all(_sym_signed(codes, 16, 4) == 0)
+    # Per tensor: a quiet row shares the loud row's scale.
+    W = np.array([[0.01] * 8, [1.0] + [0.0] * 7], dtype=F16)
+    codes, scales, zeros = oracle_mod.quantize(W, 8, 4, scheme="sym_tensor")
+    assert np.all(_bits(scales) == _bits(scales)[1, 0])
+    assert np.all(_sym_signed(codes, 8, 4)[0] == 0)
+
+
+def test_symmetric_clamp_ends(oracle_mod):
+    """Both clamp ends of [-2^(b-1), 2^(b-1) - 1] are reached when the fp16
+    scale rounds well below A / qmax: at b = 4 a subnormal range of 10 units
+    of 2^-24 gives s = 10/7 -> 1 unit, so +-10 clamp to 7 and -8."""
+    u = 2.0 ** -24
+    W = (np.array([[-10, 10, 3, -9, 0, -8, 7, 1]]) * u).astype(F16)
+    codes, scales, zeros = oracle_mod.quantize(W, 8, 4, scheme="sym")
+    assert _bits(scales)[0, 0] == 0x0001
+    assert _sym_signed(codes, 8, 4)[0].tolist() == [-8, 7, 3, -8, 0, -8, 7, 1]
+    bc, bs, bz = bruteforce.quantize_sym(W, 8, 4)
+    assert np.array_equal(codes, bc) and np.array_equal(_bits(scales), bs)
