@@ -50,10 +50,19 @@ def gemv_max_batch() -> int:
     return int(load().wq_gemv_max_batch())
 
 
-def quantize_pack(W, group: int = 128, bits: int = 4, out=None):
-    """W fp16 [N, K] (GPU) -> (codes u8 [N, K*bits//8], scales fp16 [N, K//group], zeros fp16)."""
+SCHEMES = {"asym": 0, "sym": 1, "sym_tensor": 2}
+
+
+def quantize_pack(W, group: int = 128, bits: int = 4, out=None, scheme: str = "asym"):
+    """W fp16 [N, K] (GPU) -> (codes u8 [N, K*bits//8], scales fp16 [N, K//group], zeros fp16).
+
+    scheme "asym" (min/max, integer zero point), "sym" (absolute maximum per
+    group; group = K for one scale per output channel) or "sym_tensor" (one
+    absolute maximum for the whole matrix)."""
     import torch
     lib = load()
+    if scheme not in SCHEMES:
+        raise ValueError(f"unknown scheme {scheme!r}")
     if W.dim() != 2:
         raise ValueError("W must be 2-D [N, K]")
     N, K = W.shape
@@ -70,8 +79,9 @@ def quantize_pack(W, group: int = 128, bits: int = 4, out=None):
         _need(scales, torch.float16, (N, K // group), "scales")
         _need(zeros, torch.float16, (N, K // group), "zeros")
     with torch.cuda.device(W.device):
-        st = lib.wq_quantize_pack(W.data_ptr(), N, K, group, bits, codes.data_ptr(),
-                                  scales.data_ptr(), zeros.data_ptr(), _stream_handle(W.device))
+        st = lib.wq_quantize_pack_ex(W.data_ptr(), N, K, group, bits, SCHEMES[scheme],
+                                     codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                     _stream_handle(W.device))
     check(st, "wq_quantize_pack")
     return codes, scales, zeros
 

@@ -18,6 +18,10 @@ WQ_PATH_AUTO = 0
 WQ_PATH_GEMV = 1
 WQ_PATH_MFMA = 2
 
+WQ_SCHEME_ASYM = 0
+WQ_SCHEME_SYM = 1
+WQ_SCHEME_SYM_TENSOR = 2
+
 # Every symbol include/wq.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -32,6 +36,7 @@ class GemmItem(ctypes.Structure):
 
 SIGNATURES = {
     "wq_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _P, _P, _P]),
+    "wq_quantize_pack_ex": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
     "wq_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P]),
     "wq_gemm_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
     "wq_gemm_grouped": (ctypes.c_int, [ctypes.POINTER(GemmItem), _I32, _P]),

@@ -73,8 +73,9 @@ int64_t wq_num_groups(int64_t N, int64_t K, int32_t group) {
 // kernels from B = 3 on.
 int32_t wq_gemv_max_batch(void) { return 2; }
 
-wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, int32_t bits,
-                           void* codes, void* scales, void* zeros, void* stream) {
+wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group, int32_t bits,
+                              int32_t scheme, void* codes, void* scales, void* zeros,
+                              void* stream) {
     g_last_error[0] = '\0';
     if (N < 0 || K < 1 || group < 1)
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: need N >= 0, K >= 1, group >= 1 (N=%lld K=%lld)", N, K);
@@ -82,6 +83,8 @@ wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, i
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: K=%lld is not a multiple of group=%lld", K, group);
     if (bits < 1 || bits > 8)
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: bits=%lld out of range", bits);
+    if (scheme < WQ_SCHEME_ASYM || scheme > WQ_SCHEME_SYM_TENSOR)
+        return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: unknown scheme %lld", scheme);
     if (bits < 2)
         return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: the codec takes bits 2..8 (got %lld)", bits);
     if (group % 8 != 0)
@@ -91,9 +94,15 @@ wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, i
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: null pointer");
     if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
         return fail(WQ_ERR_MISALIGNED, "wq_quantize_pack: W and codes need 16-byte alignment");
-    return check_hip(wq::launch_quantize_pack(W, N, K, group, bits, codes, scales, zeros,
+    return check_hip(wq::launch_quantize_pack(W, N, K, group, bits, scheme, codes, scales, zeros,
                                               static_cast<hipStream_t>(stream)),
                      "wq_quantize_pack launch");
+}
+
+wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, int32_t bits,
+                           void* codes, void* scales, void* zeros, void* stream) {
+    return wq_quantize_pack_ex(W, N, K, group, bits, WQ_SCHEME_ASYM, codes, scales, zeros,
+                               stream);
 }
 
 // Validates one product and picks its kernel family (path on return); does

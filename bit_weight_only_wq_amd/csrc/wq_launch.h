@@ -6,9 +6,11 @@
 
 namespace wq {
 
+// scheme: 0 asymmetric, 1 symmetric per group, 2 symmetric per tensor (the
+// last takes the stream's workspace for its maximum).
 hipError_t launch_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
-                                int32_t bits, void* codes, void* scales, void* zeros,
-                                hipStream_t stream);
+                                int32_t bits, int32_t scheme, void* codes, void* scales,
+                                void* zeros, hipStream_t stream);
 
 // GEMV family: returns hipErrorInvalidValue when the shape is outside what the
 // instantiated tilings cover (the caller maps that to WQ_ERR_UNSUPPORTED).

@@ -8,6 +8,14 @@
 // Rounding is half-to-even and every decision is the exact-rational one (see
 // wq_device.h).  Degenerate scale -> 1.0; zero point saturates at +-65504.
 //
+// Symmetric scheme ("Quantization & inference optimisation", "Quantize a
+// matrix by hand" and "Per-channel, and what it buys"): s = A/(2^(b-1)-1) with
+// A = max|x| of the group (or of the whole matrix), the signed integer
+// clamp(round(x/s), -2^(b-1), 2^(b-1)-1) stored offset by 2^(b-1), which is
+// the stored zero point.  That is the asymmetric encoder with z = 2^(b-1), so
+// both schemes share the encode and pack code and differ only in the header.
+// One scale per tensor takes A from two small reduction launches first.
+//
 // Layout: W, codes, scales and zeros are all flat row-major, and K % G == 0,
 // so group gi covers W[gi*G .. gi*G + G) and writes scales[gi], zeros[gi]
 // and codes bytes [gi*G*b/8, (gi+1)*G*b/8).  Each lane handles 8 consecutive
@@ -62,6 +70,34 @@ __device__ __forceinline__ GroupHeader make_header(float mn, float mx, int M) {
     const float tmax = __builtin_fmaxf(__builtin_fabsf(mn), __builtin_fabsf(mx)) * h.rcp;
     h.thr = 0.5f - (tmax + 1.0f) * 0x1p-20f;
     return h;
+}
+
+// Symmetric header from the scope's absolute maximum A: s = A / qmax rounded
+// once to fp16 (1.0 when that is 0), zero point 2^(b-1) (exact in fp16).
+__device__ __forceinline__ GroupHeader make_header_sym(float A, int bits) {
+    GroupHeader h;
+    const int half = 1 << (bits - 1);
+    h.sbits = scale_bits_exact(0.0f, A, half - 1);
+    h.s = half_bits_to_float(h.sbits);
+    h.rcp = __builtin_amdgcn_rcpf(h.s);
+    h.Z = (float)half;
+    h.zbits = zero_bits_from_int(h.Z);
+    h.thr = 0.5f - (A * h.rcp + 1.0f) * 0x1p-20f;   // as in make_header
+    return h;
+}
+
+// Header of one group for the scheme: 0 asymmetric, 1 symmetric per group,
+// 2 symmetric with the tensor's absolute maximum Aall.
+__device__ __forceinline__ GroupHeader header_for(int scheme, float mn, float mx, float Aall,
+                                                  int bits) {
+    if (scheme == 0) return make_header(mn, mx, (1 << bits) - 1);
+    return make_header_sym(scheme == 2 ? Aall : __builtin_fmaxf(-mn, mx), bits);
+}
+
+// fp16 bits of the tensor's absolute maximum, written by the reduction
+// launches (finite fp16 magnitudes order like their bit patterns).
+__device__ __forceinline__ float load_amax(int scheme, const uint32_t* amax) {
+    return scheme == 2 ? half_bits_to_float((uint16_t)amax[0]) : 0.0f;
 }
 
 // Codes of 8 values packed into BITS bytes: the little-endian bit stream
@@ -198,7 +234,9 @@ __device__ __forceinline__ void store_codes(uint8_t* dst, const typename Packed8
 template <int BITS, int T, int CPL>
 __global__ __launch_bounds__(256) void quantize_team_kernel(
     const uint16_t* __restrict__ W, uint8_t* __restrict__ codes,
-    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t nlanes) {
+    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t nlanes, int scheme,
+    const uint32_t* __restrict__ amax) {
+    const float Aall = load_amax(scheme, amax);
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const bool live = t < nlanes;            // teams are all live or all dead
     const int64_t u = live ? t : nlanes - 1;
@@ -214,7 +252,7 @@ __global__ __launch_bounds__(256) void quantize_team_kernel(
         mx = __builtin_fmaxf(mx, b);
     }
     group_minmax<T>(mn, mx);
-    const GroupHeader h = make_header(mn, mx, (1 << BITS) - 1);
+    const GroupHeader h = header_for(scheme, mn, mx, Aall, BITS);
     if (!live) return;
     typename Packed8<BITS>::type p[CPL];
 #pragma unroll
@@ -232,7 +270,8 @@ template <int BITS>
 __global__ __launch_bounds__(256) void quantize_wave_kernel(
     const uint16_t* __restrict__ W, uint8_t* __restrict__ codes,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ngroups,
-    int64_t G) {
+    int64_t G, int scheme, const uint32_t* __restrict__ amax) {
+    const float Aall = load_amax(scheme, amax);
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t g = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
     if (g >= ngroups) return;                // whole wave leaves together
@@ -248,7 +287,7 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
         mx = __builtin_fmaxf(mx, b);
     }
     group_minmax<kWave>(mn, mx);
-    const GroupHeader h = make_header(mn, mx, (1 << BITS) - 1);
+    const GroupHeader h = header_for(scheme, mn, mx, Aall, BITS);
     for (int64_t j = lane; j < cpg; j += kWave) {
         float x[8];
         uint4 raw;
@@ -262,37 +301,80 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
     }
 }
 
+// Absolute maximum of the whole matrix, as fp16 magnitude bits: each block
+// reduces a grid-strided share of the 16-byte chunks into part[block], then
+// one block reduces the partials into *out.
+constexpr int kAmaxBlocks = 1024;
+
+__device__ __forceinline__ uint32_t max_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t m) {
+    __shared__ uint32_t red[4];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max_u32(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+    __syncthreads();
+    return max_u32(max_u32(red[0], red[1]), max_u32(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(256) void amax_partial_kernel(const uint16_t* __restrict__ W,
+                                                           int64_t nchunks,
+                                                           uint32_t* __restrict__ part) {
+    uint32_t m = 0;
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks;
+         c += (int64_t)gridDim.x * 256) {
+        const uint4 r = *reinterpret_cast<const uint4*>(W + c * 8);
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            m = max_u32(m, max_u32(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    }
+    m = block_max_u32(m);
+    if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(256) void amax_final_kernel(const uint32_t* __restrict__ part,
+                                                         int nparts, uint32_t* __restrict__ out) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += 256) m = max_u32(m, part[i]);
+    m = block_max_u32(m);
+    if (threadIdx.x == 0) out[0] = m;
+}
+
 template <int BITS, int T, int CPL>
 hipError_t launch_team(const uint16_t* w, uint8_t* c, uint16_t* s, uint16_t* z, int64_t nvals,
-                       hipStream_t stream) {
+                       int scheme, const uint32_t* amax, hipStream_t stream) {
     const int64_t nlanes = nvals / (8 * CPL);
     const dim3 grid((unsigned)((nlanes + 255) / 256));
-    quantize_team_kernel<BITS, T, CPL><<<grid, dim3(256), 0, stream>>>(w, c, s, z, nlanes);
+    quantize_team_kernel<BITS, T, CPL><<<grid, dim3(256), 0, stream>>>(w, c, s, z, nlanes,
+                                                                       scheme, amax);
     return hipGetLastError();
 }
 
 template <int BITS>
 hipError_t launch_bits(const void* W, int64_t N, int64_t K, int32_t G, void* codes,
-                       void* scales, void* zeros, hipStream_t stream) {
+                       void* scales, void* zeros, int scheme, const uint32_t* amax,
+                       hipStream_t stream) {
     const uint16_t* w = static_cast<const uint16_t*>(W);
     uint8_t* c = static_cast<uint8_t*>(codes);
     uint16_t* s = static_cast<uint16_t*>(scales);
     uint16_t* z = static_cast<uint16_t*>(zeros);
     const int64_t nv = N * K;
     switch (G) {
-        case 8: return launch_team<BITS, 1, 1>(w, c, s, z, nv, stream);
-        case 16: return launch_team<BITS, 1, 2>(w, c, s, z, nv, stream);
-        case 32: return launch_team<BITS, 1, 4>(w, c, s, z, nv, stream);
-        case 64: return launch_team<BITS, 2, 4>(w, c, s, z, nv, stream);
-        case 128: return launch_team<BITS, 4, 4>(w, c, s, z, nv, stream);
-        case 256: return launch_team<BITS, 8, 4>(w, c, s, z, nv, stream);
-        case 512: return launch_team<BITS, 16, 4>(w, c, s, z, nv, stream);
-        case 1024: return launch_team<BITS, 32, 4>(w, c, s, z, nv, stream);
-        case 2048: return launch_team<BITS, 64, 4>(w, c, s, z, nv, stream);
+        case 8: return launch_team<BITS, 1, 1>(w, c, s, z, nv, scheme, amax, stream);
+        case 16: return launch_team<BITS, 1, 2>(w, c, s, z, nv, scheme, amax, stream);
+        case 32: return launch_team<BITS, 1, 4>(w, c, s, z, nv, scheme, amax, stream);
+        case 64: return launch_team<BITS, 2, 4>(w, c, s, z, nv, scheme, amax, stream);
+        case 128: return launch_team<BITS, 4, 4>(w, c, s, z, nv, scheme, amax, stream);
+        case 256: return launch_team<BITS, 8, 4>(w, c, s, z, nv, scheme, amax, stream);
+        case 512: return launch_team<BITS, 16, 4>(w, c, s, z, nv, scheme, amax, stream);
+        case 1024: return launch_team<BITS, 32, 4>(w, c, s, z, nv, scheme, amax, stream);
+        case 2048: return launch_team<BITS, 64, 4>(w, c, s, z, nv, scheme, amax, stream);
         default: {
             const int64_t ngroups = nv / G;
             const dim3 grid((unsigned)((ngroups + 3) / 4));
-            quantize_wave_kernel<BITS><<<grid, dim3(256), 0, stream>>>(w, c, s, z, ngroups, G);
+            quantize_wave_kernel<BITS><<<grid, dim3(256), 0, stream>>>(w, c, s, z, ngroups, G,
+                                                                       scheme, amax);
             return hipGetLastError();
         }
     }
@@ -301,16 +383,35 @@ hipError_t launch_bits(const void* W, int64_t N, int64_t K, int32_t G, void* cod
 }  // namespace
 
 hipError_t launch_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
-                                int32_t bits, void* codes, void* scales, void* zeros,
-                                hipStream_t stream) {
+                                int32_t bits, int32_t scheme, void* codes, void* scales,
+                                void* zeros, hipStream_t stream) {
+    const uint32_t* amax = nullptr;
+    if (scheme == 2) {
+        // Two reduction launches into the stream's workspace: kAmaxBlocks
+        // partials, then the maximum in the word after them.
+        uint32_t* unused = nullptr;
+        float* part = nullptr;
+        hipError_t e = workspace_get(stream, 0, (kAmaxBlocks + 1) * sizeof(uint32_t), &unused, &part);
+        if (e != hipSuccess) return e;
+        uint32_t* words = reinterpret_cast<uint32_t*>(part);
+        const int64_t nchunks = N * K / 8;
+        const int64_t want = (nchunks + 255) / 256;
+        const int blocks = (int)(want < kAmaxBlocks ? (want < 1 ? 1 : want) : kAmaxBlocks);
+        amax_partial_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+            static_cast<const uint16_t*>(W), nchunks, words);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        amax_final_kernel<<<dim3(1), dim3(256), 0, stream>>>(words, blocks, words + kAmaxBlocks);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        amax = words + kAmaxBlocks;
+    }
     switch (bits) {
-        case 2: return launch_bits<2>(W, N, K, group, codes, scales, zeros, stream);
-        case 3: return launch_bits<3>(W, N, K, group, codes, scales, zeros, stream);
-        case 4: return launch_bits<4>(W, N, K, group, codes, scales, zeros, stream);
-        case 5: return launch_bits<5>(W, N, K, group, codes, scales, zeros, stream);
-        case 6: return launch_bits<6>(W, N, K, group, codes, scales, zeros, stream);
-        case 7: return launch_bits<7>(W, N, K, group, codes, scales, zeros, stream);
-        case 8: return launch_bits<8>(W, N, K, group, codes, scales, zeros, stream);
+        case 2: return launch_bits<2>(W, N, K, group, codes, scales, zeros, scheme, amax, stream);
+        case 3: return launch_bits<3>(W, N, K, group, codes, scales, zeros, scheme, amax, stream);
+        case 4: return launch_bits<4>(W, N, K, group, codes, scales, zeros, scheme, amax, stream);
+        case 5: return launch_bits<5>(W, N, K, group, codes, scales, zeros, scheme, amax, stream);
+        case 6: return launch_bits<6>(W, N, K, group, codes, scales, zeros, scheme, amax, stream);
+        case 7: return launch_bits<7>(W, N, K, group, codes, scales, zeros, scheme, amax, stream);
+        case 8: return launch_bits<8>(W, N, K, group, codes, scales, zeros, scheme, amax, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -26,8 +26,9 @@
  * Conventions shared by every entry point:
  *   - All array pointers are DEVICE pointers to row-major, contiguous buffers
  *     that the caller allocates, owns and frees.  The only memory the library
- *     allocates itself is the fp32 split-K workspace of the MFMA path
- *     (B * N * 4 bytes per K split): one buffer per (device, stream), taken in
+ *     allocates itself is a workspace: the fp32 split-K partials of the MFMA
+ *     paths (B * N * 4 bytes per K split) and the few KB of the per-tensor
+ *     maximum of wq_quantize_pack_ex: one buffer per (device, stream), taken in
  *     stream order (hipMallocAsync on `stream`) the first time a call on that
  *     stream needs it, grown the same way when a later call needs more, and
  *     kept for reuse until the process ends.  Calls on one stream reuse it in
@@ -92,6 +93,33 @@ typedef enum {
 wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
                            int32_t bits, void* codes, void* scales, void* zeros,
                            void* stream);
+
+/* Scale scheme for wq_quantize_pack_ex. */
+typedef enum {
+    WQ_SCHEME_ASYM = 0,       /* min/max per group, integer zero point (wq_quantize_pack) */
+    WQ_SCHEME_SYM = 1,        /* symmetric, absolute maximum per group */
+    WQ_SCHEME_SYM_TENSOR = 2  /* symmetric, one absolute maximum for the whole matrix */
+} wq_scheme;
+
+/*
+ * wq_quantize_pack with a choice of scale scheme.  The symmetric schemes
+ * follow "Quantization & inference optimisation", sections "Quantize a matrix
+ * by hand" and "Per-channel, and what it buys" (and the 2-bit levels of
+ * "Serving many users at once", "Quantization: rounding the weights"):
+ *     A = max |x| over the group (WQ_SCHEME_SYM; group = K gives one scale
+ *         per output channel) or over all of W (WQ_SCHEME_SYM_TENSOR)
+ *     s = fp16(round-half-even(A / (2^(bits-1) - 1)))  (1.0 if that is 0)
+ *     q = clamp(round-half-even(x / s), -2^(bits-1), 2^(bits-1) - 1)
+ * stored in the layout of wq_quantize_pack as the code q + 2^(bits-1) with
+ * zero point 2^(bits-1) in every group header (and, per tensor, the one scale
+ * repeated in every group header), so wq_gemm multiplies by q * s unchanged.
+ * Arguments, layout and errors as wq_quantize_pack; an unknown scheme is
+ * WQ_ERR_INVALID_ARG.  WQ_SCHEME_SYM_TENSOR enqueues two small reduction
+ * launches before the quantize launch and uses the stream's workspace.
+ */
+wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group,
+                              int32_t bits, int32_t scheme, void* codes, void* scales,
+                              void* zeros, void* stream);
 
 /*
  * Decode-step product with in-register dequantization ("Quantization &
@@ -174,7 +202,7 @@ const char* wq_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int32_t wq_version(void);
 
-#define WQ_VERSION 101
+#define WQ_VERSION 102
 
 #ifdef __cplusplus
 }

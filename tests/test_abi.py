@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = wq.load()
-    assert lib.wq_version() == 101
+    assert lib.wq_version() == 102
     for st in range(5):
         assert lib.wq_status_string(st)
     assert lib.wq_status_string(99) == b"unknown status"
@@ -93,6 +93,22 @@ def test_quantize_validation_errors():
     assert _quant(W=FAKE + 2) == _lib.WQ_ERR_MISALIGNED
     assert _quant(bits=8, C=FAKE + 4) == _lib.WQ_ERR_MISALIGNED
     assert _quant(bits=4, C=FAKE + 8) == _lib.WQ_ERR_MISALIGNED
+
+
+def _quant_ex(scheme, N=64, K=256, group=128, bits=4, W=FAKE, C=FAKE, S=FAKE, Z=FAKE):
+    return wq.load().wq_quantize_pack_ex(W, N, K, group, bits, scheme, C, S, Z, None)
+
+
+def test_quantize_ex_validation_errors():
+    for scheme in (_lib.WQ_SCHEME_SYM, _lib.WQ_SCHEME_SYM_TENSOR):
+        assert _quant_ex(scheme, N=0, W=0, C=0, S=0, Z=0) == _lib.WQ_OK
+        assert _quant_ex(scheme, K=250) == _lib.WQ_ERR_INVALID_ARG
+        assert _quant_ex(scheme, bits=1) == _lib.WQ_ERR_UNSUPPORTED
+        assert _quant_ex(scheme, W=0) == _lib.WQ_ERR_INVALID_ARG
+        assert _quant_ex(scheme, W=FAKE + 2) == _lib.WQ_ERR_MISALIGNED
+    assert _quant_ex(3) == _lib.WQ_ERR_INVALID_ARG
+    assert _quant_ex(-1) == _lib.WQ_ERR_INVALID_ARG
+    assert b"scheme" in wq.load().wq_last_error()
 
 
 def test_binding_raises_on_error():
