@@ -115,15 +115,29 @@ static wq_status check_gemm(const void* X, const void* codes, const void* scales
         return fail(WQ_ERR_INVALID_ARG, "wq_gemm: need B >= 0, N >= 0, K >= 1, group >= 1 (B=%lld K=%lld)", B, K);
     if (K % group != 0)
         return fail(WQ_ERR_INVALID_ARG, "wq_gemm: K=%lld is not a multiple of group=%lld", K, group);
-    if (bits != 4 && bits != 8)
-        return fail(bits >= 1 && bits <= 8 ? WQ_ERR_UNSUPPORTED : WQ_ERR_INVALID_ARG,
-                    "wq_gemm: bits=%lld (GPU kernels take 4 or 8)", bits);
+    if (bits < 1 || bits > 8)
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm: bits=%lld out of range", bits);
+    if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: bits=%lld (GPU kernels take 2, 3, 4 or 8)", bits);
     if (path < WQ_PATH_AUTO || path > WQ_PATH_MFMA)
         return fail(WQ_ERR_INVALID_ARG, "wq_gemm: unknown path %lld", path);
-    const int vals = 128 / bits;  // codes per 16-byte chunk
-    if (K % vals != 0 || group % vals != 0)
-        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: K=%lld and group=%lld must be multiples of the 16-byte chunk",
-                    K, group);
+    const bool low = bits == 2 || bits == 3;
+    if (low) {
+        // 32-code chunks inside one group; rows of whole 16-byte loads.
+        const int unit = bits == 2 ? 64 : 128;
+        if (K % unit != 0 || group % 32 != 0)
+            return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: bits 2/3 need K %% (64 or 128) == 0 and group %% 32 == 0 "
+                        "(K=%lld group=%lld)", K, group);
+    } else {
+        const int vals = 128 / bits;  // codes per 16-byte chunk
+        if (K % vals != 0 || group % vals != 0)
+            return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: K=%lld and group=%lld must be multiples of the 16-byte chunk",
+                        K, group);
+    }
+    if (low && path == WQ_PATH_MFMA)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: bits=%lld runs on the GEMV path only", bits);
+    if (low && !wq::gemv_lowbit_supports(K, group, bits))
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: the 2/3-bit GEMV does not take K=%lld at bits=%lld", K, bits);
     if (B == 0 || N == 0) {
         path = -1;
         return WQ_OK;
@@ -133,6 +147,10 @@ static wq_status check_gemm(const void* X, const void* codes, const void* scales
     if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(Y, 2))
         return fail(WQ_ERR_MISALIGNED, "wq_gemm: X and codes need 16-byte alignment");
 
+    if (low) {
+        path = WQ_PATH_GEMV;
+        return WQ_OK;
+    }
     const bool gemv_ok = wq::gemv_supports(K, bits);
     const bool mfma_ok = wq::mfma_supports(K, group, bits);
     int use = path;
@@ -156,6 +174,10 @@ static wq_status run_gemm(const void* X, const void* codes, const void* scales, 
         return check_hip(wq::launch_gemm_mfma(X, codes, scales, zeros, Y, B, K, N, group, bits,
                                               num_cus(), st),
                          "wq_gemm (mfma) launch");
+    if (bits == 2 || bits == 3)
+        return check_hip(wq::launch_gemv_lowbit(X, codes, scales, zeros, Y, B, K, N, group, bits,
+                                                num_cus(), st),
+                         "wq_gemm (2/3-bit gemv) launch");
     return check_hip(wq::launch_gemv(X, codes, scales, zeros, Y, B, K, N, group, bits, num_cus(), st),
                      "wq_gemm (gemv) launch");
 }

@@ -109,6 +109,22 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx) {
     }
 }
 
+// A 32-bit constant held in a VGPR.  gfx9 VOP3 instructions take no literal
+// operand, so keeping unpack masks in registers lets every unpack step be a
+// single v_and_or_b32 (mask from a VGPR, the 0x6400 exponent from an SGPR).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+    return r;
+}
+
+// 128-bit load that bypasses cache allocation: every code byte is read once.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // Unsigned nibble/byte codes to fp16 pairs via the exponent trick: OR-ing a
 // code c < 1024 into the mantissa of 1024.0 (0x6400) gives exactly 1024 + c.
 // 4-bit: word w holds codes k..k+7 (code i in bits 4i..4i+3).  Pair p (0..3)

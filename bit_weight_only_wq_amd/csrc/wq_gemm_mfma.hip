@@ -59,14 +59,6 @@ __device__ __forceinline__ uint4 permute8(uint4 in) {
     return o;
 }
 
-// A 32-bit constant held in a VGPR, so that each unpack step is one
-// v_and_or_b32 (gfx9 VOP3 instructions take no literal operand).
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
-    uint32_t r;
-    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-    return r;
-}
-
 struct DqConsts {
     uint32_t m_lo, m_hi, g_lo, g_hi;  // nibble/byte masks and exponent patterns
 };

@@ -109,12 +109,6 @@ struct XrReduce {
     int32_t count;
 };
 
-__device__ __forceinline__ uint32_t vreg(uint32_t v) {
-    uint32_t r;
-    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-    return r;
-}
-
 // X vector reordered to the unpack order (see above).
 template <int BITS>
 __device__ __forceinline__ uint4 order8(uint4 in) {
@@ -330,8 +324,8 @@ __global__ __launch_bounds__(xr_waves(BTX) * 64) void gemm_xr_kernel(const XrLau
     // above keep streaming through the barrier.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    const Consts cst = BITS == 4 ? Consts{vreg(0x000F000Fu), vreg(0x00F000F0u), vreg(0x64006400u), vreg(0x54005400u)}
-                                 : Consts{vreg(0x00FF00FFu), 0u, vreg(0x64006400u), 0u};
+    const Consts cst = BITS == 4 ? Consts{vgpr_const(0x000F000Fu), vgpr_const(0x00F000F0u), vgpr_const(0x64006400u), vgpr_const(0x54005400u)}
+                                 : Consts{vgpr_const(0x00FF00FFu), 0u, vgpr_const(0x64006400u), 0u};
     // A operand of column block cb: batch row cb*16 + r16 (mod BTX), 8 k at the
     // lane group's offset.  Accumulator lane layout: batch rows
     // cb*16 + 4*g4 + i (mod BTX), weight row r16.  The unpacked codes of a

@@ -47,27 +47,11 @@ __device__ __forceinline__ void pair_positions(int j, int p, int& a, int& b) {
     }
 }
 
-// A 32-bit constant held in a VGPR.  gfx9 VOP3 instructions take no literal
-// operand, so keeping the nibble masks in registers lets every unpack step be
-// a single v_and_or_b32 (mask from a VGPR, the 0x6400 exponent from an SGPR).
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
-    uint32_t r;
-    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-    return r;
-}
-
 // Wave-scope ordering of LDS accesses made by the lanes of one wave.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// 128-bit load that bypasses cache allocation: every code byte is read once.
-__device__ __forceinline__ uint4 load_stream(const uint4* p) {
-    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-    return make_uint4(t.x, t.y, t.z, t.w);
 }
 
 // Buffer resource word 3 for raw (unformatted, unswizzled) gfx9 buffers.

@@ -19,6 +19,12 @@ hipError_t launch_gemv(const void* X, const void* codes, const void* scales,
                        const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                        int32_t group, int32_t bits, int num_cus, hipStream_t stream);
 
+// 2- and 3-bit GEMV (any batch; codes re-streamed once per 4 batch rows).
+bool gemv_lowbit_supports(int64_t K, int32_t group, int32_t bits);
+hipError_t launch_gemv_lowbit(const void* X, const void* codes, const void* scales,
+                              const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
+                              int32_t group, int32_t bits, int num_cus, hipStream_t stream);
+
 // Matrix-core family: the X-resident kernel for B <= 32 (xr_*), the tiled
 // kernel beyond.
 bool xr_supports(int64_t B, int64_t K, int32_t group, int32_t bits);

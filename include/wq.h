@@ -135,6 +135,12 @@ wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group
  * bits 4: K % 32 == 0 and group % 32 == 0.  bits 8: K % 16 == 0 and
  * group % 16 == 0.  The MFMA path additionally needs group % 128 (bits 4) or
  * group % 64 (bits 8); WQ_PATH_AUTO falls back to the GEMV path otherwise.
+ * bits 2 and 3 (the bit-stream layout of wq_quantize_pack; "Quantization &
+ * inference optimisation", "Quantization", prints their errors next to 4 and
+ * 8 bits): group % 32 == 0, K % 64 == 0 (bits 2) or K % 128 == 0 (bits 3),
+ * K <= 32768; GEMV path only, at any B (the codes are streamed once per four
+ * batch rows, so large batches are correct but not fast); bits 1, 5, 6 and 7
+ * are WQ_ERR_UNSUPPORTED.
  * Results are deterministic: no atomics, fixed reduction order.
  */
 wq_status wq_gemm(const void* X, const void* codes, const void* scales,

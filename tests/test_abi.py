@@ -64,7 +64,16 @@ def test_gemm_validation_errors():
     assert _gemm(B=-1) == _lib.WQ_ERR_INVALID_ARG
     assert _gemm(K=0) == _lib.WQ_ERR_INVALID_ARG
     assert _gemm(group=0) == _lib.WQ_ERR_INVALID_ARG
-    assert _gemm(bits=3) == _lib.WQ_ERR_UNSUPPORTED
+    assert _gemm(bits=5) == _lib.WQ_ERR_UNSUPPORTED
+    assert _gemm(bits=1) == _lib.WQ_ERR_UNSUPPORTED
+    # 2/3 bits: 32-code chunks in one group, rows of whole 16-byte loads,
+    # GEMV path only (all rejected before any launch).
+    assert _gemm(bits=3, K=192, group=64) == _lib.WQ_ERR_UNSUPPORTED
+    assert _gemm(bits=2, K=256, group=16) == _lib.WQ_ERR_UNSUPPORTED
+    assert _gemm(bits=2, K=32, group=32) == _lib.WQ_ERR_UNSUPPORTED
+    assert _gemm(bits=2, path=_lib.WQ_PATH_MFMA) == _lib.WQ_ERR_UNSUPPORTED
+    assert _gemm(bits=3, K=65536, group=128) == _lib.WQ_ERR_UNSUPPORTED
+    assert _gemm(bits=3, C=FAKE + 8) == _lib.WQ_ERR_MISALIGNED
     assert _gemm(bits=9) == _lib.WQ_ERR_INVALID_ARG
     assert _gemm(path=7) == _lib.WQ_ERR_INVALID_ARG
     assert _gemm(group=16, K=256) == _lib.WQ_ERR_UNSUPPORTED  # chunk spans groups
@@ -124,7 +133,7 @@ def test_grouped_validates_every_item_first():
     """An invalid item anywhere makes the whole call fail before any launch;
     the error names the item."""
     lib = wq.load()
-    for bad, st in [(dict(K=200), _lib.WQ_ERR_INVALID_ARG), (dict(bits=3), _lib.WQ_ERR_UNSUPPORTED),
+    for bad, st in [(dict(K=200), _lib.WQ_ERR_INVALID_ARG), (dict(bits=5), _lib.WQ_ERR_UNSUPPORTED),
                     (dict(X=FAKE + 2), _lib.WQ_ERR_MISALIGNED), (dict(Y=0), _lib.WQ_ERR_INVALID_ARG)]:
         arr = (_lib.GemmItem * 3)(_item(), _item(B=32), _item(**bad))
         assert lib.wq_gemm_grouped(arr, 3, None) == st

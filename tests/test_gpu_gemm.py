@@ -141,13 +141,14 @@ def test_workload_full_size_sampled(name):
     N, K, G, bits = cfg["N"], cfg["K"], cfg["group"], cfg["bits"]
     W, X = workload(name)
     codes, scales, zeros = wq.quantize_pack(to_dev(W), G, bits)
-    hc, hs, hz = codes.cpu().numpy(), scales.cpu().numpy(), zeros.cpu().numpy()
     rows = np.unique(np.concatenate([np.random.default_rng(16).choice(N, SAMPLE, replace=False),
                                      [0, N - 1]]))
+    # Rows are independent: the oracle quantizes and multiplies only the sample.
+    hc, hs, hz = oracle.quantize(W[rows], G, bits)
     for B in cfg["batches"]:
         note(f"{name} B={B} auto path")
         Y = wq.gemm(to_dev(X[:B]), codes, scales, zeros, N=N, K=K, group=G, bits=bits)
-        ref = oracle.gemm(X[:B], hc, hs, hz, N, K, G, bits, rows=rows)
+        ref = oracle.gemm(X[:B], hc, hs, hz, len(rows), K, G, bits)
         assert_close(Y.cpu().numpy()[:, rows].astype(np.float64), ref, f"{name} B={B}")
 
 
@@ -161,6 +162,5 @@ def test_decode_set_layer0_b32(index):
         note(f"decode-set #{index} G={group} b={bits} B=32")
         codes, scales, zeros = wq.quantize_pack(to_dev(W), group, bits)
         Y = wq.gemm(to_dev(X), codes, scales, zeros, N=N, K=K, group=group, bits=bits)
-        ref = oracle.gemm(X, codes.cpu().numpy(), scales.cpu().numpy(), zeros.cpu().numpy(),
-                          N, K, group, bits, rows=rows)
+        ref = oracle.gemm(X, *oracle.quantize(W[rows], group, bits), len(rows), K, group, bits)
         assert_close(Y.cpu().numpy()[:, rows].astype(np.float64), ref, f"#{index} b={bits}")

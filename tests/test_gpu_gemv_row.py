@@ -65,7 +65,8 @@ def test_misaligned_headers_fall_back():
     N, K, G = 300, 8192, 128
     rng = np.random.default_rng(5)
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
-    X = to_dev(rng.standard_normal((1, K)).astype(np.float16))
+    Xh = rng.standard_normal((1, K)).astype(np.float16)
+    X = to_dev(Xh)
     host, (c, s, z) = packed(W, G, 4)
     ngrp = K // G
     sbuf = torch.zeros(N * ngrp + 1, dtype=torch.float16, device=s.device)
@@ -78,5 +79,5 @@ def test_misaligned_headers_fall_back():
     note(f"gemv misaligned headers N={N} K={K}")
     y_al = wq.gemm(X, c, s, z, N=N, K=K, group=G, bits=4, path="gemv").cpu().numpy()
     y_mis = wq.gemm(X, c, s_odd, z_odd, N=N, K=K, group=G, bits=4, path="gemv").cpu().numpy()
-    assert_close(y_mis.astype(np.float64), oracle.gemm(X.cpu().numpy(), *host, N, K, G, 4), "misaligned")
+    assert_close(y_mis.astype(np.float64), oracle.gemm(Xh, *host, N, K, G, 4), "misaligned")
     assert_close(y_al.astype(np.float64), y_mis.astype(np.float64), "aligned vs misaligned")
