@@ -51,6 +51,11 @@ def parse():
     p.add_argument("--decode-set", action="store_true",
                    help="7B-class decode step, 224 products at B=32 (table)")
     p.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
+    p.add_argument("--bits", type=int, default=0,
+                   help="code width of the step (default: the workload's, 4); 2 and 3 take "
+                        "the bit-stream GEMV")
+    p.add_argument("--batches", default="",
+                   help="comma-separated batch sizes of the step (default: the workload's)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after timing, copy this many MiB device-to-device once (a "
                         "known-size kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -205,7 +210,7 @@ def write_traffic_summaries(args):
                 print("wrote", os.path.relpath(path, ROOT))
 
 
-def cpu_baseline(name, batches):
+def cpu_baseline(name, batches, bits=0):
     import numpy as np
     import oracle
     import wq_inputs
@@ -213,7 +218,8 @@ def cpu_baseline(name, batches):
     cfg = wq_inputs.WORKLOADS[name]
     rows = min(CPU_SAMPLE_ROWS, cfg["N"])
     W, X = wq_inputs.workload_arrays(name, rows=rows)
-    K, G, bits = cfg["K"], cfg["group"], cfg["bits"]
+    K, G = cfg["K"], cfg["group"]
+    bits = bits or cfg["bits"]
     oracle.build(force=False)
     reps = 0
     t0 = time.perf_counter()
@@ -243,7 +249,10 @@ def run_step_bench(args):
 
     cfg = wq_inputs.WORKLOADS[args.workload]
     N, K, G, bits = cfg["N"], cfg["K"], cfg["group"], cfg["bits"]
+    bits = args.bits or bits
     batches = [b for b in cfg["batches"] if b <= 64] or [1]
+    if args.batches:
+        batches = [int(b) for b in args.batches.split(",")]
     dev = torch.device("cuda:0")
     Wn, Xn = wq_inputs.workload_arrays(args.workload)
     Wd = [torch.from_numpy(Wn).to(dev) for _ in range(2)]
@@ -332,7 +341,8 @@ def run_step_bench(args):
         "wq_quantize_pack", rl.quantize_bytes(N, K, G, bits), 0, [per_q])
 
     head = kernels[f"wq_gemm_B{batches[0]}"]
-    traffic = read_traffic(f"wq_gemm_b{batches[0]}_{args.workload}")
+    # Counter summaries exist for the workload's own code width only.
+    traffic = read_traffic(f"wq_gemm_b{batches[0]}_{args.workload}") if bits == cfg["bits"] else None
     roof = {"kernel": head["kernel"], "bound": "hbm", "achieved": head["achieved_GBps"],
             "peak": rl.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
             "frac": round(head["achieved_GBps"] * 1e9 / rl.MI355X_HBM_BYTES_PER_S, 4),
@@ -549,7 +559,7 @@ def main():
         torch.mul(a, 3, out=b)
         torch.cuda.synchronize()
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args.workload, batches)
+        out["cpu_baseline"] = cpu_baseline(args.workload, batches, args.bits)
     print(json.dumps(out), flush=True)
 
 
