@@ -16,6 +16,9 @@ What it computes (see oracle.c for the step-by-step citations):
       tensor, stored in the same layout with zero point 2^(b-1).
   dequantize(...)           -> W_hat float64 [N, K] = (q - z) * s
   gemm(X, ...)              -> Y_ref float64 [B, N] = X W_hat^T in double.
+  kv (submodule)            decode attention over an int4 KV cache: the codec
+      above per channel for K and per token for V, dequantized, softmax in
+      float64 ("What actually happens when you quantize a KV cache").
 
 Parity status: the quantizer and packer are pinned by the worked groups of
 that page and by an exact-rational brute force; the symmetric variant by the
