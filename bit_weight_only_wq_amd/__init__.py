@@ -15,8 +15,8 @@ from . import roofline  # noqa: F401  (pure arithmetic, no GPU)
 from ._lib import (WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA, WQError,  # noqa: F401
                    LIB_PATH, check, load)
 
-__all__ = ["quantize_pack", "gemm", "codes_bytes", "num_groups", "gemv_max_batch",
-           "WQError", "LIB_PATH", "load"]
+__all__ = ["quantize_pack", "gemm", "gemm_grouped", "codes_bytes", "num_groups", "gemv_max_batch",
+           "KVCache", "kv_quantize_block", "kv_attention", "WQError", "LIB_PATH", "load"]
 
 _PATHS = {"auto": WQ_PATH_AUTO, "gemv": WQ_PATH_GEMV, "mfma": WQ_PATH_MFMA}
 
@@ -147,4 +147,67 @@ def gemm(X, codes, scales, zeros, N: int, K: int, group: int = 128, bits: int = 
                             out.data_ptr(), B, K, N, group, bits, _PATHS[path],
                             _stream_handle(X.device))
     check(st, "wq_gemm")
+    return out
+
+
+class KVCache:
+    """Caller-owned buffers of an int4 KV cache (head dimension 128, blocks of
+    128 tokens), as torch tensors on one GPU; layout as wq_kv_cache in wq.h."""
+
+    D = 128
+    G = 128
+
+    def __init__(self, heads: int, max_blocks: int, device="cuda"):
+        import torch
+        u8, f16 = torch.uint8, torch.float16
+        H, NB, D, G = heads, max_blocks, self.D, self.G
+        self.heads, self.max_blocks = heads, max_blocks
+        self.kcodes = torch.zeros((H, NB, G, D // 2), dtype=u8, device=device)
+        self.kscales = torch.zeros((H, NB, D), dtype=f16, device=device)
+        self.kzeros = torch.zeros((H, NB, D), dtype=f16, device=device)
+        self.vcodes = torch.zeros((H, NB, D, G // 2), dtype=u8, device=device)
+        self.vscales = torch.zeros((H, NB * G), dtype=f16, device=device)
+        self.vzeros = torch.zeros((H, NB * G), dtype=f16, device=device)
+        self.kres = torch.zeros((H, G, D), dtype=f16, device=device)
+        self.vres = torch.zeros((H, G, D), dtype=f16, device=device)
+
+    @property
+    def device(self):
+        return self.kcodes.device
+
+    def descriptor(self):
+        from ._lib import KvCache
+        return KvCache(self.kcodes.data_ptr(), self.kscales.data_ptr(), self.kzeros.data_ptr(),
+                       self.vcodes.data_ptr(), self.vscales.data_ptr(), self.vzeros.data_ptr(),
+                       self.kres.data_ptr(), self.vres.data_ptr(), self.heads, self.max_blocks)
+
+
+def kv_quantize_block(K, V, cache: KVCache, block: int):
+    """K, V fp16 [heads, 128, 128] (token-major) -> block `block` of every head."""
+    import ctypes
+    import torch
+    shape = (cache.heads, cache.G, cache.D)
+    _need(K, torch.float16, shape, "K")
+    _need(V, torch.float16, shape, "V")
+    desc = cache.descriptor()
+    with torch.cuda.device(cache.device):
+        st = load().wq_kv_quantize_block(K.data_ptr(), V.data_ptr(), ctypes.byref(desc), block,
+                                         _stream_handle(cache.device))
+    check(st, "wq_kv_quantize_block")
+
+
+def kv_attention(q, cache: KVCache, lens, out=None):
+    """q fp16 [heads, 128], lens int32 [heads] (GPU) -> out fp16 [heads, 128]."""
+    import ctypes
+    import torch
+    _need(q, torch.float16, (cache.heads, cache.D), "q")
+    _need(lens, torch.int32, (cache.heads,), "lens")
+    if out is None:
+        out = torch.empty((cache.heads, cache.D), dtype=torch.float16, device=q.device)
+    _need(out, torch.float16, (cache.heads, cache.D), "out")
+    desc = cache.descriptor()
+    with torch.cuda.device(cache.device):
+        st = load().wq_kv_attention(q.data_ptr(), ctypes.byref(desc), lens.data_ptr(), out.data_ptr(),
+                                    _stream_handle(cache.device))
+    check(st, "wq_kv_attention")
     return out

@@ -34,12 +34,21 @@ class GemmItem(ctypes.Structure):
                 ("B", _I64), ("K", _I64), ("N", _I64), ("group", _I32), ("bits", _I32)]
 
 
+class KvCache(ctypes.Structure):
+    """wq_kv_cache: the buffers of an int4 KV cache (device pointers)."""
+    _fields_ = [("kcodes", _P), ("kscales", _P), ("kzeros", _P), ("vcodes", _P),
+                ("vscales", _P), ("vzeros", _P), ("kres", _P), ("vres", _P),
+                ("heads", _I64), ("max_blocks", _I64)]
+
+
 SIGNATURES = {
     "wq_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _P, _P, _P]),
     "wq_quantize_pack_ex": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
     "wq_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P]),
     "wq_gemm_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
     "wq_gemm_grouped": (ctypes.c_int, [ctypes.POINTER(GemmItem), _I32, _P]),
+    "wq_kv_quantize_block": (ctypes.c_int, [_P, _P, ctypes.POINTER(KvCache), _I64, _P]),
+    "wq_kv_attention": (ctypes.c_int, [_P, ctypes.POINTER(KvCache), _P, _P, _P]),
     "wq_gemv_max_batch": (_I32, []),
     "wq_codes_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
     "wq_num_groups": (_I64, [_I64, _I64, _I32]),

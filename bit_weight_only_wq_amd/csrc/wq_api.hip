@@ -250,6 +250,56 @@ wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream
     return WQ_OK;
 }
 
+// Validates a cache descriptor (not its contents) and copies it into `a`.
+static wq_status check_kv_cache(const wq_kv_cache* c, wq::KvCacheArgs& a) {
+    if (!c) return fail(WQ_ERR_INVALID_ARG, "kv cache: null descriptor");
+    if (c->heads < 0 || c->max_blocks < 1 || c->heads > ((int64_t)1 << 31) - 1 ||
+        c->max_blocks > ((int64_t)1 << 24))
+        return fail(WQ_ERR_INVALID_ARG, "kv cache: need heads >= 0, 1 <= max_blocks <= 2^24 (heads=%lld max_blocks=%lld)",
+                    c->heads, c->max_blocks);
+    if (c->heads > 0) {
+        if (!c->kcodes || !c->kscales || !c->kzeros || !c->vcodes || !c->vscales || !c->vzeros || !c->kres ||
+            !c->vres)
+            return fail(WQ_ERR_INVALID_ARG, "kv cache: null buffer");
+        if (!aligned(c->kcodes, 16) || !aligned(c->vcodes, 16) || !aligned(c->kres, 16) || !aligned(c->vres, 16) ||
+            !aligned(c->kscales, 2) || !aligned(c->kzeros, 2) || !aligned(c->vscales, 2) || !aligned(c->vzeros, 2))
+            return fail(WQ_ERR_MISALIGNED, "kv cache: code and residual buffers need 16-byte alignment");
+    }
+    a = wq::KvCacheArgs{c->kcodes, c->kscales, c->kzeros, c->vcodes, c->vscales, c->vzeros,
+                        c->kres,   c->vres,    c->heads,  c->max_blocks};
+    return WQ_OK;
+}
+
+wq_status wq_kv_quantize_block(const void* K, const void* V, const wq_kv_cache* cache, int64_t block,
+                               void* stream) {
+    g_last_error[0] = '\0';
+    wq::KvCacheArgs a;
+    const wq_status st = check_kv_cache(cache, a);
+    if (st != WQ_OK) return st;
+    if (block < 0 || block >= a.max_blocks)
+        return fail(WQ_ERR_INVALID_ARG, "wq_kv_quantize_block: block=%lld outside [0, %lld)", block, a.max_blocks);
+    if (a.heads == 0) return WQ_OK;
+    if (!K || !V) return fail(WQ_ERR_INVALID_ARG, "wq_kv_quantize_block: null K or V");
+    if (!aligned(K, 16) || !aligned(V, 16))
+        return fail(WQ_ERR_MISALIGNED, "wq_kv_quantize_block: K and V need 16-byte alignment");
+    return check_hip(wq::launch_kv_quantize(K, V, a, block, static_cast<hipStream_t>(stream)),
+                     "wq_kv_quantize_block launch");
+}
+
+wq_status wq_kv_attention(const void* q, const wq_kv_cache* cache, const int32_t* lens, void* out,
+                          void* stream) {
+    g_last_error[0] = '\0';
+    wq::KvCacheArgs a;
+    const wq_status st = check_kv_cache(cache, a);
+    if (st != WQ_OK) return st;
+    if (a.heads == 0) return WQ_OK;
+    if (!q || !lens || !out) return fail(WQ_ERR_INVALID_ARG, "wq_kv_attention: null q, lens or out");
+    if (!aligned(q, 2) || !aligned(out, 2) || !aligned(lens, 4))
+        return fail(WQ_ERR_MISALIGNED, "wq_kv_attention: q/out need 2-byte and lens 4-byte alignment");
+    return check_hip(wq::launch_kv_attention(q, a, lens, out, num_cus(), static_cast<hipStream_t>(stream)),
+                     "wq_kv_attention launch");
+}
+
 wq_status wq_gemm(const void* X, const void* codes, const void* scales, const void* zeros,
                   void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
                   void* stream) {

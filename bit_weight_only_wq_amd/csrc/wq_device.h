@@ -76,6 +76,31 @@ __device__ __forceinline__ uint16_t zero_bits_from_int(float k) {
     return b;
 }
 
+// Per-group header of the asymmetric codec from the exact min and max of a
+// group with M = 2^b - 1 steps: fp16 scale and zero point, and what the
+// encoder needs (reciprocal, zero point as a float, tie-safety threshold).
+struct GroupHeader {
+    float s, rcp, Z, thr;
+    uint16_t sbits, zbits;
+};
+
+__device__ __forceinline__ GroupHeader make_header(float mn, float mx, int M) {
+    GroupHeader h;
+    h.sbits = scale_bits_exact(mn, mx, M);
+    h.s = half_bits_to_float(h.sbits);
+    h.rcp = __builtin_amdgcn_rcpf(h.s);
+    // z = round(-min / s): estimates beyond +-2^17 all saturate the fp16 zero.
+    float k = rne_div_exact(-mn, h.s, h.rcp, -131072.0f, 131072.0f);
+    h.zbits = zero_bits_from_int(k);
+    h.Z = half_bits_to_float(h.zbits);
+    // |x*rcp - x/s| <= |x/s| * 2^-22 (rcp within 1 ulp, one rounding of the
+    // product).  A fraction |t - rint(t)| at most thr therefore cannot be a tie
+    // or on the wrong side of one; thr keeps a 4x margin on that bound.
+    const float tmax = __builtin_fmaxf(__builtin_fabsf(mn), __builtin_fabsf(mx)) * h.rcp;
+    h.thr = 0.5f - (tmax + 1.0f) * 0x1p-20f;
+    return h;
+}
+
 // ---------------------------------------------------------------------------
 // Wavefront reductions.  DPP moves inside 16-lane rows, then cross-row steps.
 // ---------------------------------------------------------------------------

@@ -1,0 +1,483 @@
+// Decode attention over an int4 KV cache (gfx950), and the quantize-on-append
+// step that fills it.
+//
+// "What actually happens when you quantize a KV cache": one decode step
+// scores the new query against every cached key and averages the values with
+// the softmax weights (§2); the cache holds the group-wise asymmetric int4
+// codec of §3-§4, K grouped per channel over 128 tokens and V per token (§7
+// "axis choice"), with the newest tokens that do not fill a K group in fp16;
+// the step streams the whole cache, so it is bandwidth-bound (§6).
+//
+// Cache of one head (head dimension D = 128, blocks of G = 128 tokens):
+//   kcodes [blocks][G tokens][64 B]   token-major: byte i of token t holds
+//                                     channels 2i (low nibble) and 2i+1
+//   kscales, kzeros [blocks][D]       fp16, one per channel per block
+//   vcodes [blocks][D channels][64 B] channel-major: byte i of channel d
+//                                     holds tokens 2i (low nibble) and 2i+1
+//   vscales, vzeros [blocks * G]      fp16, one per token
+//   kres, vres [G][D]                 fp16, the residual tokens (token-major)
+// Codes are stored against the grouping axis on purpose: a score is
+//   sum_d q_d s_d (c_td - z_d) = sum_d a_d c_td - sum_d a_d z_d,  a_d = q_d s_d,
+// a dot product along a 64-byte token row with a per-block vector a, and an
+// output channel is
+//   sum_t p_t s_t (c_dt - z_t) = sum_t w_t c_dt - sum_t w_t z_t,  w_t = p_t s_t,
+// a dot product along a 64-byte channel row with a per-block vector w.  Both
+// run like the weight GEMV: codes unpack to fp16 (1024 + c) or (1024 + 16c)
+// pairs with one AND-OR, and v_dot2_f32_f16 multiplies them by a or w, held as
+// an fp16 hi/lo pair (a = hi + lo to 2^-22) so the products keep fp32
+// accuracy; the offsets and zero points enter once per block.
+//
+// Attention is split over the context (flash decoding): each (head, split)
+// workgroup streams its blocks with a running max, sum and output, and a
+// second kernel combines the splits.  Scores are kept in log2 units (log2(e)
+// and 1/sqrt(D) folded into a), so the softmax uses v_exp_f32 directly.
+#include "wq_device.h"
+#include "wq_launch.h"
+
+namespace wq {
+
+namespace {
+
+constexpr int kD = 128;         // head dimension
+constexpr int kG = 128;         // tokens per block
+constexpr int kRow = 64;        // bytes per code row
+constexpr uint32_t kMagic = 0x64006400u;
+
+// LDS slot (in fp16 units) of position u (0..127) of a row in unpack order:
+// quarter k = u / 32 is one 16-byte chunk; within it word j = (u % 32) / 8
+// holds 8 codes, unpacked as the pairs (0,4) (1,5) (2,6) (3,7) -> uint4
+// components x, y, z, w; the first code of a pair is the low half.
+__device__ __forceinline__ int pair_slot(int u) {
+    const int k = u >> 5, j = (u >> 3) & 3, r = u & 7;
+    return (((k * 4 + j) * 4 + (r & 3)) << 1) | (r >> 2);
+}
+
+// Offset that position u carries in the unpacked pair: 1024 (even u) or,
+// after the 1/16 rescale, 64 (odd u).
+__device__ __forceinline__ float unpack_offset(int u) { return (u & 1) ? 64.0f : 1024.0f; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// dot of one 16-byte chunk (32 codes) with the hi/lo vector of its quarter
+// (xh, xl: 4 uint4 each), codes as (1024 + c) / (1024 + 16c) pairs.
+__device__ __forceinline__ float chunk_dot_hl(const uint4& w4, const uint4* xh, const uint4* xl,
+                                              uint32_t m_lo, uint32_t m_hi) {
+    const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+    float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t sh = w[j] >> 8;
+        const h2_t q04 = as_h2((w[j] & m_lo) | kMagic);
+        const h2_t q15 = as_h2((w[j] & m_hi) | kMagic);
+        const h2_t q26 = as_h2((sh & m_lo) | kMagic);
+        const h2_t q37 = as_h2((sh & m_hi) | kMagic);
+        pa = __builtin_amdgcn_fdot2(q04, as_h2(xh[j].x), pa, false);
+        pa = __builtin_amdgcn_fdot2(q04, as_h2(xl[j].x), pa, false);
+        pb = __builtin_amdgcn_fdot2(q15, as_h2(xh[j].y), pb, false);
+        pb = __builtin_amdgcn_fdot2(q15, as_h2(xl[j].y), pb, false);
+        pa = __builtin_amdgcn_fdot2(q26, as_h2(xh[j].z), pa, false);
+        pa = __builtin_amdgcn_fdot2(q26, as_h2(xl[j].z), pa, false);
+        pb = __builtin_amdgcn_fdot2(q37, as_h2(xh[j].w), pb, false);
+        pb = __builtin_amdgcn_fdot2(q37, as_h2(xl[j].w), pb, false);
+    }
+    return __builtin_fmaf(pb, 0.0625f, pa);
+}
+
+// Sum of a value held by threads 0..127 (others pass 0), returned to all.
+__device__ __forceinline__ float block_sum128(float v, float* red) {
+    v = group_sum<64>(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float t = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ float block_max256(float v, float* red) {
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float t = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    __syncthreads();
+    return t;
+}
+
+struct KvPtrs {
+    const uint8_t* kc;
+    const uint16_t* ks;
+    const uint16_t* kz;
+    const uint8_t* vc;
+    const uint16_t* vs;
+    const uint16_t* vz;
+    const uint16_t* kr;
+    const uint16_t* vr;
+    int64_t max_blocks;
+};
+
+// One workgroup per (head, split).  Thread i: quad i/4 owns rows r0 = i/4 and
+// r0 + 64 of a block (tokens in the score phase, channels in the output
+// phase), lane i%4 the quarter (32 codes) of those rows.
+__global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict__ Q, const KvPtrs P,
+                                                      const int32_t* __restrict__ lens, int splits,
+                                                      float q_scale, float* __restrict__ part,
+                                                      uint16_t* __restrict__ out) {
+    __shared__ __align__(16) uint16_t xh[kD];       // hi halves in unpack order
+    __shared__ __align__(16) uint16_t xl[kD];       // lo halves
+    __shared__ float qf[kD];
+    __shared__ float pr[kG];                        // residual-token weights
+    __shared__ float red[4];
+
+    const int h = blockIdx.x;
+    const int sp = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int quad = tid >> 2, qk = tid & 3;
+    const int r0 = quad, r1 = quad + 64;
+
+    // Tokens of this head, clamped to what the cache holds.
+    int64_t len = lens[h];
+    const int64_t cap = P.max_blocks * kG + (kG - 1);
+    len = len < 0 ? 0 : (len > cap ? cap : len);
+    const int nblk = (int)(len / kG) < P.max_blocks ? (int)(len / kG) : (int)P.max_blocks;
+    const int nres = (int)(len - (int64_t)nblk * kG);
+    const int bps = (nblk + splits - 1) / splits;
+    const int j0 = sp * bps;
+    const int j1 = (j0 + bps) < nblk ? (j0 + bps) : nblk;
+    const bool last = sp == splits - 1;
+
+    if (tid < kD) qf[tid] = half_bits_to_float(Q[(int64_t)h * kD + tid]) * q_scale;
+    __syncthreads();
+
+    const uint32_t m_lo = vgpr_const(0x000F000Fu);
+    const uint32_t m_hi = vgpr_const(0x00F000F0u);
+    float M = -__builtin_huge_valf();    // running max (log2 units)
+    float lsum = 0.0f;                   // this thread's share of sum p (lane qk == 0 rows)
+    float o0 = 0.0f, o1 = 0.0f;          // output channels r0, r1 (all four lanes of the quad)
+
+    const int64_t hb = (int64_t)h * P.max_blocks;
+    for (int j = j0; j < j1; ++j) {
+        const int64_t blk = hb + j;
+        // Codes of this block for this thread (K rows = tokens, V rows = channels).
+        const uint4* kc = reinterpret_cast<const uint4*>(P.kc + blk * (kG * kRow));
+        const uint4* vc = reinterpret_cast<const uint4*>(P.vc + blk * (kD * kRow));
+        const uint4 k0 = load_stream(kc + r0 * 4 + qk);
+        const uint4 k1 = load_stream(kc + r1 * 4 + qk);
+        const uint4 v0 = load_stream(vc + r0 * 4 + qk);
+        const uint4 v1 = load_stream(vc + r1 * 4 + qk);
+
+        // ---- K side: a_d = q_d s_d as hi/lo, and C_K = sum_d a_d (off_d + z_d).
+        float ck = 0.0f;
+        if (tid < kD) {
+            const float s = half_bits_to_float(P.ks[blk * kD + tid]);
+            const float z = half_bits_to_float(P.kz[blk * kD + tid]);
+            const float a = qf[tid] * s;
+            const _Float16 ah = (_Float16)a;
+            const _Float16 al = (_Float16)(a - (float)ah);
+            xh[pair_slot(tid)] = __builtin_bit_cast(uint16_t, ah);
+            xl[pair_slot(tid)] = __builtin_bit_cast(uint16_t, al);
+            ck = ((float)ah + (float)al) * (unpack_offset(tid) + z);
+        }
+        const float CK = block_sum128(ck, red);     // (its barrier also publishes xh/xl)
+        const uint4* hq = reinterpret_cast<const uint4*>(xh) + qk * 4;
+        const uint4* lq = reinterpret_cast<const uint4*>(xl) + qk * 4;
+        float s0 = group_sum<4>(chunk_dot_hl(k0, hq, lq, m_lo, m_hi)) - CK;
+        float s1 = group_sum<4>(chunk_dot_hl(k1, hq, lq, m_lo, m_hi)) - CK;
+
+        // ---- softmax update over the block's 128 scores.
+        const float bm = block_max256(__builtin_fmaxf(s0, s1), red);
+        const float Mn = __builtin_fmaxf(M, bm);
+        const float alpha = exp2_fast(M - Mn);
+        M = Mn;
+        const float p0 = exp2_fast(s0 - Mn), p1 = exp2_fast(s1 - Mn);
+        lsum = lsum * alpha + (qk == 0 ? p0 + p1 : 0.0f);
+        o0 *= alpha;
+        o1 *= alpha;
+
+        // ---- V side: w_t = p_t s_t as hi/lo, C_V = sum_t w_t (off_t + z_t).
+        float cv = 0.0f;
+        if (qk == 0) {
+            const int64_t tb = (int64_t)blk * kG;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int t = e ? r1 : r0;
+                const float w = (e ? p1 : p0) * half_bits_to_float(P.vs[tb + t]);
+                const _Float16 wh = (_Float16)w;
+                const _Float16 wl = (_Float16)(w - (float)wh);
+                xh[pair_slot(t)] = __builtin_bit_cast(uint16_t, wh);
+                xl[pair_slot(t)] = __builtin_bit_cast(uint16_t, wl);
+                cv += ((float)wh + (float)wl) * (unpack_offset(t) + half_bits_to_float(P.vz[tb + t]));
+            }
+        }
+        // Threads 0..127 hold the sum's inputs only partly (qk == 0 lanes of
+        // all 64 quads): fold the other 128 threads in through LDS as well.
+        cv = group_sum<64>(cv);
+        if ((tid & 63) == 0) red[tid >> 6] = cv;
+        __syncthreads();
+        const float CV = red[0] + red[1] + red[2] + red[3];
+        o0 += group_sum<4>(chunk_dot_hl(v0, hq, lq, m_lo, m_hi)) - CV;
+        o1 += group_sum<4>(chunk_dot_hl(v1, hq, lq, m_lo, m_hi)) - CV;
+        __syncthreads();                 // xh/xl and red are rewritten by the next block
+    }
+
+    // ---- residual tokens (fp16), last split only.
+    if (last && nres > 0) {
+        const uint16_t* kr = P.kr + (int64_t)h * kG * kD;
+        const uint16_t* vr = P.vr + (int64_t)h * kG * kD;
+        float s = -__builtin_huge_valf();
+        if (tid < nres) {
+            s = 0.0f;
+            const uint4* row = reinterpret_cast<const uint4*>(kr + (int64_t)tid * kD);
+#pragma unroll 4
+            for (int c = 0; c < kD / 8; ++c) {
+                const uint4 u = row[c];
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s = __builtin_fmaf(half_bits_to_float((uint16_t)(w[i] & 0xFFFFu)), qf[8 * c + 2 * i], s);
+                    s = __builtin_fmaf(half_bits_to_float((uint16_t)(w[i] >> 16)), qf[8 * c + 2 * i + 1], s);
+                }
+            }
+        }
+        const float bm = block_max256(s, red);
+        const float Mn = __builtin_fmaxf(M, bm);
+        const float alpha = exp2_fast(M - Mn);
+        M = Mn;
+        const float p = tid < nres ? exp2_fast(s - Mn) : 0.0f;
+        if (tid < kG) pr[tid] = p;
+        lsum = lsum * alpha + p;          // residual weights counted by their own thread
+        o0 *= alpha;
+        o1 *= alpha;
+        __syncthreads();
+        if (qk == 0) {
+            float a0 = 0.0f, a1 = 0.0f;
+            for (int t = 0; t < nres; ++t) {
+                a0 = __builtin_fmaf(pr[t], half_bits_to_float(vr[(int64_t)t * kD + r0]), a0);
+                a1 = __builtin_fmaf(pr[t], half_bits_to_float(vr[(int64_t)t * kD + r1]), a1);
+            }
+            o0 += a0;
+            o1 += a1;
+        }
+        // (the other lanes of the quad keep stale o0/o1; only qk == 0 stores)
+    }
+
+    // Total of the per-thread sums of p.
+    float lt = group_sum<64>(lsum);
+    if ((tid & 63) == 0) red[tid >> 6] = lt;
+    __syncthreads();
+    lt = red[0] + red[1] + red[2] + red[3];
+
+    if (splits == 1) {
+        if (qk == 0) {
+            const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+            out[(int64_t)h * kD + r0] = float_to_half_bits_rne(o0 * inv);
+            out[(int64_t)h * kD + r1] = float_to_half_bits_rne(o1 * inv);
+        }
+        return;
+    }
+    float* pp = part + ((int64_t)h * splits + sp) * (kD + 4);
+    if (tid == 0) {
+        pp[0] = M;
+        pp[1] = lt;
+    }
+    if (qk == 0) {
+        pp[4 + r0] = o0;
+        pp[4 + r1] = o1;
+    }
+}
+
+// out[h, d] = sum_s 2^(M_s - M) o_s[d] / sum_s 2^(M_s - M) l_s.
+__global__ __launch_bounds__(128) void kv_combine_kernel(const float* __restrict__ part, int splits,
+                                                         uint16_t* __restrict__ out) {
+    const int h = blockIdx.x;
+    const int d = threadIdx.x;
+    const float* pp = part + (int64_t)h * splits * (kD + 4);
+    float M = -__builtin_huge_valf();
+    for (int s = 0; s < splits; ++s) M = __builtin_fmaxf(M, pp[s * (kD + 4)]);
+    float num = 0.0f, den = 0.0f;
+    if (M > -__builtin_huge_valf()) {
+        for (int s = 0; s < splits; ++s) {
+            const float f = exp2_fast(pp[s * (kD + 4)] - M);
+            num = __builtin_fmaf(f, pp[s * (kD + 4) + 4 + d], num);
+            den = __builtin_fmaf(f, pp[s * (kD + 4) + 1], den);
+        }
+    }
+    out[(int64_t)h * kD + d] = float_to_half_bits_rne(den > 0.0f ? num / den : 0.0f);
+}
+
+// ---- quantize-on-append ------------------------------------------------------
+// One workgroup per head: the head's block of G tokens of K and V (fp16,
+// token-major [G][D]) becomes block `block` of its cache.  K: min/max per
+// channel over the G tokens; V: per token over the D channels; both with the
+// exact decisions of the weight quantizer.
+__device__ __forceinline__ uint32_t encode_one(float x, float s, float rcp, float Z) {
+    const float k = rne_div_exact(x, s, rcp, -Z - 2.0f, 17.0f - Z);
+    const float q = __builtin_amdgcn_fmed3f(k + Z, 0.0f, 15.0f);
+    return (uint32_t)q;
+}
+
+__global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ V,
+                                                          uint8_t* __restrict__ kc, uint16_t* __restrict__ ks,
+                                                          uint16_t* __restrict__ kz, uint8_t* __restrict__ vc,
+                                                          uint16_t* __restrict__ vs, uint16_t* __restrict__ vz,
+                                                          int64_t max_blocks, int64_t block) {
+    constexpr int PAD = kD + 2;                  // row stride in halves (4-byte aligned, breaks bank aliasing)
+    __shared__ uint16_t tile[kG * PAD];
+    __shared__ float hs[kD], hr[kD], hzf[kD];
+    __shared__ float mnx[2][2][kD];
+
+    const int h = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t blk = (int64_t)h * max_blocks + block;
+
+    auto load_tile = [&](const uint16_t* src) {
+        for (int i = tid; i < kG * (kD / 8); i += 256) {
+            const int t = i / (kD / 8), c = i % (kD / 8);
+            const uint4 u = reinterpret_cast<const uint4*>(src + (int64_t)t * kD)[c];
+            uint32_t* dst = reinterpret_cast<uint32_t*>(tile + t * PAD + 8 * c);
+            dst[0] = u.x;
+            dst[1] = u.y;
+            dst[2] = u.z;
+            dst[3] = u.w;
+        }
+    };
+    auto at = [&](int t, int d) { return half_bits_to_float(tile[t * PAD + d]); };
+
+    // ---- K: one group per channel.
+    load_tile(K + (int64_t)h * kG * kD);
+    __syncthreads();
+    {
+        const int d = tid & (kD - 1), half = tid >> 7;
+        float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+        for (int t = half * 64; t < half * 64 + 64; ++t) {
+            const float x = at(t, d);
+            mn = __builtin_fminf(mn, x);
+            mx = __builtin_fmaxf(mx, x);
+        }
+        mnx[half][0][d] = mn;
+        mnx[half][1][d] = mx;
+    }
+    __syncthreads();
+    if (tid < kD) {
+        const GroupHeader g = make_header(__builtin_fminf(mnx[0][0][tid], mnx[1][0][tid]),
+                                          __builtin_fmaxf(mnx[0][1][tid], mnx[1][1][tid]), 15);
+        hs[tid] = g.s;
+        hr[tid] = g.rcp;
+        hzf[tid] = g.Z;
+        ks[blk * kD + tid] = g.sbits;
+        kz[blk * kD + tid] = g.zbits;
+    }
+    __syncthreads();
+    {
+        // Token t = tid / 2, channels [64 * (tid & 1), +64) -> 32 bytes of its row.
+        const int t = tid >> 1, c0 = (tid & 1) * 64;
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                const int d = c0 + 8 * i + n;
+                v |= encode_one(at(t, d), hs[d], hr[d], hzf[d]) << (4 * n);
+            }
+            w[i] = v;
+        }
+        uint4* dst = reinterpret_cast<uint4*>(kc + (blk * kG + t) * kRow + c0 / 2);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+    __syncthreads();
+
+    // ---- V: one group per token.
+    load_tile(V + (int64_t)h * kG * kD);
+    __syncthreads();
+    {
+        const int t = tid >> 1, c0 = (tid & 1) * 64;
+        float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+        for (int d = c0; d < c0 + 64; ++d) {
+            const float x = at(t, d);
+            mn = __builtin_fminf(mn, x);
+            mx = __builtin_fmaxf(mx, x);
+        }
+        mn = __builtin_fminf(mn, __shfl_xor(mn, 1, 64));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1, 64));
+        if ((tid & 1) == 0) {
+            const GroupHeader g = make_header(mn, mx, 15);
+            hs[t] = g.s;
+            hr[t] = g.rcp;
+            hzf[t] = g.Z;
+            vs[blk * kG + t] = g.sbits;
+            vz[blk * kG + t] = g.zbits;
+        }
+    }
+    __syncthreads();
+    {
+        // Channel d = tid / 2, tokens [64 * (tid & 1), +64) -> 32 bytes of its row.
+        const int d = tid >> 1, t0 = (tid & 1) * 64;
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                const int t = t0 + 8 * i + n;
+                v |= encode_one(at(t, d), hs[t], hr[t], hzf[t]) << (4 * n);
+            }
+            w[i] = v;
+        }
+        uint4* dst = reinterpret_cast<uint4*>(vc + (blk * kD + d) * kRow + t0 / 2);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+}
+
+}  // namespace
+
+int kv_splits(int64_t heads, int64_t max_blocks, int num_cus) {
+    // Enough (head, split) workgroups for about eight per compute unit.
+    const int64_t want = ((int64_t)8 * num_cus + heads - 1) / (heads > 0 ? heads : 1);
+    int64_t s = want < 1 ? 1 : want;
+    if (s > max_blocks) s = max_blocks;
+    if (s > 64) s = 64;
+    return (int)(s < 1 ? 1 : s);
+}
+
+hipError_t launch_kv_attention(const void* q, const KvCacheArgs& c, const int32_t* lens, void* out,
+                               int num_cus, hipStream_t stream) {
+    const int splits = kv_splits(c.heads, c.max_blocks, num_cus);
+    float* part = nullptr;
+    if (splits > 1) {
+        uint32_t* unused = nullptr;
+        const hipError_t e = workspace_get(stream, 0, (size_t)c.heads * splits * (kD + 4) * sizeof(float),
+                                           &unused, &part);
+        if (e != hipSuccess) return e;
+    }
+    const KvPtrs P{static_cast<const uint8_t*>(c.kcodes), static_cast<const uint16_t*>(c.kscales),
+                   static_cast<const uint16_t*>(c.kzeros), static_cast<const uint8_t*>(c.vcodes),
+                   static_cast<const uint16_t*>(c.vscales), static_cast<const uint16_t*>(c.vzeros),
+                   static_cast<const uint16_t*>(c.kres), static_cast<const uint16_t*>(c.vres), c.max_blocks};
+    // log2(e) / sqrt(D): scores in log2 units for v_exp_f32.
+    const float q_scale = 1.4426950408889634f / 11.313708498984761f;
+    kv_attn_kernel<<<dim3((unsigned)c.heads, (unsigned)splits), dim3(256), 0, stream>>>(
+        static_cast<const uint16_t*>(q), P, lens, splits, q_scale, part, static_cast<uint16_t*>(out));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    kv_combine_kernel<<<dim3((unsigned)c.heads), dim3(kD), 0, stream>>>(part, splits, static_cast<uint16_t*>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_quantize(const void* K, const void* V, const KvCacheArgs& c, int64_t block,
+                              hipStream_t stream) {
+    kv_quantize_kernel<<<dim3((unsigned)c.heads), dim3(256), 0, stream>>>(
+        static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), static_cast<uint8_t*>(c.kcodes),
+        static_cast<uint16_t*>(c.kscales), static_cast<uint16_t*>(c.kzeros), static_cast<uint8_t*>(c.vcodes),
+        static_cast<uint16_t*>(c.vscales), static_cast<uint16_t*>(c.vzeros), c.max_blocks, block);
+    return hipGetLastError();
+}
+
+}  // namespace wq

@@ -54,6 +54,25 @@ hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales
                             const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                             int32_t group, int32_t bits, int num_cus, hipStream_t stream);
 
+// int4 KV cache of `heads` heads (head dimension 128, blocks of 128 tokens,
+// `max_blocks` blocks per head); layouts in wq_kv.hip.
+struct KvCacheArgs {
+    void* kcodes;
+    void* kscales;
+    void* kzeros;
+    void* vcodes;
+    void* vscales;
+    void* vzeros;
+    void* kres;
+    void* vres;
+    int64_t heads, max_blocks;
+};
+int kv_splits(int64_t heads, int64_t max_blocks, int num_cus);
+hipError_t launch_kv_attention(const void* q, const KvCacheArgs& c, const int32_t* lens, void* out,
+                               int num_cus, hipStream_t stream);
+hipError_t launch_kv_quantize(const void* K, const void* V, const KvCacheArgs& c, int64_t block,
+                              hipStream_t stream);
+
 // Split-K workspace of the calling device and `stream`: counter_words zeroed
 // 32-bit counters (a kernel that uses them leaves them at zero) and part_bytes
 // of fp32 partials, reused by later calls on the same stream.

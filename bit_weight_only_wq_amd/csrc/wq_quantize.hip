@@ -49,29 +49,6 @@ __device__ __forceinline__ void minmax8(const uint4& raw, float& mn, float& mx) 
     mx = __builtin_fmaxf((float)hi.x, (float)hi.y);
 }
 
-// Per-group header from the exact min and max.
-struct GroupHeader {
-    float s, rcp, Z, thr;
-    uint16_t sbits, zbits;
-};
-
-__device__ __forceinline__ GroupHeader make_header(float mn, float mx, int M) {
-    GroupHeader h;
-    h.sbits = scale_bits_exact(mn, mx, M);
-    h.s = half_bits_to_float(h.sbits);
-    h.rcp = __builtin_amdgcn_rcpf(h.s);
-    // z = round(-min / s): estimates beyond +-2^17 all saturate the fp16 zero.
-    float k = rne_div_exact(-mn, h.s, h.rcp, -131072.0f, 131072.0f);
-    h.zbits = zero_bits_from_int(k);
-    h.Z = half_bits_to_float(h.zbits);
-    // |x*rcp - x/s| <= |x/s| * 2^-22 (rcp within 1 ulp, one rounding of the
-    // product).  A fraction |t - rint(t)| at most thr therefore cannot be a tie
-    // or on the wrong side of one; thr keeps a 4x margin on that bound.
-    const float tmax = __builtin_fmaxf(__builtin_fabsf(mn), __builtin_fabsf(mx)) * h.rcp;
-    h.thr = 0.5f - (tmax + 1.0f) * 0x1p-20f;
-    return h;
-}
-
 // Symmetric header from the scope's absolute maximum A: s = A / qmax rounded
 // once to fp16 (1.0 when that is 0), zero point 2^(b-1) (exact in fp16).
 __device__ __forceinline__ GroupHeader make_header_sym(float A, int bits) {

@@ -199,6 +199,68 @@ size_t wq_codes_bytes(int64_t N, int64_t K, int32_t bits);
  * (-1 on invalid input). */
 int64_t wq_num_groups(int64_t N, int64_t K, int32_t group);
 
+/*
+ * int4 KV cache for decode attention ("What actually happens when you
+ * quantize a KV cache": §2 the decode step, §3-§4 the codec, §5 the byte
+ * count, §7 "axis choice").  Head dimension 128; tokens are cached in blocks
+ * of 128.  Per head, for each block:
+ *   kcodes   u8   [heads][max_blocks][128 tokens][64]   K codes, token-major:
+ *                 byte i of a token row holds channels 2i (low nibble), 2i+1
+ *   kscales, kzeros fp16 [heads][max_blocks][128]       per channel of a block
+ *                 (one K group = one channel over the block's 128 tokens)
+ *   vcodes   u8   [heads][max_blocks][128 channels][64] V codes, channel-major:
+ *                 byte i of a channel row holds tokens 2i (low nibble), 2i+1
+ *   vscales, vzeros fp16 [heads][max_blocks * 128]      per token (one V group
+ *                 = one token's 128 values)
+ *   kres, vres fp16 [heads][128][128]                    the newest tokens that
+ *                 do not fill a block, token-major, in fp16
+ * A head holding L tokens has its first L / 128 blocks quantized and the
+ * remaining L % 128 tokens in rows 0.. of kres/vres.  The codec is the one of
+ * wq_quantize_pack (asymmetric, 4 bits, round half to even, fp16 headers).
+ * 136 bytes per token per head (the page's 136 KiB per token over 32 layers of
+ * 32 heads).  The caller allocates and owns every buffer; code buffers and
+ * kres/vres 16-byte aligned, header arrays 2-byte aligned.
+ */
+typedef struct wq_kv_cache {
+    void* kcodes;
+    void* kscales;
+    void* kzeros;
+    void* vcodes;
+    void* vscales;
+    void* vzeros;
+    void* kres;
+    void* vres;
+    int64_t heads;
+    int64_t max_blocks;
+} wq_kv_cache;
+
+/*
+ * Quantize-on-append ("cheap enough to run inline as tokens are generated",
+ * §4): K and V, fp16 [heads][128 tokens][128] token-major (16-byte aligned),
+ * become block `block` (0 <= block < max_blocks) of every head's cache.  K is
+ * grouped per channel over the 128 tokens, V per token; codes and headers are
+ * bit-identical to the oracle's.  Typically called when a head's residual
+ * window fills, with K = kres and V = vres.  heads == 0 is a no-op.
+ */
+wq_status wq_kv_quantize_block(const void* K, const void* V, const wq_kv_cache* cache,
+                               int64_t block, void* stream);
+
+/*
+ * Decode attention of one new token per head:
+ *     out[h] = softmax(K_h q_h / sqrt(128)) V_h
+ * over the cached tokens of head h: its quantized blocks (dequantized as
+ * (q - z) * s in registers) followed by its residual fp16 tokens.
+ * q, out  fp16 [heads][128] (q 2-byte aligned, out 2-byte aligned)
+ * lens    int32 [heads], DEVICE memory: tokens held by each head; values are
+ *         clamped to [0, max_blocks * 128 + 127] (a head with 0 tokens gives 0)
+ * fp32 scores, softmax and accumulation; the context is split over several
+ * workgroups per head when there are few heads (the partials use the
+ * stream's workspace).  Tolerance against the float64 oracle: the product
+ * tolerance (max|d| <= 1e-2 max|ref|, rel L2 <= 1e-3).
+ */
+wq_status wq_kv_attention(const void* q, const wq_kv_cache* cache, const int32_t* lens,
+                          void* out, void* stream);
+
 /* Static description of a status code. */
 const char* wq_status_string(wq_status s);
 
@@ -208,7 +270,7 @@ const char* wq_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int32_t wq_version(void);
 
-#define WQ_VERSION 102
+#define WQ_VERSION 103
 
 #ifdef __cplusplus
 }

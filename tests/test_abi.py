@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = wq.load()
-    assert lib.wq_version() == 102
+    assert lib.wq_version() == 103
     for st in range(5):
         assert lib.wq_status_string(st)
     assert lib.wq_status_string(99) == b"unknown status"
@@ -144,3 +144,34 @@ def test_grouped_validates_every_item_first():
     # No-op items (B == 0 or N == 0) are valid and enqueue nothing.
     arr = (_lib.GemmItem * 2)(_item(B=0), _item(N=0))
     assert lib.wq_gemm_grouped(arr, 2, None) == _lib.WQ_OK
+
+
+def _cache(heads=4, max_blocks=2, **kw):
+    f = dict(kcodes=FAKE, kscales=FAKE, kzeros=FAKE, vcodes=FAKE, vscales=FAKE, vzeros=FAKE,
+             kres=FAKE, vres=FAKE)
+    f.update(kw)
+    return _lib.KvCache(f["kcodes"], f["kscales"], f["kzeros"], f["vcodes"], f["vscales"],
+                        f["vzeros"], f["kres"], f["vres"], heads, max_blocks)
+
+
+def test_kv_validation_errors():
+    import ctypes
+    lib = wq.load()
+    q = lib.wq_kv_quantize_block
+    a = lib.wq_kv_attention
+    assert q(FAKE, FAKE, None, 0, None) == _lib.WQ_ERR_INVALID_ARG
+    assert a(FAKE, None, FAKE, FAKE, None) == _lib.WQ_ERR_INVALID_ARG
+    assert q(FAKE, FAKE, ctypes.byref(_cache(max_blocks=0)), 0, None) == _lib.WQ_ERR_INVALID_ARG
+    assert q(FAKE, FAKE, ctypes.byref(_cache(heads=-1)), 0, None) == _lib.WQ_ERR_INVALID_ARG
+    assert q(FAKE, FAKE, ctypes.byref(_cache()), 2, None) == _lib.WQ_ERR_INVALID_ARG
+    assert q(FAKE, FAKE, ctypes.byref(_cache()), -1, None) == _lib.WQ_ERR_INVALID_ARG
+    assert q(0, FAKE, ctypes.byref(_cache()), 0, None) == _lib.WQ_ERR_INVALID_ARG
+    assert q(FAKE + 8, FAKE, ctypes.byref(_cache()), 0, None) == _lib.WQ_ERR_MISALIGNED
+    assert q(FAKE, FAKE, ctypes.byref(_cache(vcodes=0)), 0, None) == _lib.WQ_ERR_INVALID_ARG
+    assert q(FAKE, FAKE, ctypes.byref(_cache(kres=FAKE + 2)), 0, None) == _lib.WQ_ERR_MISALIGNED
+    assert a(FAKE, ctypes.byref(_cache()), 0, FAKE, None) == _lib.WQ_ERR_INVALID_ARG
+    assert a(FAKE, ctypes.byref(_cache()), FAKE + 2, FAKE, None) == _lib.WQ_ERR_MISALIGNED
+    assert a(FAKE + 1, ctypes.byref(_cache()), FAKE, FAKE, None) == _lib.WQ_ERR_MISALIGNED
+    # No heads: nothing to do.
+    assert q(0, 0, ctypes.byref(_cache(heads=0, kcodes=0)), 0, None) == _lib.WQ_OK
+    assert a(0, ctypes.byref(_cache(heads=0)), 0, 0, None) == _lib.WQ_OK
