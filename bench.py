@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="batch sweep on K=N=8192 (table)")
     p.add_argument("--decode-set", action="store_true",
                    help="7B-class decode step, 224 products at B=32 (table)")
+    p.add_argument("--kv", action="store_true",
+                   help="decode attention over an int4 KV cache, 1024 heads x 4096 tokens "
+                        "(a 7B-class model's whole cache; table line)")
     p.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
     p.add_argument("--bits", type=int, default=0,
                    help="code width of the step (default: the workload's, 4); 2 and 3 take "
@@ -91,7 +94,11 @@ KERNEL_SOURCES = {
     "mfma": ["wq_gemm_mfma.hip", "wq_device.h"],
     "xr": ["wq_gemm_xr.hip", "wq_device.h"],
     "quantize": ["wq_quantize.hip", "wq_device.h"],
+    "kv_attn": ["wq_kv.hip", "wq_device.h"],
+    "kv_quantize": ["wq_kv.hip", "wq_device.h"],
 }
+KV_WORKLOAD = "kv_decode_7b_ctx4096"
+KV_SHAPE = (1024, 4096, 128, 128)   # heads (32 layers x 32), tokens, head dim, block
 # rocprofv3 kernel-name fragment of each family.
 KERNEL_NAMES = {"gemv": "gemv_", "mfma": "gemm_mfma_kernel", "xr": "gemm_xr_kernel",
                 "quantize": "quantize_"}
@@ -167,12 +174,43 @@ def traffic_from(fetch_csv, write_csv, copy_mib):
     return out, fr, wr
 
 
+def write_summary(args, tag, workload, fam, name, f, w, fr, wr, algo):
+    path = traffic_path(f"{tag}_{workload}")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic per launch of {tag} on {workload}\n")
+        fh.write(f"# kernel: {name}\n")
+        fh.write(f"# fetch: {args.fetch_cmd}\n# write: {args.write_cmd}\n")
+        fh.write("# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over launches) "
+                 "scaled by known/counted bytes of a torch elementwise multiply "
+                 f"over {args.copy_calibration_mib} MiB\n")
+        fh.write(f"fetch_scale: {fr:.6f}\nwrite_scale: {wr:.6f}\n")
+        fh.write(f"fetch_bytes_per_launch: {f:.0f}\nwrite_bytes_per_launch: {w:.0f}\n")
+        fh.write(f"hbm_bytes_per_launch: {f + w:.0f}\n")
+        fh.write(f"algorithmic_bytes_per_launch: {algo}\n")
+        fh.write(f"traffic_over_algorithmic: {(f + w) / algo:.4f}\n")
+        fh.write(f"sources: {' '.join(KERNEL_SOURCES[fam])}\n")
+        fh.write(f"sources_sha256: {sources_sha256(KERNEL_SOURCES[fam])}\n")
+    print("wrote", os.path.relpath(path, ROOT))
+
+
 def write_traffic_summaries(args):
     """Print every wq kernel's calibrated traffic and write one summary file
     per kernel family and grid size under profiles/."""
     import bit_weight_only_wq_amd.roofline as rl
     import wq_inputs
     out, fr, wr = traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_calibration_mib)
+    if args.kv:
+        H, T, D, G = KV_SHAPE
+        for (name, grid), (f, w) in sorted(out.items()):
+            print(f"{name[:100]} grid={grid}: fetch {f / 1e6:.2f} MB, write {w / 1e6:.2f} MB")
+            if "kv_attn_kernel" in name:
+                write_summary(args, "wq_kv_attention", KV_WORKLOAD, "kv_attn", name, f, w, fr, wr,
+                              rl.kv_attention_bytes(H, T, D))
+            elif "kv_quantize_kernel" in name:
+                write_summary(args, "wq_kv_quantize_block", KV_WORKLOAD, "kv_quantize", name, f, w, fr, wr,
+                              rl.kv_append_bytes(H, G, D))
+        return
     cfg = wq_inputs.WORKLOADS[args.workload]
     N, K, G, bits = cfg["N"], cfg["K"], cfg["group"], cfg["bits"]
     batches = [b for b in cfg["batches"] if b <= 64] or [1]
@@ -191,23 +229,7 @@ def write_traffic_summaries(args):
                 if not args.traffic_match or not any(m in name and tag.endswith(t)
                                                      for t, m in args.traffic_match):
                     continue
-                path = traffic_path(f"{tag}_{args.workload}")
-                os.makedirs(os.path.dirname(path), exist_ok=True)
-                with open(path, "w") as fh:
-                    fh.write(f"# HBM traffic per launch of {tag} on {args.workload}\n")
-                    fh.write(f"# kernel: {name}\n")
-                    fh.write(f"# fetch: {args.fetch_cmd}\n# write: {args.write_cmd}\n")
-                    fh.write("# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over launches) "
-                             "scaled by known/counted bytes of a torch elementwise multiply "
-                             f"over {args.copy_calibration_mib} MiB\n")
-                    fh.write(f"fetch_scale: {fr:.6f}\nwrite_scale: {wr:.6f}\n")
-                    fh.write(f"fetch_bytes_per_launch: {f:.0f}\nwrite_bytes_per_launch: {w:.0f}\n")
-                    fh.write(f"hbm_bytes_per_launch: {f + w:.0f}\n")
-                    fh.write(f"algorithmic_bytes_per_launch: {algo}\n")
-                    fh.write(f"traffic_over_algorithmic: {(f + w) / algo:.4f}\n")
-                    fh.write(f"sources: {' '.join(KERNEL_SOURCES[fam])}\n")
-                    fh.write(f"sources_sha256: {sources_sha256(KERNEL_SOURCES[fam])}\n")
-                print("wrote", os.path.relpath(path, ROOT))
+                write_summary(args, tag, args.workload, fam, name, f, w, fr, wr, algo)
 
 
 def cpu_baseline(name, batches, bits=0):
@@ -532,6 +554,76 @@ def run_decode_set(args):
     return out
 
 
+def run_kv(args):
+    """Decode attention over the int4 KV cache of a 7B-class model (32 layers x
+    32 heads of dimension 128) at 4096 tokens: every head's cache read once
+    per step.  Two caches alternate (1.1 GB, beyond the 256 MB Infinity
+    Cache); inputs are drawn on the GPU, K with one hot channel."""
+    import torch
+
+    import bit_weight_only_wq_amd as wq
+    from bit_weight_only_wq_amd import roofline as rl
+
+    H, T, D, G = KV_SHAPE
+    nb = T // G
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    caches = []
+    for _ in range(2):
+        cache = wq.KVCache(H, nb)
+        for j in range(nb):
+            Kb = torch.randn((H, G, D), generator=gen, device="cuda")
+            Kb[:, :, 3] *= 8.0
+            wq.kv_quantize_block(Kb.half(), torch.randn((H, G, D), generator=gen, device="cuda").half(),
+                                 cache, j)
+        caches.append(cache)
+    q = torch.randn((H, D), generator=gen, device="cuda").half()
+    lens = torch.full((H,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty((H, D), dtype=torch.float16, device="cuda")
+    Kb = torch.randn((H, G, D), generator=gen, device="cuda").half()
+    Vb = torch.randn((H, G, D), generator=gen, device="cuda").half()
+    stream = torch.cuda.current_stream()
+
+    def burst(fn, reps):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_attn = burst(lambda i: wq.kv_attention(q, caches[i % 2], lens, out=out), args.steps)
+    ms_app = burst(lambda i: wq.kv_quantize_block(Kb, Vb, caches[i % 2], i % nb), args.steps)
+    b_attn = rl.kv_attention_bytes(H, T, D)
+    b_app = rl.kv_append_bytes(H, G, D)
+    gbs = b_attn / (ms_attn * 1e-3) / 1e9
+    row = {
+        "metric": "decode attention over an int4 KV cache (GB/s of cache read)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "ms_per_step": round(ms_attn, 4), "higher_is_better": True, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": KV_WORKLOAD, "heads": H, "tokens": T, "head_dim": D,
+                   "group": G, "bits": 4},
+        "roofline": {"kernel": "kv_attn_kernel + kv_combine_kernel", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": rl.MI355X_HBM_BYTES_PER_S / 1e9,
+                     "unit": "GB/s", "frac": round(gbs * 1e9 / rl.MI355X_HBM_BYTES_PER_S, 4),
+                     "traffic": read_traffic(f"wq_kv_attention_{KV_WORKLOAD}"),
+                     "bytes_per_launch": int(b_attn), "avg_us": round(ms_attn * 1e3, 2)},
+        "kernels": {
+            "kv_attention": {"avg_us": round(ms_attn * 1e3, 2), "bytes": int(b_attn),
+                             "achieved_GBps": round(gbs, 1)},
+            "kv_quantize_block": {"avg_us": round(ms_app * 1e3, 2), "bytes": int(b_app),
+                                  "achieved_GBps": round(b_app / (ms_app * 1e-3) / 1e9, 1)},
+        },
+    }
+    print(json.dumps(row), flush=True)
+    return row
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -547,7 +639,18 @@ def main():
     if args.decode_set:
         run_decode_set(args)
         return
+    if args.kv:
+        run_kv(args)
+        calibration_copy(args)
+        return
     out, batches = run_step_bench(args)
+    calibration_copy(args)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(args.workload, batches, args.bits)
+    print(json.dumps(out), flush=True)
+
+
+def calibration_copy(args):
     if args.copy_calibration_mib:
         import torch
         # An elementwise kernel (not a DMA copy, which the counters do not see)
@@ -558,9 +661,6 @@ def main():
         torch.cuda.synchronize()
         torch.mul(a, 3, out=b)
         torch.cuda.synchronize()
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args.workload, batches, args.bits)
-    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

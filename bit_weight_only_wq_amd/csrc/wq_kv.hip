@@ -159,34 +159,51 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
     float lsum = 0.0f;                   // this thread's share of sum p (lane qk == 0 rows)
     float o0 = 0.0f, o1 = 0.0f;          // output channels r0, r1 (all four lanes of the quad)
 
+    // One block's loads for this thread: its four 16-byte code chunks and the
+    // headers it applies (a channel's K header for threads 0..127, its two
+    // tokens' V headers for lane 0 of each quad).  The next block's loads are
+    // issued before the current block is computed.
+    struct Blk {
+        uint4 k0, k1, v0, v1;
+        uint32_t ks, kz, vs0, vs1, vz0, vz1;
+    };
     const int64_t hb = (int64_t)h * P.max_blocks;
-    for (int j = j0; j < j1; ++j) {
+    auto load_blk = [&](int j, Blk& b) {
         const int64_t blk = hb + j;
-        // Codes of this block for this thread (K rows = tokens, V rows = channels).
         const uint4* kc = reinterpret_cast<const uint4*>(P.kc + blk * (kG * kRow));
         const uint4* vc = reinterpret_cast<const uint4*>(P.vc + blk * (kD * kRow));
-        const uint4 k0 = load_stream(kc + r0 * 4 + qk);
-        const uint4 k1 = load_stream(kc + r1 * 4 + qk);
-        const uint4 v0 = load_stream(vc + r0 * 4 + qk);
-        const uint4 v1 = load_stream(vc + r1 * 4 + qk);
-
+        b.k0 = load_stream(kc + r0 * 4 + qk);
+        b.k1 = load_stream(kc + r1 * 4 + qk);
+        b.v0 = load_stream(vc + r0 * 4 + qk);
+        b.v1 = load_stream(vc + r1 * 4 + qk);
+        if (tid < kD) {
+            b.ks = P.ks[blk * kD + tid];
+            b.kz = P.kz[blk * kD + tid];
+        }
+        if (qk == 0) {
+            const int64_t tb = blk * kG;
+            b.vs0 = P.vs[tb + r0];
+            b.vs1 = P.vs[tb + r1];
+            b.vz0 = P.vz[tb + r0];
+            b.vz1 = P.vz[tb + r1];
+        }
+    };
+    auto process = [&](const Blk& b) {
         // ---- K side: a_d = q_d s_d as hi/lo, and C_K = sum_d a_d (off_d + z_d).
         float ck = 0.0f;
         if (tid < kD) {
-            const float s = half_bits_to_float(P.ks[blk * kD + tid]);
-            const float z = half_bits_to_float(P.kz[blk * kD + tid]);
-            const float a = qf[tid] * s;
+            const float a = qf[tid] * half_bits_to_float((uint16_t)b.ks);
             const _Float16 ah = (_Float16)a;
             const _Float16 al = (_Float16)(a - (float)ah);
             xh[pair_slot(tid)] = __builtin_bit_cast(uint16_t, ah);
             xl[pair_slot(tid)] = __builtin_bit_cast(uint16_t, al);
-            ck = ((float)ah + (float)al) * (unpack_offset(tid) + z);
+            ck = ((float)ah + (float)al) * (unpack_offset(tid) + half_bits_to_float((uint16_t)b.kz));
         }
         const float CK = block_sum128(ck, red);     // (its barrier also publishes xh/xl)
         const uint4* hq = reinterpret_cast<const uint4*>(xh) + qk * 4;
         const uint4* lq = reinterpret_cast<const uint4*>(xl) + qk * 4;
-        float s0 = group_sum<4>(chunk_dot_hl(k0, hq, lq, m_lo, m_hi)) - CK;
-        float s1 = group_sum<4>(chunk_dot_hl(k1, hq, lq, m_lo, m_hi)) - CK;
+        const float s0 = group_sum<4>(chunk_dot_hl(b.k0, hq, lq, m_lo, m_hi)) - CK;
+        const float s1 = group_sum<4>(chunk_dot_hl(b.k1, hq, lq, m_lo, m_hi)) - CK;
 
         // ---- softmax update over the block's 128 scores.
         const float bm = block_max256(__builtin_fmaxf(s0, s1), red);
@@ -198,30 +215,39 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
         o0 *= alpha;
         o1 *= alpha;
 
-        // ---- V side: w_t = p_t s_t as hi/lo, C_V = sum_t w_t (off_t + z_t).
+        // ---- V side: w_t = p_t s_t as hi/lo, C_V = sum_t w_t (off_t + z_t),
+        // written by lane 0 of each quad for its two tokens.
         float cv = 0.0f;
         if (qk == 0) {
-            const int64_t tb = (int64_t)blk * kG;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int t = e ? r1 : r0;
-                const float w = (e ? p1 : p0) * half_bits_to_float(P.vs[tb + t]);
+                const float w = (e ? p1 : p0) * half_bits_to_float((uint16_t)(e ? b.vs1 : b.vs0));
                 const _Float16 wh = (_Float16)w;
                 const _Float16 wl = (_Float16)(w - (float)wh);
                 xh[pair_slot(t)] = __builtin_bit_cast(uint16_t, wh);
                 xl[pair_slot(t)] = __builtin_bit_cast(uint16_t, wl);
-                cv += ((float)wh + (float)wl) * (unpack_offset(t) + half_bits_to_float(P.vz[tb + t]));
+                cv += ((float)wh + (float)wl) *
+                      (unpack_offset(t) + half_bits_to_float((uint16_t)(e ? b.vz1 : b.vz0)));
             }
         }
-        // Threads 0..127 hold the sum's inputs only partly (qk == 0 lanes of
-        // all 64 quads): fold the other 128 threads in through LDS as well.
         cv = group_sum<64>(cv);
         if ((tid & 63) == 0) red[tid >> 6] = cv;
         __syncthreads();
         const float CV = red[0] + red[1] + red[2] + red[3];
-        o0 += group_sum<4>(chunk_dot_hl(v0, hq, lq, m_lo, m_hi)) - CV;
-        o1 += group_sum<4>(chunk_dot_hl(v1, hq, lq, m_lo, m_hi)) - CV;
+        o0 += group_sum<4>(chunk_dot_hl(b.v0, hq, lq, m_lo, m_hi)) - CV;
+        o1 += group_sum<4>(chunk_dot_hl(b.v1, hq, lq, m_lo, m_hi)) - CV;
         __syncthreads();                 // xh/xl and red are rewritten by the next block
+    };
+
+    Blk A = {}, B = {};
+    if (j0 < j1) load_blk(j0, A);
+    for (int j = j0; j < j1; j += 2) {
+        if (j + 1 < j1) load_blk(j + 1, B);
+        process(A);
+        if (j + 1 >= j1) break;
+        if (j + 2 < j1) load_blk(j + 2, A);
+        process(B);
     }
 
     // ---- residual tokens (fp16), last split only.
@@ -439,10 +465,14 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
 }  // namespace
 
 int kv_splits(int64_t heads, int64_t max_blocks, int num_cus) {
-    // Enough (head, split) workgroups for about eight per compute unit.
-    const int64_t want = ((int64_t)8 * num_cus + heads - 1) / (heads > 0 ? heads : 1);
-    int64_t s = want < 1 ? 1 : want;
-    if (s > max_blocks) s = max_blocks;
+    // About six (head, split) workgroups per compute unit, but at least eight
+    // blocks per split (each split pays for its query set-up, its prefetch
+    // ramp and a partial in the combine), and at most 64 splits.  Measured on
+    // 1024 heads x 4096 tokens (2 splits), 256 x 4096 (4) and 32 x 32768 (32).
+    const int64_t h = heads > 0 ? heads : 1;
+    int64_t s = ((int64_t)6 * num_cus + h - 1) / h;
+    const int64_t by_len = max_blocks / 8 > 1 ? max_blocks / 8 : 1;
+    if (s > by_len) s = by_len;
     if (s > 64) s = 64;
     return (int)(s < 1 ? 1 : s);
 }

@@ -83,3 +83,26 @@ def roofline_time_s(bytes_moved: float, flops: float,
                     peak_flops: float = MI355X_FP16_MFMA_FLOPS) -> float:
     """Lower bound on a kernel's time: max(bytes/BW, flops/peak)."""
     return max(bytes_moved / bandwidth, flops / peak_flops)
+
+
+def kv_cache_bytes(heads: int, tokens: int, head_dim: int = 128, group: int = 128, bits: int = 4) -> int:
+    """Quantized KV cache of `heads` heads holding `tokens` tokens each: K and V
+    codes plus one 4-byte header per group (K per channel per `group` tokens,
+    V per token) -- 136 B per token per head at 4 bits, D = G = 128, the
+    "What actually happens when you quantize a KV cache" §5 count."""
+    codes = 2 * heads * tokens * head_dim * bits // 8
+    k_hdr = HEADER_BYTES_PER_GROUP * heads * head_dim * (tokens // group)
+    v_hdr = HEADER_BYTES_PER_GROUP * heads * tokens
+    return codes + k_hdr + v_hdr
+
+
+def kv_attention_bytes(heads: int, tokens: int, head_dim: int = 128) -> int:
+    """Algorithmic bytes of one decode-attention step: the whole cache read
+    once, the fp16 query read and the fp16 output written."""
+    return kv_cache_bytes(heads, tokens, head_dim) + 2 * 2 * heads * head_dim
+
+
+def kv_append_bytes(heads: int, group: int = 128, head_dim: int = 128) -> int:
+    """Quantize-on-append of one block per head: fp16 K and V read, codes and
+    headers written."""
+    return 2 * 2 * heads * group * head_dim + kv_cache_bytes(heads, group, head_dim, group)
