@@ -89,23 +89,22 @@ __device__ __forceinline__ float chunk_dot_hl(const uint4& w4, const uint4* xh, 
     return __builtin_fmaf(pb, 0.0625f, pa);
 }
 
-// Sum of a value held by threads 0..127 (others pass 0), returned to all.
-__device__ __forceinline__ float block_sum128(float v, float* red) {
+// Block-wide sum / max over the four waves through `red` (one barrier).  The
+// caller keeps `red` untouched until every thread has read it: the kernels
+// below use a separate `red` per reduction of a block and reach another
+// barrier before a reduction reuses its array.
+__device__ __forceinline__ float block_sum(float v, float* red) {
     v = group_sum<64>(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    const float t = red[0] + red[1] + red[2] + red[3];
-    __syncthreads();
-    return t;
+    return red[0] + red[1] + red[2] + red[3];
 }
 
-__device__ __forceinline__ float block_max256(float v, float* red) {
+__device__ __forceinline__ float block_max(float v, float* red) {
     v = wave_max(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    const float t = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
-    __syncthreads();
-    return t;
+    return __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
 }
 
 struct KvPtrs {
@@ -127,11 +126,16 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
                                                       const int32_t* __restrict__ lens, int splits,
                                                       float q_scale, float* __restrict__ part,
                                                       uint16_t* __restrict__ out) {
-    __shared__ __align__(16) uint16_t xh[kD];       // hi halves in unpack order
-    __shared__ __align__(16) uint16_t xl[kD];       // lo halves
+    // Per-block vectors in unpack order, hi and lo halves: a (K side) and w
+    // (V side) in separate arrays, and one reduction array per block-wide
+    // reduction.  Barrier order then keeps every array's readers ahead of its
+    // next writers: a thread rewrites kh/kl only after all threads passed the
+    // previous block's softmax barrier (their last kh/kl reads came before
+    // it), and vh/vl only after all passed this block's C_K barrier.
+    __shared__ __align__(16) uint16_t kh[kD], kl[kD], vh[kG], vl[kG];
     __shared__ float qf[kD];
     __shared__ float pr[kG];                        // residual-token weights
-    __shared__ float red[4];
+    __shared__ float red_k[4], red_m[4], red_v[4], red_r[4];
 
     const int h = blockIdx.x;
     const int sp = blockIdx.y;
@@ -159,10 +163,11 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
     float lsum = 0.0f;                   // this thread's share of sum p (lane qk == 0 rows)
     float o0 = 0.0f, o1 = 0.0f;          // output channels r0, r1 (all four lanes of the quad)
 
-    // One block's loads for this thread: its four 16-byte code chunks and the
-    // headers it applies (a channel's K header for threads 0..127, its two
-    // tokens' V headers for lane 0 of each quad).  The next block's loads are
-    // issued before the current block is computed.
+    // One block's loads for this thread: its four 16-byte code chunks, the K
+    // header of channel tid % 128 and the V headers of its two tokens.  Every
+    // lane issues the same ten loads in the order they are consumed (lanes
+    // that do not use a header still load it), so the compiler can count the
+    // next block's loads in flight and wait only for the current block's.
     struct Blk {
         uint4 k0, k1, v0, v1;
         uint32_t ks, kz, vs0, vs1, vz0, vz1;
@@ -172,21 +177,17 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
         const int64_t blk = hb + j;
         const uint4* kc = reinterpret_cast<const uint4*>(P.kc + blk * (kG * kRow));
         const uint4* vc = reinterpret_cast<const uint4*>(P.vc + blk * (kD * kRow));
+        const int64_t tb = blk * kG;
         b.k0 = load_stream(kc + r0 * 4 + qk);
         b.k1 = load_stream(kc + r1 * 4 + qk);
+        b.ks = P.ks[blk * kD + (tid & (kD - 1))];
+        b.kz = P.kz[blk * kD + (tid & (kD - 1))];
         b.v0 = load_stream(vc + r0 * 4 + qk);
         b.v1 = load_stream(vc + r1 * 4 + qk);
-        if (tid < kD) {
-            b.ks = P.ks[blk * kD + tid];
-            b.kz = P.kz[blk * kD + tid];
-        }
-        if (qk == 0) {
-            const int64_t tb = blk * kG;
-            b.vs0 = P.vs[tb + r0];
-            b.vs1 = P.vs[tb + r1];
-            b.vz0 = P.vz[tb + r0];
-            b.vz1 = P.vz[tb + r1];
-        }
+        b.vs0 = P.vs[tb + r0];
+        b.vs1 = P.vs[tb + r1];
+        b.vz0 = P.vz[tb + r0];
+        b.vz1 = P.vz[tb + r1];
     };
     auto process = [&](const Blk& b) {
         // ---- K side: a_d = q_d s_d as hi/lo, and C_K = sum_d a_d (off_d + z_d).
@@ -195,18 +196,18 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
             const float a = qf[tid] * half_bits_to_float((uint16_t)b.ks);
             const _Float16 ah = (_Float16)a;
             const _Float16 al = (_Float16)(a - (float)ah);
-            xh[pair_slot(tid)] = __builtin_bit_cast(uint16_t, ah);
-            xl[pair_slot(tid)] = __builtin_bit_cast(uint16_t, al);
+            kh[pair_slot(tid)] = __builtin_bit_cast(uint16_t, ah);
+            kl[pair_slot(tid)] = __builtin_bit_cast(uint16_t, al);
             ck = ((float)ah + (float)al) * (unpack_offset(tid) + half_bits_to_float((uint16_t)b.kz));
         }
-        const float CK = block_sum128(ck, red);     // (its barrier also publishes xh/xl)
-        const uint4* hq = reinterpret_cast<const uint4*>(xh) + qk * 4;
-        const uint4* lq = reinterpret_cast<const uint4*>(xl) + qk * 4;
-        const float s0 = group_sum<4>(chunk_dot_hl(b.k0, hq, lq, m_lo, m_hi)) - CK;
-        const float s1 = group_sum<4>(chunk_dot_hl(b.k1, hq, lq, m_lo, m_hi)) - CK;
+        const float CK = block_sum(ck, red_k);      // (its barrier also publishes kh/kl)
+        const uint4* khq = reinterpret_cast<const uint4*>(kh) + qk * 4;
+        const uint4* klq = reinterpret_cast<const uint4*>(kl) + qk * 4;
+        const float s0 = group_sum<4>(chunk_dot_hl(b.k0, khq, klq, m_lo, m_hi)) - CK;
+        const float s1 = group_sum<4>(chunk_dot_hl(b.k1, khq, klq, m_lo, m_hi)) - CK;
 
         // ---- softmax update over the block's 128 scores.
-        const float bm = block_max256(__builtin_fmaxf(s0, s1), red);
+        const float bm = block_max(__builtin_fmaxf(s0, s1), red_m);
         const float Mn = __builtin_fmaxf(M, bm);
         const float alpha = exp2_fast(M - Mn);
         M = Mn;
@@ -225,19 +226,17 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
                 const float w = (e ? p1 : p0) * half_bits_to_float((uint16_t)(e ? b.vs1 : b.vs0));
                 const _Float16 wh = (_Float16)w;
                 const _Float16 wl = (_Float16)(w - (float)wh);
-                xh[pair_slot(t)] = __builtin_bit_cast(uint16_t, wh);
-                xl[pair_slot(t)] = __builtin_bit_cast(uint16_t, wl);
+                vh[pair_slot(t)] = __builtin_bit_cast(uint16_t, wh);
+                vl[pair_slot(t)] = __builtin_bit_cast(uint16_t, wl);
                 cv += ((float)wh + (float)wl) *
                       (unpack_offset(t) + half_bits_to_float((uint16_t)(e ? b.vz1 : b.vz0)));
             }
         }
-        cv = group_sum<64>(cv);
-        if ((tid & 63) == 0) red[tid >> 6] = cv;
-        __syncthreads();
-        const float CV = red[0] + red[1] + red[2] + red[3];
-        o0 += group_sum<4>(chunk_dot_hl(b.v0, hq, lq, m_lo, m_hi)) - CV;
-        o1 += group_sum<4>(chunk_dot_hl(b.v1, hq, lq, m_lo, m_hi)) - CV;
-        __syncthreads();                 // xh/xl and red are rewritten by the next block
+        const float CV = block_sum(cv, red_v);      // (its barrier also publishes vh/vl)
+        const uint4* vhq = reinterpret_cast<const uint4*>(vh) + qk * 4;
+        const uint4* vlq = reinterpret_cast<const uint4*>(vl) + qk * 4;
+        o0 += group_sum<4>(chunk_dot_hl(b.v0, vhq, vlq, m_lo, m_hi)) - CV;
+        o1 += group_sum<4>(chunk_dot_hl(b.v1, vhq, vlq, m_lo, m_hi)) - CV;
     };
 
     Blk A = {}, B = {};
@@ -269,7 +268,7 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
                 }
             }
         }
-        const float bm = block_max256(s, red);
+        const float bm = block_max(s, red_r);
         const float Mn = __builtin_fmaxf(M, bm);
         const float alpha = exp2_fast(M - Mn);
         M = Mn;
@@ -291,11 +290,9 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
         // (the other lanes of the quad keep stale o0/o1; only qk == 0 stores)
     }
 
-    // Total of the per-thread sums of p.
-    float lt = group_sum<64>(lsum);
-    if ((tid & 63) == 0) red[tid >> 6] = lt;
-    __syncthreads();
-    lt = red[0] + red[1] + red[2] + red[3];
+    // Total of the per-thread sums of p (red_k's last readers passed at least
+    // two barriers since, or it was never used).
+    const float lt = block_sum(lsum, red_k);
 
     if (splits == 1) {
         if (qk == 0) {
