@@ -1,0 +1,136 @@
+"""Pins of the NF4 oracle (CPU only): the level set, the encoder and the
+product.  Source: "Gör inference billig: KV cache, batching och
+kvantisering", the NF4 paragraph (normal-quantile levels, absolute-maximum
+block scaling, 4.25 bits per weight at blocks of 64)."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+F16 = np.float16
+
+
+@pytest.fixture(scope="module")
+def nf4(oracle_mod):
+    import oracle.nf4 as m
+    return m
+
+
+def test_levels_are_normal_quantiles(nf4):
+    """Checked against empirical quantiles of a large normal sample (not the
+    library quantile function the oracle uses)."""
+    L = nf4.levels_f64()
+    x = np.sort(np.random.default_rng(0).standard_normal(4_000_000))
+    emp = x[((np.arange(16) + 0.5) / 16 * x.size).astype(int)]
+    emp = emp / np.abs(emp).max()
+    assert np.allclose(L, emp, atol=3e-3)
+    h = nf4.levels()
+    assert h[0] == -1 and h[-1] == 1 and np.all(np.diff(h.astype(np.float64)) > 0)
+    assert np.array_equal(h, -h[::-1])                 # symmetric, no exact zero
+    # Denser near zero than in the tails (the page's point).
+    gaps = np.diff(h.astype(np.float64))
+    assert gaps[7] < gaps[3] < gaps[0]
+
+
+def test_bits_per_weight_at_block_64():
+    # 4-bit codes plus one 16-bit scale per 64 weights: 4.25 (and 4.125 at 128).
+    assert 4 + 16 / 64 == 4.25 and 4 + 16 / 128 == 4.125
+
+
+def _brute(W, group, L):
+    """Nearest fp16 level to fp32(w / s), ties to the lower code, in exact
+    rationals."""
+    N, K = W.shape
+    Lf = [Fraction(float(v)) for v in L]
+    codes = np.zeros((N, K), dtype=np.int64)
+    scales = np.zeros((N, K // group), dtype=np.float16)
+    for n in range(N):
+        for g in range(K // group):
+            v = W[n, g * group:(g + 1) * group]
+            s = max(abs(float(a)) for a in v)
+            s = 1.0 if s == 0 else s
+            scales[n, g] = s
+            for i, a in enumerate(v):
+                t = Fraction(float(np.float32(np.float32(a) / np.float32(s))))
+                d = [abs(t - l) for l in Lf]
+                codes[n, g * group + i] = min(range(16), key=lambda j: (d[j], j))
+    return codes, scales
+
+
+def test_ties_go_to_the_lower_code(nf4):
+    """With fp16 inputs the fp32 quotient can only land exactly on the middle
+    midpoint (0): +0 and -0 in a non-zero group take code 7, the lower of the
+    two central levels.  (Other midpoints need 12 significant bits; an fp16
+    weight over an fp16 scale reaches one only through a rare fp32 rounding,
+    and the brute-force test covers whatever the random groups produce.)"""
+    W = np.array([[0.0, -0.0, 0.25, -0.125] * 8], dtype=F16)
+    codes, scales = nf4.quantize(W, 32)
+    q = nf4.unpack(codes, 32)[0]
+    assert float(nf4.midpoints()[7]) == 0.0
+    assert np.all(q[0::4] == 7) and np.all(q[1::4] == 7)
+    L = nf4.levels()
+    assert q[2] == 15 and L[q[3]] == L[np.argmin(np.abs(L.astype(np.float64) + 0.5))]
+
+
+@pytest.mark.parametrize("group", [8, 64])
+def test_encoder_matches_bruteforce(nf4, group):
+    rng = np.random.default_rng(group)
+    W = (rng.standard_normal((6, 128)) * 0.02).astype(F16)
+    W[0, :group] = 0                                     # all-zero group: scale 1.0
+    W[1, 5] = 0.5                                        # an outlier
+    L = nf4.levels()
+    # Values exactly on the midpoints of the first row's second group (ties).
+    s = float(np.abs(W[2, :group].astype(np.float64)).max())
+    mids = nf4.midpoints().astype(np.float64)
+    for i in range(min(group - 1, 15)):
+        cand = F16(mids[i] * s)
+        if float(np.float32(cand) / np.float32(s)) == mids[i]:
+            W[2, i + 1] = cand
+    codes, scales = nf4.quantize(W, group)
+    bc, bs = _brute(W, group, L)
+    assert np.array_equal(nf4.unpack(codes, 128), bc)
+    assert np.array_equal(scales.view(np.uint16), bs.view(np.uint16))
+
+
+def test_fixpoint_and_error_bound(nf4):
+    L = nf4.levels().astype(np.float64)
+    rng = np.random.default_rng(3)
+    q = rng.integers(0, 16, (4, 64))
+    q[:, 0] = 15                                         # the group maximum is +s
+    s = 2.0 ** rng.integers(-10, -2, (4, 1))
+    W = (L[q] * s).astype(F16)
+    assert np.array_equal(W.astype(np.float64), L[q] * s)
+    codes, scales = nf4.quantize(W, 64)
+    assert np.array_equal(nf4.unpack(codes, 64), q)
+    assert np.array_equal(nf4.dequantize(codes, scales, 64, 64), W.astype(np.float64))
+    # Error bound: half the widest level gap, times s.
+    W = (rng.standard_normal((32, 256)) * 0.02).astype(F16)
+    codes, scales = nf4.quantize(W, 64)
+    err = np.abs(nf4.dequantize(codes, scales, 256, 64) - W.astype(np.float64))
+    s = np.repeat(scales.astype(np.float64), 64, axis=1)
+    assert np.all(err <= s * np.diff(L).max() / 2 * (1 + 2.0 ** -20))
+
+
+def test_gemm_is_the_dequantized_product(nf4):
+    rng = np.random.default_rng(4)
+    W = (rng.standard_normal((40, 256)) * 0.02).astype(F16)
+    X = rng.standard_normal((3, 256)).astype(F16)
+    codes, scales = nf4.quantize(W, 64)
+    Wh = nf4.dequantize(codes, scales, 256, 64)
+    ref = np.einsum("bk,nk->bn", X.astype(np.float64), Wh)
+    assert np.allclose(nf4.gemm(X, codes, scales, 256, 64), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_quality_on_gaussian_weights(nf4, oracle_mod):
+    """Not a pin: on N(0, 1)-shaped weights, NF4 at block 64 beats symmetric
+    int4 absmax at group 128 (the page's comparison; its 28 % is measured
+    on real weights)."""
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((256, 1024)) * 0.02).astype(F16)
+    x = W.astype(np.float64)
+    codes, scales = nf4.quantize(W, 64)
+    e_nf4 = np.linalg.norm(nf4.dequantize(codes, scales, 1024, 64) - x) / np.linalg.norm(x)
+    c, s, z = oracle_mod.quantize(W, 128, 4, scheme="sym")
+    e_sym = np.linalg.norm(oracle_mod.dequantize(c, s, z, 256, 1024, 128, 4) - x) / np.linalg.norm(x)
+    assert e_nf4 < e_sym
