@@ -17,10 +17,12 @@ Readings (the page gives no formula):
     fp16 values (the set is symmetric and has no exact zero);
   * the scale of a group is its largest |w|, stored in fp16 (exact: it is one
     of the fp16 inputs), 1.0 for an all-zero group;
-  * a weight's code is the level nearest to t = fp32(w / s), the quotient
-    rounded once to fp32; a t exactly between two levels takes the lower
-    code.  Midpoints of adjacent fp16 levels are exact in fp32, so the
-    decision is exact given t;
+  * a weight's code is the level nearest to the exact quotient w / s (an
+    exact-rational decision, like every decision of the integer codec); a
+    quotient exactly between two levels takes the lower code.  Midpoints of
+    adjacent fp16 levels have at most 12 significant bits, so a midpoint
+    times an fp16 scale is exact in fp32 and w can be compared with it
+    directly;
   * codes are packed two per byte, even k in the low nibble (the layout of
     the 4-bit integer codes); dequantization is level[q] * s.
 
@@ -62,11 +64,13 @@ def quantize(W: np.ndarray, group: int):
     N, K = W.shape
     if K % group or group % 2:
         raise ValueError("nf4: K must be a multiple of group, group even")
-    g = W.reshape(N, K // group, group)
-    s = np.abs(g.astype(np.float32)).max(axis=2)
-    s = np.where(s == 0, np.float32(1.0), s).astype(np.float16)
-    t = g.astype(np.float32) / s.astype(np.float32)[:, :, None]       # IEEE fp32 division
-    q = np.searchsorted(midpoints(), t.reshape(-1), side="left").reshape(N, K).astype(np.uint8)
+    g = W.reshape(N, K // group, group).astype(np.float64)
+    s = np.abs(g).max(axis=2)
+    s = np.where(s == 0, 1.0, s).astype(np.float16)
+    # Thresholds mid_i * s are exact in float64 (and in fp32); the code is the
+    # number of thresholds strictly below w.
+    th = midpoints().astype(np.float64)[None, None, :] * s.astype(np.float64)[:, :, None]
+    q = (g[:, :, :, None] > th[:, :, None, :]).sum(axis=3).reshape(N, K).astype(np.uint8)
     codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
     return codes, s
 

@@ -39,8 +39,8 @@ def test_bits_per_weight_at_block_64():
 
 
 def _brute(W, group, L):
-    """Nearest fp16 level to fp32(w / s), ties to the lower code, in exact
-    rationals."""
+    """Nearest fp16 level to the exact quotient w / s, ties to the lower code,
+    in exact rationals."""
     N, K = W.shape
     Lf = [Fraction(float(v)) for v in L]
     codes = np.zeros((N, K), dtype=np.int64)
@@ -52,18 +52,17 @@ def _brute(W, group, L):
             s = 1.0 if s == 0 else s
             scales[n, g] = s
             for i, a in enumerate(v):
-                t = Fraction(float(np.float32(np.float32(a) / np.float32(s))))
+                t = Fraction(float(a)) / Fraction(s)
                 d = [abs(t - l) for l in Lf]
                 codes[n, g * group + i] = min(range(16), key=lambda j: (d[j], j))
     return codes, scales
 
 
 def test_ties_go_to_the_lower_code(nf4):
-    """With fp16 inputs the fp32 quotient can only land exactly on the middle
-    midpoint (0): +0 and -0 in a non-zero group take code 7, the lower of the
-    two central levels.  (Other midpoints need 12 significant bits; an fp16
-    weight over an fp16 scale reaches one only through a rare fp32 rounding,
-    and the brute-force test covers whatever the random groups produce.)"""
+    """+0 and -0 in a non-zero group sit exactly on the middle midpoint (0)
+    and take code 7, the lower of the two central levels.  (The other
+    midpoints have 12 significant bits, so w / s equals one only for rare
+    pairs; the brute-force test covers whatever the random groups produce.)"""
     W = np.array([[0.0, -0.0, 0.25, -0.125] * 8], dtype=F16)
     codes, scales = nf4.quantize(W, 32)
     q = nf4.unpack(codes, 32)[0]
