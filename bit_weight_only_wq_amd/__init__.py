@@ -16,7 +16,7 @@ from ._lib import (WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA, WQError,  # noqa: F
                    LIB_PATH, check, load)
 
 __all__ = ["quantize_pack", "gemm", "gemm_grouped", "codes_bytes", "num_groups", "gemv_max_batch",
-           "KVCache", "kv_quantize_block", "kv_attention", "WQError", "LIB_PATH", "load"]
+           "gemm_nf4", "KVCache", "kv_quantize_block", "kv_attention", "WQError", "LIB_PATH", "load"]
 
 _PATHS = {"auto": WQ_PATH_AUTO, "gemv": WQ_PATH_GEMV, "mfma": WQ_PATH_MFMA}
 
@@ -50,15 +50,16 @@ def gemv_max_batch() -> int:
     return int(load().wq_gemv_max_batch())
 
 
-SCHEMES = {"asym": 0, "sym": 1, "sym_tensor": 2}
+SCHEMES = {"asym": 0, "sym": 1, "sym_tensor": 2, "nf4": 3}
 
 
 def quantize_pack(W, group: int = 128, bits: int = 4, out=None, scheme: str = "asym"):
     """W fp16 [N, K] (GPU) -> (codes u8 [N, K*bits//8], scales fp16 [N, K//group], zeros fp16).
 
     scheme "asym" (min/max, integer zero point), "sym" (absolute maximum per
-    group; group = K for one scale per output channel) or "sym_tensor" (one
-    absolute maximum for the whole matrix)."""
+    group; group = K for one scale per output channel), "sym_tensor" (one
+    absolute maximum for the whole matrix) or "nf4" (normal-quantile levels,
+    bits = 4; multiply with gemm_nf4)."""
     import torch
     lib = load()
     if scheme not in SCHEMES:
@@ -210,4 +211,24 @@ def kv_attention(q, cache: KVCache, lens, out=None):
         st = load().wq_kv_attention(q.data_ptr(), ctypes.byref(desc), lens.data_ptr(), out.data_ptr(),
                                     _stream_handle(cache.device))
     check(st, "wq_kv_attention")
+    return out
+
+
+def gemm_nf4(X, codes, scales, N: int, K: int, group: int = 64, out=None):
+    """Y fp16 [B, N] = X [B, K] times the NF4 weights (codes, scales from
+    quantize_pack(..., scheme="nf4"))."""
+    import torch
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [B, K]")
+    B = X.shape[0]
+    _need(X, torch.float16, (B, K), "X")
+    _need(codes, torch.uint8, (N, K // 2), "codes")
+    _need(scales, torch.float16, (N, K // group), "scales")
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float16, device=X.device)
+    _need(out, torch.float16, (B, N), "out")
+    with torch.cuda.device(X.device):
+        st = load().wq_gemm_nf4(X.data_ptr(), codes.data_ptr(), scales.data_ptr(), out.data_ptr(),
+                                B, K, N, group, _stream_handle(X.device))
+    check(st, "wq_gemm_nf4")
     return out

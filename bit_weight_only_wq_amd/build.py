@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libwq.so")
-SOURCES = ["wq_api.hip", "wq_quantize.hip", "wq_gemv.hip", "wq_gemv_lowbit.hip", "wq_gemm_mfma.hip", "wq_gemm_xr.hip", "wq_kv.hip", "wq_workspace.hip"]
+SOURCES = ["wq_api.hip", "wq_quantize.hip", "wq_gemv.hip", "wq_gemv_lowbit.hip", "wq_gemv_nf4.hip", "wq_gemm_mfma.hip", "wq_gemm_xr.hip", "wq_kv.hip", "wq_workspace.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -26,6 +26,8 @@ HIPCC_FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
+    from . import gen_nf4
+    gen_nf4.write()                      # csrc/wq_nf4_levels.h (NF4 level table)
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
     tmp = LIB + ".tmp"

@@ -83,8 +83,10 @@ wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: K=%lld is not a multiple of group=%lld", K, group);
     if (bits < 1 || bits > 8)
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: bits=%lld out of range", bits);
-    if (scheme < WQ_SCHEME_ASYM || scheme > WQ_SCHEME_SYM_TENSOR)
+    if (scheme < WQ_SCHEME_ASYM || scheme > WQ_SCHEME_NF4)
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: unknown scheme %lld", scheme);
+    if (scheme == WQ_SCHEME_NF4 && bits != 4)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: NF4 codes are 4 bits (got %lld)", bits);
     if (bits < 2)
         return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: the codec takes bits 2..8 (got %lld)", bits);
     if (group % 8 != 0)
@@ -298,6 +300,25 @@ wq_status wq_kv_attention(const void* q, const wq_kv_cache* cache, const int32_t
         return fail(WQ_ERR_MISALIGNED, "wq_kv_attention: q/out need 2-byte and lens 4-byte alignment");
     return check_hip(wq::launch_kv_attention(q, a, lens, out, num_cus(), static_cast<hipStream_t>(stream)),
                      "wq_kv_attention launch");
+}
+
+wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B,
+                      int64_t K, int64_t N, int32_t group, void* stream) {
+    g_last_error[0] = '\0';
+    if (B < 0 || N < 0 || K < 1 || group < 1)
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm_nf4: need B >= 0, N >= 0, K >= 1, group >= 1 (B=%lld K=%lld)", B, K);
+    if (K % group != 0)
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm_nf4: K=%lld is not a multiple of group=%lld", K, group);
+    if (!wq::gemv_nf4_supports(K, group))
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm_nf4: needs K %% 32 == 0, group %% 32 == 0, K <= 16384 (K=%lld group=%lld)",
+                    K, group);
+    if (B == 0 || N == 0) return WQ_OK;
+    if (!X || !codes || !scales || !Y) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_nf4: null pointer");
+    if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(Y, 2))
+        return fail(WQ_ERR_MISALIGNED, "wq_gemm_nf4: X and codes need 16-byte alignment");
+    return check_hip(wq::launch_gemv_nf4(X, codes, scales, Y, B, K, N, group, num_cus(),
+                                         static_cast<hipStream_t>(stream)),
+                     "wq_gemm_nf4 launch");
 }
 
 wq_status wq_gemm(const void* X, const void* codes, const void* scales, const void* zeros,

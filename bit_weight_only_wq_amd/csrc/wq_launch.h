@@ -25,6 +25,11 @@ hipError_t launch_gemv_lowbit(const void* X, const void* codes, const void* scal
                               const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                               int32_t group, int32_t bits, int num_cus, hipStream_t stream);
 
+// NF4 GEMV (level table lookup; any batch, codes re-streamed per four rows).
+bool gemv_nf4_supports(int64_t K, int32_t group);
+hipError_t launch_gemv_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B,
+                           int64_t K, int64_t N, int32_t group, int num_cus, hipStream_t stream);
+
 // Matrix-core family: the X-resident kernel for B <= 32 (xr_*), the tiled
 // kernel beyond.
 bool xr_supports(int64_t B, int64_t K, int32_t group, int32_t bits);

@@ -23,6 +23,7 @@
 // wave are contiguous.
 #include "wq_device.h"
 #include "wq_launch.h"
+#include "wq_nf4_levels.h"
 
 namespace wq {
 
@@ -69,6 +70,45 @@ __device__ __forceinline__ GroupHeader header_for(int scheme, float mn, float mx
                                                   int bits) {
     if (scheme == 0) return make_header(mn, mx, (1 << bits) - 1);
     return make_header_sym(scheme == 2 ? Aall : __builtin_fmaxf(-mn, mx), bits);
+}
+
+// NF4 (scheme 3, 4-bit codes only; "Gör inference billig", the NF4
+// paragraph): scale s = the group's largest |w| (an fp16 input, so exact;
+// 1.0 for an all-zero group) and code = the level nearest to w / s, ties to
+// the lower code.  The levels are symmetric, so with a = |w| the code is
+// 8 + #{j >= 8 : mid_j * s < a} for w > 0 and 7 - #{j >= 8 : mid_j * s <= a}
+// otherwise; mid_j * s is exact in fp32 (12 + 11 significant bits), so every
+// comparison is exact.
+struct Nf4Group {
+    float th[7];        // mid_j * s, j = 8..14
+    uint16_t sbits;
+};
+
+__device__ __forceinline__ Nf4Group nf4_group(float mn, float mx) {
+    Nf4Group g;
+    float A = __builtin_fmaxf(-mn, mx);
+    A = A == 0.0f ? 1.0f : A;
+    g.sbits = float_to_half_bits_rne(A);
+#pragma unroll
+    for (int j = 0; j < 7; ++j) g.th[j] = kNf4Mid[8 + j] * A;
+    return g;
+}
+
+__device__ __forceinline__ uint32_t nf4_code(float x, const Nf4Group& g) {
+    const float a = __builtin_fabsf(x);
+    const bool pos = x > 0.0f;
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) c += pos ? (g.th[j] < a) : (g.th[j] <= a);
+    return (uint32_t)(pos ? 8 + c : 7 - c);
+}
+
+// Eight NF4 codes packed as eight nibbles (even position low).
+__device__ __forceinline__ uint32_t nf4_encode8(const float* x, const Nf4Group& g) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= nf4_code(x[i], g) << (4 * i);
+    return w;
 }
 
 // fp16 bits of the tensor's absolute maximum, written by the reduction
@@ -229,6 +269,21 @@ __global__ __launch_bounds__(256) void quantize_team_kernel(
         mx = __builtin_fmaxf(mx, b);
     }
     group_minmax<T>(mn, mx);
+    if constexpr (BITS == 4) {
+        if (scheme == 3) {
+            const Nf4Group g = nf4_group(mn, mx);
+            if (!live) return;
+            uint32_t p[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) p[i] = nf4_encode8(x[i], g);
+            store_codes<4, CPL>(codes + u * CPL * 4, p);
+            if ((threadIdx.x & (T - 1)) == 0) {
+                scales[u / T] = g.sbits;
+                zeros[u / T] = 0;
+            }
+            return;
+        }
+    }
     const GroupHeader h = header_for(scheme, mn, mx, Aall, BITS);
     if (!live) return;
     typename Packed8<BITS>::type p[CPL];
@@ -264,6 +319,23 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
         mx = __builtin_fmaxf(mx, b);
     }
     group_minmax<kWave>(mn, mx);
+    if constexpr (BITS == 4) {
+        if (scheme == 3) {
+            const Nf4Group ng = nf4_group(mn, mx);
+            for (int64_t j = lane; j < cpg; j += kWave) {
+                float x[8];
+                uint4 raw;
+                load8(W + (c0 + j) * 8, x, raw);
+                const uint32_t p = nf4_encode8(x, ng);
+                store_codes<4, 1>(codes + (c0 + j) * 4, &p);
+            }
+            if (lane == 0) {
+                scales[g] = ng.sbits;
+                zeros[g] = 0;
+            }
+            return;
+        }
+    }
     const GroupHeader h = header_for(scheme, mn, mx, Aall, BITS);
     for (int64_t j = lane; j < cpg; j += kWave) {
         float x[8];

@@ -98,7 +98,8 @@ wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
 typedef enum {
     WQ_SCHEME_ASYM = 0,       /* min/max per group, integer zero point (wq_quantize_pack) */
     WQ_SCHEME_SYM = 1,        /* symmetric, absolute maximum per group */
-    WQ_SCHEME_SYM_TENSOR = 2  /* symmetric, one absolute maximum for the whole matrix */
+    WQ_SCHEME_SYM_TENSOR = 2, /* symmetric, one absolute maximum for the whole matrix */
+    WQ_SCHEME_NF4 = 3         /* NF4 levels, absolute maximum per group (bits = 4) */
 } wq_scheme;
 
 /*
@@ -116,6 +117,15 @@ typedef enum {
  * Arguments, layout and errors as wq_quantize_pack; an unknown scheme is
  * WQ_ERR_INVALID_ARG.  WQ_SCHEME_SYM_TENSOR enqueues two small reduction
  * launches before the quantize launch and uses the stream's workspace.
+ *
+ * WQ_SCHEME_NF4 ("Gör inference billig: KV cache, batching och
+ * kvantisering", the NF4 paragraph; bits must be 4, else
+ * WQ_ERR_UNSUPPORTED): sixteen fixed levels, level i = the standard normal
+ * quantile at (i + 1/2)/16 normalised to [-1, 1] and rounded to fp16;
+ * s = the group's largest |w| (1.0 for an all-zero group); code = the level
+ * nearest to w / s, decided exactly, ties to the lower code.  Codes two per
+ * byte as for 4-bit integers; `zeros` is written with +0.0 (NF4 has no zero
+ * point).  Multiply with wq_gemm_nf4, not wq_gemm.
  */
 wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group,
                               int32_t bits, int32_t scheme, void* codes, void* scales,
@@ -153,6 +163,19 @@ wq_status wq_gemm(const void* X, const void* codes, const void* scales,
 wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales,
                      const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                      int32_t group, int32_t bits, int32_t path, void* stream);
+
+/*
+ * Product with NF4 weights (codes and scales from wq_quantize_pack_ex with
+ * WQ_SCHEME_NF4):
+ *     Y[b, n] = sum_k X[b, k] * level[q[n, k]] * scales[n, k/group]
+ * fp32 accumulation, Y rounded once to fp16.  X fp16 [B, K] (16-byte
+ * aligned), codes u8 [N, K/2] (16-byte aligned), scales fp16 [N, K/group],
+ * Y fp16 [B, N].  K % 32 == 0, group % 32 == 0, K <= 16384 (else
+ * WQ_ERR_UNSUPPORTED); B or N == 0 is a no-op.  VALU kernel with a level
+ * lookup table, any B (codes are streamed once per four batch rows).
+ */
+wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B,
+                      int64_t K, int64_t N, int32_t group, void* stream);
 
 /* The arguments of one wq_gemm call, for wq_gemm_grouped. */
 typedef struct wq_gemm_item {
@@ -270,7 +293,7 @@ const char* wq_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int32_t wq_version(void);
 
-#define WQ_VERSION 103
+#define WQ_VERSION 104
 
 #ifdef __cplusplus
 }
