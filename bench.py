@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--kv", action="store_true",
                    help="decode attention over an int4 KV cache, 1024 heads x 4096 tokens "
                         "(a 7B-class model's whole cache; table line)")
+    p.add_argument("--nf4", action="store_true",
+                   help="NF4 weights (block 64) on the step's workload: quantize + GEMV at "
+                        "--batches (default 1) (table line)")
     p.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
     p.add_argument("--bits", type=int, default=0,
                    help="code width of the step (default: the workload's, 4); 2 and 3 take "
@@ -624,6 +627,69 @@ def run_kv(args):
     return row
 
 
+def run_nf4(args):
+    """NF4 at blocks of 64 (the block the NF4 paragraph of "Gör inference
+    billig" uses) on the step's workload: GPU quantize and the level-table
+    GEMV, each timed as a burst of launches rotating over >= 1 GiB of
+    packed copies."""
+    import torch
+
+    import bit_weight_only_wq_amd as wq
+    import wq_inputs
+    from bit_weight_only_wq_amd import roofline as rl
+
+    cfg = wq_inputs.WORKLOADS[args.workload]
+    N, K, G = cfg["N"], cfg["K"], 64
+    batches = [int(b) for b in args.batches.split(",")] if args.batches else [1]
+    Wn, Xn = wq_inputs.workload_arrays(args.workload)
+    W = torch.from_numpy(Wn).cuda()
+    X = torch.from_numpy(Xn).cuda()
+    packed = N * K // 2 + 2 * N * (K // G)            # codes + one fp16 scale per block
+    P = max(3, -(-POOL_BYTES // packed))
+    pool = [wq.quantize_pack(W, G, 4, scheme="nf4")[:2] for _ in range(P)]
+    stream = torch.cuda.current_stream()
+
+    def burst(fn, reps):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    kernels = {}
+    for B in batches:
+        Xb = X[:B].contiguous()
+        Y = torch.empty((B, N), dtype=torch.float16, device="cuda")
+        ms = burst(lambda i: wq.gemm_nf4(Xb, *pool[i % P], N=N, K=K, group=G, out=Y), args.steps)
+        nbytes = packed + 2 * B * K + 2 * B * N
+        kernels[f"wq_gemm_nf4_B{B}"] = {"avg_us": round(ms * 1e3, 2), "bytes": nbytes,
+                                        "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    outs = [(torch.empty_like(pool[0][0]), torch.empty_like(pool[0][1]),
+             torch.empty((N, K // G), dtype=torch.float16, device="cuda")) for _ in range(2)]
+    ms_q = burst(lambda i: wq.quantize_pack(W, G, 4, out=outs[i % 2], scheme="nf4"), args.steps)
+    qb = 2 * N * K + packed
+    kernels["wq_quantize_pack_nf4"] = {"avg_us": round(ms_q * 1e3, 2), "bytes": qb,
+                                       "achieved_GBps": round(qb / (ms_q * 1e-3) / 1e9, 1)}
+    head = kernels[f"wq_gemm_nf4_B{batches[0]}"]
+    row = {"metric": "NF4 decode GEMV, achieved HBM GB/s", "value": head["achieved_GBps"], "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "ms_per_step": round(head["avg_us"] / 1e3, 5),
+           "higher_is_better": True, "dtype": "f16", "data": "synthetic",
+           "config": {"workload": args.workload, "N": N, "K": K, "group": G, "format": "nf4",
+                      "batches": batches},
+           "roofline": {"bound": "hbm", "achieved": head["achieved_GBps"],
+                        "peak": rl.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
+                        "frac": round(head["achieved_GBps"] * 1e9 / rl.MI355X_HBM_BYTES_PER_S, 4)},
+           "kernels": kernels}
+    print(json.dumps(row), flush=True)
+    return row
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -642,6 +708,9 @@ def main():
     if args.kv:
         run_kv(args)
         calibration_copy(args)
+        return
+    if args.nf4:
+        run_nf4(args)
         return
     out, batches = run_step_bench(args)
     calibration_copy(args)

@@ -95,11 +95,14 @@ __device__ __forceinline__ Nf4Group nf4_group(float mn, float mx) {
 }
 
 __device__ __forceinline__ uint32_t nf4_code(float x, const Nf4Group& g) {
+    // th <= a is th < nextup(a) (every threshold is a normal float), so both
+    // signs take one strict comparison per threshold.
     const float a = __builtin_fabsf(x);
     const bool pos = x > 0.0f;
+    const float a2 = pos ? a : __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) + 1u);
     int c = 0;
 #pragma unroll
-    for (int j = 0; j < 7; ++j) c += pos ? (g.th[j] < a) : (g.th[j] <= a);
+    for (int j = 0; j < 7; ++j) c += g.th[j] < a2 ? 1 : 0;
     return (uint32_t)(pos ? 8 + c : 7 - c);
 }
 
