@@ -9,6 +9,10 @@ What it computes (see oracle.c for the step-by-step citations):
       group-wise asymmetric quantization along K in exact integer arithmetic,
       following the codec of "What actually happens when you quantize a KV
       cache" §3 steps 3-5 and §4.
+  quantize(W, group, bits, scheme="offset") / dequantize_offset / gemm_offset
+      the float-offset variant of "Quantization & inference optimisation"
+      ("Quantization"): codes round((x - min)/s), x_hat = q*s + min, with the
+      group minimum stored in fp16 in place of the zero point.
   quantize(W, group, bits, scheme="sym" | "sym_tensor")
       symmetric absolute-maximum quantization ("Quantization & inference
       optimisation", "Quantize a matrix by hand" and "Per-channel, and what it
@@ -68,10 +72,12 @@ def _load():
         i32 = ctypes.c_int32
         lib.oracle_quantize.argtypes = [p, i64, i64, i32, i32, p, p, p]
         lib.oracle_quantize_sym.argtypes = [p, i64, i64, i32, i32, i32, p, p, p]
+        lib.oracle_quantize_offset.argtypes = [p, i64, i64, i32, i32, p, p, p]
         lib.oracle_dequantize.argtypes = [p, p, p, i64, i64, i32, i32, p]
         lib.oracle_gemm.argtypes = [p, p, p, p, i64, i64, i64, i32, i32, p]
         lib.oracle_gemm_rows.argtypes = [p, p, p, p, i64, i64, i64, i32, i32, p, i64, p]
-        for f in (lib.oracle_quantize, lib.oracle_quantize_sym, lib.oracle_dequantize,
+        for f in (lib.oracle_quantize, lib.oracle_quantize_sym, lib.oracle_quantize_offset,
+                  lib.oracle_dequantize,
                   lib.oracle_gemm,
                   lib.oracle_gemm_rows):
             f.restype = ctypes.c_int
@@ -94,14 +100,16 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-SCHEMES = ("asym", "sym", "sym_tensor")
+SCHEMES = ("asym", "sym", "sym_tensor", "offset")
 
 
 def quantize(W: np.ndarray, group: int, bits: int, scheme: str = "asym"):
     """W fp16 [N, K] -> (codes u8 [N, K*bits//8], scales fp16 [N, K//group], zeros fp16).
 
     scheme "asym": min/max per group; "sym": absolute maximum per group;
-    "sym_tensor": one absolute maximum over the whole matrix.
+    "sym_tensor": one absolute maximum over the whole matrix; "offset": the
+    float-offset variant, whose third array holds the group minima (fp16)
+    instead of zero points (dequantize with dequantize_offset).
     """
     if scheme not in SCHEMES:
         raise ValueError(f"oracle: unknown scheme {scheme!r}")
@@ -116,6 +124,9 @@ def quantize(W: np.ndarray, group: int, bits: int, scheme: str = "asym"):
     if scheme == "asym":
         rc = lib.oracle_quantize(_ptr(W), N, K, group, bits, _ptr(codes), _ptr(scales),
                                  _ptr(zeros))
+    elif scheme == "offset":
+        rc = lib.oracle_quantize_offset(_ptr(W), N, K, group, bits, _ptr(codes), _ptr(scales),
+                                        _ptr(zeros))
     else:
         rc = lib.oracle_quantize_sym(_ptr(W), N, K, group, bits, int(scheme == "sym_tensor"),
                                      _ptr(codes), _ptr(scales), _ptr(zeros))
@@ -155,3 +166,25 @@ def gemm(X, codes, scales, zeros, N: int, K: int, group: int, bits: int,
     _check(lib.oracle_gemm_rows(_ptr(X), _ptr(codes), _ptr(scales), _ptr(zeros), B, K, N,
                                 group, bits, _ptr(r), r.size, _ptr(Y)))
     return Y
+
+
+def _unpack_codes(codes: np.ndarray, K: int, bits: int) -> np.ndarray:
+    bitsarr = np.unpackbits(np.ascontiguousarray(codes, dtype=np.uint8), axis=1,
+                            bitorder="little")[:, :K * bits]
+    w = 1 << np.arange(bits, dtype=np.int64)
+    return (bitsarr.reshape(codes.shape[0], K, bits).astype(np.int64) * w).sum(-1)
+
+
+def dequantize_offset(codes, scales, mins, K: int, group: int, bits: int) -> np.ndarray:
+    """Float-offset variant: W_hat float64 [N, K] = q * s + min (exact in
+    double: q * s has at most 19 significant bits)."""
+    q = _unpack_codes(codes, K, bits)
+    s = np.repeat(np.asarray(scales, dtype=np.float16).astype(np.float64), group, axis=1)
+    m = np.repeat(np.asarray(mins, dtype=np.float16).astype(np.float64), group, axis=1)
+    return q * s + m
+
+
+def gemm_offset(X, codes, scales, mins, K: int, group: int, bits: int) -> np.ndarray:
+    """Y_ref float64 [B, N] = X W_hat^T for the float-offset variant."""
+    return np.asarray(X, dtype=np.float16).astype(np.float64) @ \
+        dequantize_offset(codes, scales, mins, K, group, bits).T

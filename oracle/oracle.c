@@ -42,6 +42,10 @@
  *     nibble" at b = 4 and one byte per code at b = 8;
  *   - NaN and Inf weights are rejected.
  *
+ * Float-offset variant (oracle_quantize_offset), readings: the scale as
+ * above; the offset is the group minimum itself in fp16 (exact); codes
+ * round((x - min)/s) half to even, clamped to [0, 2^b - 1]; x_hat = q*s + min.
+ *
  * Symmetric variant (oracle_quantize_sym), readings:
  *   - the scale is max|x| / (2^(b-1) - 1), the exact quotient rounded once to
  *     fp16 as above; an all-zero scope gets scale 1.0;
@@ -348,6 +352,92 @@ int oracle_quantize_sym(const uint16_t *W, int64_t N, int64_t K, int32_t group,
             }
             quantize_group_sym(xu, group, bits, per_tensor ? Aall : A, q,
                                &scales[n * ngroups + g], &zeros[n * ngroups + g]);
+            for (i = 0; i < group; i++)
+                put_code(codes + n * row_bytes, g * group + i, bits, q[i]);
+        }
+        free(xu);
+        free(q);
+    }
+    return err;
+}
+
+/*
+ * Float-offset variant ([QIO] "Quantization", the affine per-group code
+ * block): the group's minimum is kept as a float offset instead of an
+ * integer zero point.
+ *   s = (max - min) / (2^b - 1)            stored in fp16 (as above)
+ *   m = min                                stored in fp16 (exact: an input)
+ *   q = clamp(round((x - m) / s), 0, 2^b - 1)
+ *   x_hat = q * s + m
+ * The clamp only acts when the fp16 scale rounded below the exact quotient.
+ */
+static void quantize_group_offset(const int64_t *x, int64_t G, int bits, unsigned *q,
+                                  uint16_t *scale_bits, uint16_t *min_bits)
+{
+    const int64_t M = ((int64_t)1 << bits) - 1;
+    int64_t mn = x[0], mx = x[0], S = 0, i;
+    int ovf;
+    uint16_t sb;
+    for (i = 1; i < G; i++) {
+        if (x[i] < mn) mn = x[i];
+        if (x[i] > mx) mx = x[i];
+    }
+    sb = fp16_nearest_ratio(mx - mn, M, &ovf);
+    if (sb == 0)
+        sb = 0x3C00;
+    fp16_to_units(sb, &S);
+    for (i = 0; i < G; i++) {
+        int64_t c = rne_div(x[i] - mn, S);
+        if (c > M) c = M;
+        q[i] = (unsigned)c;              /* x - mn >= 0, so c >= 0 */
+    }
+    *scale_bits = sb;
+    *min_bits = 0;
+    {
+        /* the minimum is one of the fp16 inputs: recover its bits */
+        int64_t mag = mn < 0 ? -mn : mn;
+        uint16_t b = 0;
+        if (mag != 0) {
+            int dummy;
+            b = fp16_nearest_ratio(mag, 1, &dummy);
+        }
+        *min_bits = (uint16_t)(mn < 0 ? (b | 0x8000) : b);
+    }
+}
+
+int oracle_quantize_offset(const uint16_t *W, int64_t N, int64_t K, int32_t group,
+                           int32_t bits, uint8_t *codes, uint16_t *scales, uint16_t *mins)
+{
+    const int64_t row_bytes = K * bits / 8;
+    const int64_t ngroups = K / group;
+    int64_t n;
+    int err = check_shape(N, K, group, bits);
+    if (err)
+        return err;
+    for (n = 0; n < N * K; n++) {
+        int64_t u;
+        if (fp16_to_units(W[n], &u) != 0)
+            return ORACLE_ENONFINITE;
+    }
+    memset(codes, 0, (size_t)(N * row_bytes));
+    err = ORACLE_OK;
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; n++) {
+        int64_t *xu = (int64_t *)malloc(sizeof(int64_t) * (size_t)group);
+        unsigned *q = (unsigned *)malloc(sizeof(unsigned) * (size_t)group);
+        int64_t g, i;
+        if (!xu || !q) {
+            err = ORACLE_ENOMEM;
+            free(xu);
+            free(q);
+            continue;
+        }
+        for (g = 0; g < ngroups; g++) {
+            const uint16_t *src = W + n * K + g * group;
+            for (i = 0; i < group; i++)
+                fp16_to_units(src[i], &xu[i]);
+            quantize_group_offset(xu, group, bits, q, &scales[n * ngroups + g],
+                                  &mins[n * ngroups + g]);
             for (i = 0; i < group; i++)
                 put_code(codes + n * row_bytes, g * group + i, bits, q[i]);
         }

@@ -142,3 +142,36 @@ def quantize_sym(W16: np.ndarray, group: int, bits: int, per_tensor: bool = Fals
             sb[n, g], zb[n, g] = s, z
         codes[n] = np.frombuffer(pack_row(row_codes, bits), dtype=np.uint8)
     return codes, sb, zb
+
+
+def quantize_group_offset(xbits, bits):
+    """Float-offset group ("Quantization & inference optimisation",
+    "Quantization"): (codes, scale_bits, min_bits) with codes
+    round((x - min) / s) clamped to [0, 2^b - 1] and s as for the integer
+    zero point."""
+    M = 2 ** bits - 1
+    x = [fp16_value(b) for b in xbits]
+    mn, mx = min(x), max(x)
+    sb = nearest_fp16_bits((mx - mn) / M)
+    if sb == 0:
+        sb = 0x3C00
+    s = fp16_value(sb)
+    codes = [int(min(round_half_even((v - mn) / s), M)) for v in x]
+    mb = nearest_fp16_bits(abs(mn)) | (0x8000 if mn < 0 else 0)
+    return codes, sb, mb
+
+
+def quantize_offset(W16: np.ndarray, group: int, bits: int):
+    N, K = W16.shape
+    wb = W16.view(np.uint16)
+    codes = np.zeros((N, K * bits // 8), dtype=np.uint8)
+    sb = np.zeros((N, K // group), dtype=np.uint16)
+    mb = np.zeros((N, K // group), dtype=np.uint16)
+    for n in range(N):
+        row_codes = []
+        for g in range(K // group):
+            q, s, m = quantize_group_offset([int(v) for v in wb[n, g * group:(g + 1) * group]], bits)
+            row_codes += q
+            sb[n, g], mb[n, g] = s, m
+        codes[n] = np.frombuffer(pack_row(row_codes, bits), dtype=np.uint8)
+    return codes, sb, mb
