@@ -16,7 +16,7 @@ from ._lib import (WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA, WQError,  # noqa: F
                    LIB_PATH, check, load)
 
 __all__ = ["quantize_pack", "gemm", "gemm_grouped", "codes_bytes", "num_groups", "gemv_max_batch",
-           "gemm_nf4", "KVCache", "kv_quantize_block", "kv_attention", "WQError", "LIB_PATH", "load"]
+           "gemm_nf4", "gemm_offset", "KVCache", "kv_quantize_block", "kv_attention", "WQError", "LIB_PATH", "load"]
 
 _PATHS = {"auto": WQ_PATH_AUTO, "gemv": WQ_PATH_GEMV, "mfma": WQ_PATH_MFMA}
 
@@ -50,7 +50,7 @@ def gemv_max_batch() -> int:
     return int(load().wq_gemv_max_batch())
 
 
-SCHEMES = {"asym": 0, "sym": 1, "sym_tensor": 2, "nf4": 3}
+SCHEMES = {"asym": 0, "sym": 1, "sym_tensor": 2, "nf4": 3, "offset": 4}
 
 
 def quantize_pack(W, group: int = 128, bits: int = 4, out=None, scheme: str = "asym"):
@@ -58,8 +58,9 @@ def quantize_pack(W, group: int = 128, bits: int = 4, out=None, scheme: str = "a
 
     scheme "asym" (min/max, integer zero point), "sym" (absolute maximum per
     group; group = K for one scale per output channel), "sym_tensor" (one
-    absolute maximum for the whole matrix) or "nf4" (normal-quantile levels,
-    bits = 4; multiply with gemm_nf4)."""
+    absolute maximum for the whole matrix), "nf4" (normal-quantile levels,
+    bits = 4; multiply with gemm_nf4) or "offset" (the group minimum as a
+    float offset in the third array; multiply with gemm_offset)."""
     import torch
     lib = load()
     if scheme not in SCHEMES:
@@ -231,4 +232,24 @@ def gemm_nf4(X, codes, scales, N: int, K: int, group: int = 64, out=None):
         st = load().wq_gemm_nf4(X.data_ptr(), codes.data_ptr(), scales.data_ptr(), out.data_ptr(),
                                 B, K, N, group, _stream_handle(X.device))
     check(st, "wq_gemm_nf4")
+    return out
+
+
+def gemm_offset(X, codes, scales, mins, N: int, K: int, group: int = 128, bits: int = 4, out=None):
+    """Y fp16 [B, N] for float-offset weights (quantize_pack(..., scheme="offset"))."""
+    import torch
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [B, K]")
+    B = X.shape[0]
+    _need(X, torch.float16, (B, K), "X")
+    _need(codes, torch.uint8, (N, K * bits // 8), "codes")
+    _need(scales, torch.float16, (N, K // group), "scales")
+    _need(mins, torch.float16, (N, K // group), "mins")
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float16, device=X.device)
+    _need(out, torch.float16, (B, N), "out")
+    with torch.cuda.device(X.device):
+        st = load().wq_gemm_offset(X.data_ptr(), codes.data_ptr(), scales.data_ptr(), mins.data_ptr(),
+                                   out.data_ptr(), B, K, N, group, bits, _stream_handle(X.device))
+    check(st, "wq_gemm_offset")
     return out

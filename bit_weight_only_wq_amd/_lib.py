@@ -22,6 +22,7 @@ WQ_SCHEME_ASYM = 0
 WQ_SCHEME_SYM = 1
 WQ_SCHEME_SYM_TENSOR = 2
 WQ_SCHEME_NF4 = 3
+WQ_SCHEME_OFFSET = 4
 
 # Every symbol include/wq.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -51,6 +52,7 @@ SIGNATURES = {
     "wq_kv_quantize_block": (ctypes.c_int, [_P, _P, ctypes.POINTER(KvCache), _I64, _P]),
     "wq_kv_attention": (ctypes.c_int, [_P, ctypes.POINTER(KvCache), _P, _P, _P]),
     "wq_gemm_nf4": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P]),
+    "wq_gemm_offset": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P]),
     "wq_gemv_max_batch": (_I32, []),
     "wq_codes_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
     "wq_num_groups": (_I64, [_I64, _I64, _I32]),

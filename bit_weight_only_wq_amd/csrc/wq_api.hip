@@ -83,7 +83,7 @@ wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: K=%lld is not a multiple of group=%lld", K, group);
     if (bits < 1 || bits > 8)
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: bits=%lld out of range", bits);
-    if (scheme < WQ_SCHEME_ASYM || scheme > WQ_SCHEME_NF4)
+    if (scheme < WQ_SCHEME_ASYM || scheme > WQ_SCHEME_OFFSET)
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: unknown scheme %lld", scheme);
     if (scheme == WQ_SCHEME_NF4 && bits != 4)
         return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: NF4 codes are 4 bits (got %lld)", bits);
@@ -177,7 +177,7 @@ static wq_status run_gemm(const void* X, const void* codes, const void* scales, 
                                               num_cus(), st),
                          "wq_gemm (mfma) launch");
     if (bits == 2 || bits == 3)
-        return check_hip(wq::launch_gemv_lowbit(X, codes, scales, zeros, Y, B, K, N, group, bits,
+        return check_hip(wq::launch_gemv_lowbit(X, codes, scales, zeros, Y, B, K, N, group, bits, 0,
                                                 num_cus(), st),
                          "wq_gemm (2/3-bit gemv) launch");
     return check_hip(wq::launch_gemv(X, codes, scales, zeros, Y, B, K, N, group, bits, num_cus(), st),
@@ -300,6 +300,27 @@ wq_status wq_kv_attention(const void* q, const wq_kv_cache* cache, const int32_t
         return fail(WQ_ERR_MISALIGNED, "wq_kv_attention: q/out need 2-byte and lens 4-byte alignment");
     return check_hip(wq::launch_kv_attention(q, a, lens, out, num_cus(), static_cast<hipStream_t>(stream)),
                      "wq_kv_attention launch");
+}
+
+wq_status wq_gemm_offset(const void* X, const void* codes, const void* scales, const void* mins,
+                         void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                         void* stream) {
+    g_last_error[0] = '\0';
+    if (B < 0 || N < 0 || K < 1 || group < 1)
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm_offset: need B >= 0, N >= 0, K >= 1, group >= 1 (B=%lld K=%lld)", B, K);
+    if (K % group != 0)
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm_offset: K=%lld is not a multiple of group=%lld", K, group);
+    if (bits < 1 || bits > 8) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_offset: bits=%lld out of range", bits);
+    if (!wq::gemv_lowbit_supports(K, group, bits))
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm_offset: bits 2, 3, 4 or 8, group %% 32 == 0 and K a multiple of "
+                    "the load unit (K=%lld bits=%lld)", K, bits);
+    if (B == 0 || N == 0) return WQ_OK;
+    if (!X || !codes || !scales || !mins || !Y) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_offset: null pointer");
+    if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(mins, 2) || !aligned(Y, 2))
+        return fail(WQ_ERR_MISALIGNED, "wq_gemm_offset: X and codes need 16-byte alignment");
+    return check_hip(wq::launch_gemv_lowbit(X, codes, scales, mins, Y, B, K, N, group, bits, 1, num_cus(),
+                                            static_cast<hipStream_t>(stream)),
+                     "wq_gemm_offset launch");
 }
 
 wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B,

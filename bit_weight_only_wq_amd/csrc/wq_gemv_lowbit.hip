@@ -1,6 +1,10 @@
-// Decode GEMV for 2- and 3-bit codes (gfx950, VALU):
+// Bit-stream decode GEMV (gfx950, VALU) for 2- and 3-bit codes with integer
+// zero points, and for 2-, 3-, 4- and 8-bit codes of the float-offset variant:
 //   Y[B,N] = X[B,K] * dequant(W)[N,K]^T, W stored as the little-endian bit
-//   stream of wq_quantize_pack (code k of a row at bits [k*b, k*b+b)).
+//   stream of wq_quantize_pack (code k of a row at bits [k*b, k*b+b)), with
+//   dequant (q - z) * s (integer zero point) or q * s + m (float offset,
+//   "Quantization & inference optimisation", "Quantization").  A chunk adds
+//   s * sum_k q_k x_k, then -s*z or m times sum_k x_k.
 //
 // Same plan as the 4/8-bit GEMV ("Quantization & inference optimisation",
 // "Bandwidth, not compute": at small batch the time is the bytes streamed):
@@ -45,6 +49,16 @@ struct LowGeom<3> {
     static constexpr int CPL = 4;
     static constexpr int LOADS = 3;
 };
+template <>
+struct LowGeom<4> {
+    static constexpr int CPL = 1;     // one 16-byte load, 32 codes
+    static constexpr int LOADS = 1;
+};
+template <>
+struct LowGeom<8> {
+    static constexpr int CPL = 1;     // two 16-byte loads, 32 codes
+    static constexpr int LOADS = 2;
+};
 
 // uint4 per X record of one (batch row, unit): 4 per chunk of fp16 X pairs,
 // then one uint4 with each chunk's sum of X (xT) as a float.
@@ -57,7 +71,17 @@ constexpr int low_rec() {
 // chunk and the factor m its unpacked codes carry (1024 + m*q).
 template <int BITS>
 __host__ __device__ constexpr void low_pair(int P, int& a, int& b, int& m) {
-    if constexpr (BITS == 2) {
+    if constexpr (BITS == 4) {
+        const int j = P >> 2, r = P & 3;                     // word, pair in word
+        a = 8 * j + r;
+        b = a + 4;
+        m = (r & 1) ? 16 : 1;
+    } else if constexpr (BITS == 8) {
+        const int j = P >> 1, r = P & 1;
+        a = 4 * j + r;
+        b = a + 2;
+        m = 1;
+    } else if constexpr (BITS == 2) {
         const int j = P >> 3, h = (P >> 2) & 1, s = P & 3;   // word, w >> 8h, mask 2s
         a = 16 * j + 4 * h + s;
         b = a + 8;
@@ -107,6 +131,26 @@ __device__ __forceinline__ float chunk_dot(const uint32_t* cw, const uint4* xp,
                     p[s] = __builtin_amdgcn_fdot2(unpack_pair(v, mask[s]), as_h2(x[8 * j + 4 * h + s]), p[s], false);
             }
         return __builtin_fmaf(p[3], 0.015625f, __builtin_fmaf(p[2], 0.0625f, __builtin_fmaf(p[1], 0.25f, p[0])));
+    } else if constexpr (BITS == 4) {
+        // Word j holds codes 8j..8j+7: (q0,q4) and (q2,q6) as 1024 + q,
+        // (q1,q5) and (q3,q7) as 1024 + 16q.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t sh = cw[j] >> 8;
+            p[0] = __builtin_amdgcn_fdot2(unpack_pair(cw[j], mask[0]), as_h2(x[4 * j]), p[0], false);
+            p[1] = __builtin_amdgcn_fdot2(unpack_pair(cw[j], mask[1]), as_h2(x[4 * j + 1]), p[1], false);
+            p[0] = __builtin_amdgcn_fdot2(unpack_pair(sh, mask[0]), as_h2(x[4 * j + 2]), p[0], false);
+            p[1] = __builtin_amdgcn_fdot2(unpack_pair(sh, mask[1]), as_h2(x[4 * j + 3]), p[1], false);
+        }
+        return __builtin_fmaf(p[1], 0.0625f, p[0]);
+    } else if constexpr (BITS == 8) {
+        // Word j holds codes 4j..4j+3: (q0,q2) and (q1,q3) as 1024 + q.
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[0] = __builtin_amdgcn_fdot2(unpack_pair(cw[j], mask[0]), as_h2(x[2 * j]), p[0], false);
+            p[1] = __builtin_amdgcn_fdot2(unpack_pair(cw[j] >> 8, mask[0]), as_h2(x[2 * j + 1]), p[1], false);
+        }
+        return p[0] + p[1];
     } else {
         const uint32_t u[4] = {cw[0], __builtin_amdgcn_alignbit(cw[1], cw[0], 24),
                                __builtin_amdgcn_alignbit(cw[2], cw[1], 16), cw[2] >> 8};
@@ -126,12 +170,13 @@ __device__ __forceinline__ float chunk_dot(const uint32_t* cw, const uint4* xp,
 // Grid: (persistent row-pass blocks, ceil(B / NB)).  TG threads per row,
 // 256 / TG rows per block pass; thread tl of a row owns units tl, tl + TG, ...
 // (CPT of them).  HPU = group headers per unit: 1 when a group spans whole
-// units, CPL when every chunk may start a new group.
+// units, CPL when every chunk may start a new group.  offset != 0: `zeros`
+// holds float offsets (q * s + m) instead of integer zero points.
 template <int BITS, int NB, int TG, int CPT, int HPU>
 __global__ __launch_bounds__(256) void gemv_lowbit_kernel(
     const uint16_t* __restrict__ X, const uint4* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
-    uint16_t* __restrict__ Y, int64_t B, int64_t N, int64_t K, int32_t G) {
+    uint16_t* __restrict__ Y, int64_t B, int64_t N, int64_t K, int32_t G, int offset) {
     typedef LowGeom<BITS> LG;
     constexpr int CPL = LG::CPL;
     constexpr int LOADS = LG::LOADS;
@@ -150,8 +195,13 @@ __global__ __launch_bounds__(256) void gemv_lowbit_kernel(
     const int nb = (int)((B - b0) < NB ? (B - b0) : NB);
     const int64_t passes = (N + RPB - 1) / RPB;
 
-    uint32_t mask[4];
-    if constexpr (BITS == 2) {
+    uint32_t mask[4] = {0u, 0u, 0u, 0u};
+    if constexpr (BITS == 4) {
+        mask[0] = vgpr_const(0x000F000Fu);
+        mask[1] = vgpr_const(0x00F000F0u);
+    } else if constexpr (BITS == 8) {
+        mask[0] = vgpr_const(0x00FF00FFu);
+    } else if constexpr (BITS == 2) {
         mask[0] = vgpr_const(0x00030003u);
         mask[1] = vgpr_const(0x000C000Cu);
         mask[2] = vgpr_const(0x00300030u);
@@ -267,8 +317,13 @@ __global__ __launch_bounds__(256) void gemv_lowbit_kernel(
                     const uint32_t xtw = k == 0 ? kx.x : k == 1 ? kx.y : k == 2 ? kx.z : kx.w;
                     const float xT = __builtin_bit_cast(float, xtw);
                     float t = chunk_dot<BITS>(cw + BITS * k, rec + 4 * k, mask);
-                    t = __builtin_fmaf(-z, xT, t);
-                    acc[b] = __builtin_fmaf(s, t, acc[b]);
+                    if (offset) {
+                        acc[b] = __builtin_fmaf(s, t, acc[b]);
+                        acc[b] = __builtin_fmaf((row_ok && cin[i]) ? z : 0.0f, xT, acc[b]);
+                    } else {
+                        t = __builtin_fmaf(-z, xT, t);
+                        acc[b] = __builtin_fmaf(s, t, acc[b]);
+                    }
                 }
             }
         }
@@ -289,8 +344,9 @@ struct LowChoice {
 };
 
 bool low_choose(int64_t B, int64_t K, int32_t G, int32_t bits, LowChoice& ch) {
-    const int cpl = bits == 2 ? LowGeom<2>::CPL : LowGeom<3>::CPL;
-    const size_t rec = (size_t)(bits == 2 ? low_rec<2>() : low_rec<3>()) * sizeof(uint4);
+    const int cpl = bits == 2 ? LowGeom<2>::CPL : bits == 3 ? LowGeom<3>::CPL : 1;
+    const size_t rec = (size_t)(bits == 2 ? low_rec<2>() : bits == 3 ? low_rec<3>() : low_rec<4>()) *
+                       sizeof(uint4);
     if (K % (32 * cpl) != 0 || G % 32 != 0) return false;
     const int64_t U = K / (32 * cpl);
     ch.nb = B >= 2 && 4 * U * rec <= kLowMaxLds ? 4 : 1;
@@ -300,7 +356,7 @@ bool low_choose(int64_t B, int64_t K, int32_t G, int32_t bits, LowChoice& ch) {
     else if (U <= 64) ch.tg = 64, ch.cpt = 1;
     else if (U <= 128) ch.tg = 64, ch.cpt = 2;
     else if (U <= 256) ch.tg = 64, ch.cpt = 4;
-    else if (U <= 512 && bits == 2) ch.tg = 64, ch.cpt = 8;
+    else if (U <= 512 && bits != 3) ch.tg = 64, ch.cpt = 8;
     else return false;
     ch.hpu = G % (32 * cpl) == 0 ? 1 : cpl;
     return true;
@@ -308,7 +364,7 @@ bool low_choose(int64_t B, int64_t K, int32_t G, int32_t bits, LowChoice& ch) {
 
 template <int BITS, int NB, int TG, int CPT, int HPU>
 hipError_t low_launch(const void* X, const void* codes, const void* scales, const void* zeros,
-                      void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int num_cus,
+                      void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int offset, int num_cus,
                       hipStream_t stream) {
     constexpr int RPB = 256 / TG;
     const int64_t U = K / (32 * LowGeom<BITS>::CPL);
@@ -329,34 +385,36 @@ hipError_t low_launch(const void* X, const void* codes, const void* scales, cons
     gemv_lowbit_kernel<BITS, NB, TG, CPT, HPU><<<grid, dim3(256), lds, stream>>>(
         static_cast<const uint16_t*>(X), static_cast<const uint4*>(codes),
         static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
-        static_cast<uint16_t*>(Y), B, N, K, G);
+        static_cast<uint16_t*>(Y), B, N, K, G, offset);
     return hipGetLastError();
 }
 
 template <int BITS, int NB, int HPU>
 hipError_t low_by_shape(const LowChoice& ch, const void* X, const void* codes, const void* scales,
                         const void* zeros, void* Y, int64_t B, int64_t K, int64_t N, int32_t G,
-                        int cus, hipStream_t st) {
+                        int off, int cus, hipStream_t st) {
 #define WQ_LOW_CASE(TG_, CPT_)                                                                   \
     if (ch.tg == TG_ && ch.cpt == CPT_)                                                          \
-        return low_launch<BITS, NB, TG_, CPT_, HPU>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+        return low_launch<BITS, NB, TG_, CPT_, HPU>(X, codes, scales, zeros, Y, B, K, N, G, off, cus, st);
     WQ_LOW_CASE(16, 1) WQ_LOW_CASE(16, 2) WQ_LOW_CASE(64, 1) WQ_LOW_CASE(64, 2) WQ_LOW_CASE(64, 4)
 #undef WQ_LOW_CASE
-    if constexpr (BITS == 2)
+    if constexpr (BITS != 3)
         if (ch.tg == 64 && ch.cpt == 8)
-            return low_launch<BITS, NB, 64, 8, HPU>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+            return low_launch<BITS, NB, 64, 8, HPU>(X, codes, scales, zeros, Y, B, K, N, G, off, cus, st);
     return hipErrorInvalidValue;
 }
 
 template <int BITS>
 hipError_t low_by_bits(const LowChoice& ch, const void* X, const void* codes, const void* scales,
                        const void* zeros, void* Y, int64_t B, int64_t K, int64_t N, int32_t G,
-                       int cus, hipStream_t st) {
+                       int off, int cus, hipStream_t st) {
     constexpr int CPL = LowGeom<BITS>::CPL;
-    if (ch.nb == 1 && ch.hpu == 1) return low_by_shape<BITS, 1, 1>(ch, X, codes, scales, zeros, Y, B, K, N, G, cus, st);
-    if (ch.nb == 1 && ch.hpu == CPL) return low_by_shape<BITS, 1, CPL>(ch, X, codes, scales, zeros, Y, B, K, N, G, cus, st);
-    if (ch.nb == 4 && ch.hpu == 1) return low_by_shape<BITS, 4, 1>(ch, X, codes, scales, zeros, Y, B, K, N, G, cus, st);
-    if (ch.nb == 4 && ch.hpu == CPL) return low_by_shape<BITS, 4, CPL>(ch, X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+    if (ch.nb == 1 && ch.hpu == 1) return low_by_shape<BITS, 1, 1>(ch, X, codes, scales, zeros, Y, B, K, N, G, off, cus, st);
+    if (ch.nb == 4 && ch.hpu == 1) return low_by_shape<BITS, 4, 1>(ch, X, codes, scales, zeros, Y, B, K, N, G, off, cus, st);
+    if constexpr (CPL > 1) {
+        if (ch.nb == 1 && ch.hpu == CPL) return low_by_shape<BITS, 1, CPL>(ch, X, codes, scales, zeros, Y, B, K, N, G, off, cus, st);
+        if (ch.nb == 4 && ch.hpu == CPL) return low_by_shape<BITS, 4, CPL>(ch, X, codes, scales, zeros, Y, B, K, N, G, off, cus, st);
+    }
     return hipErrorInvalidValue;
 }
 
@@ -364,16 +422,21 @@ hipError_t low_by_bits(const LowChoice& ch, const void* X, const void* codes, co
 
 bool gemv_lowbit_supports(int64_t K, int32_t group, int32_t bits) {
     LowChoice ch;
-    return (bits == 2 || bits == 3) && low_choose(1, K, group, bits, ch);
+    return (bits == 2 || bits == 3 || bits == 4 || bits == 8) && low_choose(1, K, group, bits, ch);
 }
 
 hipError_t launch_gemv_lowbit(const void* X, const void* codes, const void* scales,
                               const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
-                              int32_t group, int32_t bits, int num_cus, hipStream_t stream) {
+                              int32_t group, int32_t bits, int offset, int num_cus, hipStream_t stream) {
     LowChoice ch;
-    if ((bits != 2 && bits != 3) || !low_choose(B, K, group, bits, ch)) return hipErrorInvalidValue;
-    if (bits == 2) return low_by_bits<2>(ch, X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
-    return low_by_bits<3>(ch, X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+    if (!gemv_lowbit_supports(K, group, bits) || !low_choose(B, K, group, bits, ch)) return hipErrorInvalidValue;
+    switch (bits) {
+        case 2: return low_by_bits<2>(ch, X, codes, scales, zeros, Y, B, K, N, group, offset, num_cus, stream);
+        case 3: return low_by_bits<3>(ch, X, codes, scales, zeros, Y, B, K, N, group, offset, num_cus, stream);
+        case 4: return low_by_bits<4>(ch, X, codes, scales, zeros, Y, B, K, N, group, offset, num_cus, stream);
+        case 8: return low_by_bits<8>(ch, X, codes, scales, zeros, Y, B, K, N, group, offset, num_cus, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace wq

@@ -19,11 +19,13 @@ hipError_t launch_gemv(const void* X, const void* codes, const void* scales,
                        const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                        int32_t group, int32_t bits, int num_cus, hipStream_t stream);
 
-// 2- and 3-bit GEMV (any batch; codes re-streamed once per 4 batch rows).
+// Bit-stream GEMV (any batch; codes re-streamed once per 4 batch rows): 2/3-bit
+// codes with integer zero points (offset = 0), or 2/3/4/8-bit codes of the
+// float-offset variant (offset = 1, `zeros` holds the group minima).
 bool gemv_lowbit_supports(int64_t K, int32_t group, int32_t bits);
 hipError_t launch_gemv_lowbit(const void* X, const void* codes, const void* scales,
                               const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
-                              int32_t group, int32_t bits, int num_cus, hipStream_t stream);
+                              int32_t group, int32_t bits, int offset, int num_cus, hipStream_t stream);
 
 // NF4 GEMV (level table lookup; any batch, codes re-streamed per four rows).
 bool gemv_nf4_supports(int64_t K, int32_t group);

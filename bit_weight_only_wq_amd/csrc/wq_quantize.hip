@@ -8,6 +8,10 @@
 // Rounding is half-to-even and every decision is the exact-rational one (see
 // wq_device.h).  Degenerate scale -> 1.0; zero point saturates at +-65504.
 //
+// Float-offset scheme ("Quantization & inference optimisation",
+// "Quantization"): the scale as above, the group minimum stored in place of
+// the zero point, codes round((x - min)/s) clamped to [0, 2^b - 1].
+//
 // Symmetric scheme ("Quantization & inference optimisation", "Quantize a
 // matrix by hand" and "Per-channel, and what it buys"): s = A/(2^(b-1)-1) with
 // A = max|x| of the group (or of the whole matrix), the signed integer
@@ -138,6 +142,9 @@ struct Packed8<8> {
 };
 
 template <int BITS>
+__device__ __forceinline__ typename Packed8<BITS>::type pack8(const float* q);
+
+template <int BITS>
 __device__ __forceinline__ typename Packed8<BITS>::type encode8(const float* x, const GroupHeader& h) {
     constexpr float M = (float)((1 << BITS) - 1);
     // Fast path: rint of the fp32 quotient estimate, exact unless the estimate
@@ -174,6 +181,35 @@ __device__ __forceinline__ typename Packed8<BITS>::type encode8(const float* x, 
     float q[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_fmed3f(k[i] + h.Z, 0.0f, M);
+    return pack8<BITS>(q);
+}
+
+// Float-offset variant (scheme 4; "Quantization & inference optimisation",
+// "Quantization"): q = clamp(round((x - mn) / s), 0, 2^b - 1).  In double,
+// x - mn is exact (fp16 inputs: at most 41 significant bits), and with
+// kl = floor(t) for t ~ (x - mn)/s the remainder (x - mn) - (kl + 1/2) s is
+// exact too, so its sign takes the rounding decision, ties to even.  An
+// estimate t one off at an exact integer is corrected by the same test.
+template <int BITS>
+__device__ __forceinline__ typename Packed8<BITS>::type encode8_offset(const float* x, float mn, float s) {
+    constexpr float M = (float)((1 << BITS) - 1);
+    const double sd = (double)s, rcp = 1.0 / sd, md = (double)mn;
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double d = (double)x[i] - md;
+        const double kl = __builtin_floor(d * rcp);
+        const double r = __builtin_fma(-(kl + 0.5), sd, d);
+        const bool odd = ((int)kl & 1) != 0;            // 0 <= kl < 2^20
+        const double k = (r > 0.0) | ((r == 0.0) & odd) ? kl + 1.0 : kl;
+        q[i] = __builtin_amdgcn_fmed3f((float)k, 0.0f, M);
+    }
+    return pack8<BITS>(q);
+}
+
+// Codes q[0..7] (integral floats in [0, 2^b - 1]) packed into BITS bytes.
+template <int BITS>
+__device__ __forceinline__ typename Packed8<BITS>::type pack8(const float* q) {
     if constexpr (BITS == 4) {
         // Bytes (q0,q2,q4,q6) and (q1,q3,q5,q7); byte j = q[2j] | q[2j+1] << 4.
         uint32_t ev = 0, od = 0;
@@ -287,6 +323,20 @@ __global__ __launch_bounds__(256) void quantize_team_kernel(
             return;
         }
     }
+    if (scheme == 4) {
+        const uint16_t sb = scale_bits_exact(mn, mx, (1 << BITS) - 1);
+        const float s = half_bits_to_float(sb);
+        if (!live) return;
+        typename Packed8<BITS>::type p[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) p[i] = encode8_offset<BITS>(x[i], mn, s);
+        store_codes<BITS, CPL>(codes + u * CPL * BITS, p);
+        if ((threadIdx.x & (T - 1)) == 0) {
+            scales[u / T] = sb;
+            zeros[u / T] = float_to_half_bits_rne(mn);   // exact: mn is an fp16 input
+        }
+        return;
+    }
     const GroupHeader h = header_for(scheme, mn, mx, Aall, BITS);
     if (!live) return;
     typename Packed8<BITS>::type p[CPL];
@@ -338,6 +388,22 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
             }
             return;
         }
+    }
+    if (scheme == 4) {
+        const uint16_t sb = scale_bits_exact(mn, mx, (1 << BITS) - 1);
+        const float s = half_bits_to_float(sb);
+        for (int64_t j = lane; j < cpg; j += kWave) {
+            float x[8];
+            uint4 raw;
+            load8(W + (c0 + j) * 8, x, raw);
+            const typename Packed8<BITS>::type p = encode8_offset<BITS>(x, mn, s);
+            store_codes<BITS, 1>(codes + (c0 + j) * BITS, &p);
+        }
+        if (lane == 0) {
+            scales[g] = sb;
+            zeros[g] = float_to_half_bits_rne(mn);
+        }
+        return;
     }
     const GroupHeader h = header_for(scheme, mn, mx, Aall, BITS);
     for (int64_t j = lane; j < cpg; j += kWave) {

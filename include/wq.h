@@ -99,7 +99,8 @@ typedef enum {
     WQ_SCHEME_ASYM = 0,       /* min/max per group, integer zero point (wq_quantize_pack) */
     WQ_SCHEME_SYM = 1,        /* symmetric, absolute maximum per group */
     WQ_SCHEME_SYM_TENSOR = 2, /* symmetric, one absolute maximum for the whole matrix */
-    WQ_SCHEME_NF4 = 3         /* NF4 levels, absolute maximum per group (bits = 4) */
+    WQ_SCHEME_NF4 = 3,        /* NF4 levels, absolute maximum per group (bits = 4) */
+    WQ_SCHEME_OFFSET = 4      /* min/max per group, float minimum kept as the offset */
 } wq_scheme;
 
 /*
@@ -126,6 +127,12 @@ typedef enum {
  * nearest to w / s, decided exactly, ties to the lower code.  Codes two per
  * byte as for 4-bit integers; `zeros` is written with +0.0 (NF4 has no zero
  * point).  Multiply with wq_gemm_nf4, not wq_gemm.
+ *
+ * WQ_SCHEME_OFFSET ("Quantization & inference optimisation", section
+ * "Quantization", the affine per-group code): s as for WQ_SCHEME_ASYM, the
+ * group's minimum m written to `zeros` (fp16, exact), codes
+ * round-half-even((x - m) / s) clamped to [0, 2^bits - 1], decided exactly;
+ * x_hat = q * s + m.  Any bits 2..8.  Multiply with wq_gemm_offset.
  */
 wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group,
                               int32_t bits, int32_t scheme, void* codes, void* scales,
@@ -176,6 +183,21 @@ wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales,
  */
 wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B,
                       int64_t K, int64_t N, int32_t group, void* stream);
+
+/*
+ * Product with float-offset weights (codes, scales and minima from
+ * wq_quantize_pack_ex with WQ_SCHEME_OFFSET; "Quantization & inference
+ * optimisation", section "Quantization"):
+ *     Y[b, n] = sum_k X[b, k] * (q[n, k] * scales[n, k/group] + mins[n, k/group])
+ * fp32 accumulation, Y rounded once to fp16.  bits 2, 3, 4 or 8 (others
+ * WQ_ERR_UNSUPPORTED); group % 32 == 0; K % 64 (bits 2), % 128 (bits 3) or
+ * % 32 (bits 4, 8); K <= 16384 (32768 at bits 3).  Layout and alignment as
+ * wq_gemm, `mins` in place of `zeros`.  VALU bit-stream kernel, any B (codes
+ * are streamed once per four batch rows).
+ */
+wq_status wq_gemm_offset(const void* X, const void* codes, const void* scales, const void* mins,
+                         void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                         void* stream);
 
 /* The arguments of one wq_gemm call, for wq_gemm_grouped. */
 typedef struct wq_gemm_item {
@@ -293,7 +315,7 @@ const char* wq_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int32_t wq_version(void);
 
-#define WQ_VERSION 104
+#define WQ_VERSION 105
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = wq.load()
-    assert lib.wq_version() == 104
+    assert lib.wq_version() == 105
     for st in range(5):
         assert lib.wq_status_string(st)
     assert lib.wq_status_string(99) == b"unknown status"
@@ -115,7 +115,7 @@ def test_quantize_ex_validation_errors():
         assert _quant_ex(scheme, bits=1) == _lib.WQ_ERR_UNSUPPORTED
         assert _quant_ex(scheme, W=0) == _lib.WQ_ERR_INVALID_ARG
         assert _quant_ex(scheme, W=FAKE + 2) == _lib.WQ_ERR_MISALIGNED
-    assert _quant_ex(4) == _lib.WQ_ERR_INVALID_ARG
+    assert _quant_ex(5) == _lib.WQ_ERR_INVALID_ARG
     assert _quant_ex(-1) == _lib.WQ_ERR_INVALID_ARG
     assert b"scheme" in wq.load().wq_last_error()
 
@@ -189,4 +189,19 @@ def test_nf4_validation_errors():
     assert g(X=FAKE + 8) == _lib.WQ_ERR_MISALIGNED
     assert g(B=0, X=0, Y=0) == _lib.WQ_OK
     assert _quant_ex(_lib.WQ_SCHEME_NF4, bits=3) == _lib.WQ_ERR_UNSUPPORTED
-    assert _quant_ex(_lib.WQ_SCHEME_NF4 + 1) == _lib.WQ_ERR_INVALID_ARG
+    assert _quant_ex(_lib.WQ_SCHEME_OFFSET + 1) == _lib.WQ_ERR_INVALID_ARG
+
+
+def test_offset_gemm_validation_errors():
+    lib = wq.load()
+    g = lambda **kw: lib.wq_gemm_offset(kw.get("X", FAKE), FAKE, FAKE, kw.get("M", FAKE), kw.get("Y", FAKE),
+                                        kw.get("B", 2), kw.get("K", 256), 64, kw.get("group", 64),
+                                        kw.get("bits", 4), None)
+    assert g(bits=5) == _lib.WQ_ERR_UNSUPPORTED
+    assert g(bits=0) == _lib.WQ_ERR_INVALID_ARG
+    assert g(group=16) == _lib.WQ_ERR_UNSUPPORTED
+    assert g(bits=3, K=192, group=64) == _lib.WQ_ERR_UNSUPPORTED
+    assert g(K=250) == _lib.WQ_ERR_INVALID_ARG
+    assert g(M=0) == _lib.WQ_ERR_INVALID_ARG
+    assert g(M=FAKE + 1) == _lib.WQ_ERR_MISALIGNED
+    assert g(B=0, X=0, Y=0) == _lib.WQ_OK
