@@ -53,9 +53,10 @@ def parse():
     p.add_argument("--kv", action="store_true",
                    help="decode attention over an int4 KV cache, 1024 heads x 4096 tokens "
                         "(a 7B-class model's whole cache; table line)")
-    p.add_argument("--nf4", action="store_true",
-                   help="NF4 weights (block 64) on the step's workload: quantize + GEMV at "
-                        "--batches (default 1) (table line)")
+    p.add_argument("--format", choices=["nf4", "offset"], default=None,
+                   help="another weight format on the step's workload: NF4 at blocks of 64, or "
+                        "the float-offset variant at the workload's group and --bits; quantize + "
+                        "GEMV at --batches (default 1) (table line)")
     p.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
     p.add_argument("--bits", type=int, default=0,
                    help="code width of the step (default: the workload's, 4); 2 and 3 take "
@@ -627,11 +628,13 @@ def run_kv(args):
     return row
 
 
-def run_nf4(args):
-    """NF4 at blocks of 64 (the block the NF4 paragraph of "Gör inference
-    billig" uses) on the step's workload: GPU quantize and the level-table
-    GEMV, each timed as a burst of launches rotating over >= 1 GiB of
-    packed copies."""
+def run_format(args):
+    """Another weight format on the step's workload: NF4 at blocks of 64 (the
+    block the NF4 paragraph of "Gör inference billig" uses), or the
+    float-offset variant of "Quantization & inference optimisation"
+    ("Quantization") at the workload's group.  GPU quantize and the format's
+    GEMV, each timed as a burst of launches rotating over >= 1 GiB of packed
+    copies."""
     import torch
 
     import bit_weight_only_wq_amd as wq
@@ -639,15 +642,25 @@ def run_nf4(args):
     from bit_weight_only_wq_amd import roofline as rl
 
     cfg = wq_inputs.WORKLOADS[args.workload]
-    N, K, G = cfg["N"], cfg["K"], 64
+    fmt = args.format
+    N, K = cfg["N"], cfg["K"]
+    G = 64 if fmt == "nf4" else cfg["group"]
+    bits = 4 if fmt == "nf4" else (args.bits or cfg["bits"])
     batches = [int(b) for b in args.batches.split(",")] if args.batches else [1]
     Wn, Xn = wq_inputs.workload_arrays(args.workload)
     W = torch.from_numpy(Wn).cuda()
     X = torch.from_numpy(Xn).cuda()
-    packed = N * K // 2 + 2 * N * (K // G)            # codes + one fp16 scale per block
+    hdr = 2 if fmt == "nf4" else 4                    # fp16 scale (+ fp16 minimum) per group
+    packed = N * K * bits // 8 + hdr * N * (K // G)
     P = max(3, -(-POOL_BYTES // packed))
-    pool = [wq.quantize_pack(W, G, 4, scheme="nf4")[:2] for _ in range(P)]
+    pool = [wq.quantize_pack(W, G, bits, scheme=fmt) for _ in range(P)]
     stream = torch.cuda.current_stream()
+
+    def product(Xb, slot, Y):
+        c, s, m = slot
+        if fmt == "nf4":
+            return wq.gemm_nf4(Xb, c, s, N=N, K=K, group=G, out=Y)
+        return wq.gemm_offset(Xb, c, s, m, N=N, K=K, group=G, bits=bits, out=Y)
 
     def burst(fn, reps):
         for i in range(3):
@@ -666,21 +679,20 @@ def run_nf4(args):
     for B in batches:
         Xb = X[:B].contiguous()
         Y = torch.empty((B, N), dtype=torch.float16, device="cuda")
-        ms = burst(lambda i: wq.gemm_nf4(Xb, *pool[i % P], N=N, K=K, group=G, out=Y), args.steps)
+        ms = burst(lambda i: product(Xb, pool[i % P], Y), args.steps)
         nbytes = packed + 2 * B * K + 2 * B * N
-        kernels[f"wq_gemm_nf4_B{B}"] = {"avg_us": round(ms * 1e3, 2), "bytes": nbytes,
-                                        "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
-    outs = [(torch.empty_like(pool[0][0]), torch.empty_like(pool[0][1]),
-             torch.empty((N, K // G), dtype=torch.float16, device="cuda")) for _ in range(2)]
-    ms_q = burst(lambda i: wq.quantize_pack(W, G, 4, out=outs[i % 2], scheme="nf4"), args.steps)
+        kernels[f"wq_gemm_{fmt}_B{B}"] = {"avg_us": round(ms * 1e3, 2), "bytes": nbytes,
+                                          "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    outs = [tuple(torch.empty_like(t) for t in pool[0]) for _ in range(2)]
+    ms_q = burst(lambda i: wq.quantize_pack(W, G, bits, out=outs[i % 2], scheme=fmt), args.steps)
     qb = 2 * N * K + packed
-    kernels["wq_quantize_pack_nf4"] = {"avg_us": round(ms_q * 1e3, 2), "bytes": qb,
-                                       "achieved_GBps": round(qb / (ms_q * 1e-3) / 1e9, 1)}
-    head = kernels[f"wq_gemm_nf4_B{batches[0]}"]
-    row = {"metric": "NF4 decode GEMV, achieved HBM GB/s", "value": head["achieved_GBps"], "unit": "GB/s",
+    kernels[f"wq_quantize_pack_{fmt}"] = {"avg_us": round(ms_q * 1e3, 2), "bytes": qb,
+                                          "achieved_GBps": round(qb / (ms_q * 1e-3) / 1e9, 1)}
+    head = kernels[f"wq_gemm_{fmt}_B{batches[0]}"]
+    row = {"metric": f"{fmt} decode GEMV, achieved HBM GB/s", "value": head["achieved_GBps"], "unit": "GB/s",
            "n_gpus": 1, "steps": args.steps, "ms_per_step": round(head["avg_us"] / 1e3, 5),
            "higher_is_better": True, "dtype": "f16", "data": "synthetic",
-           "config": {"workload": args.workload, "N": N, "K": K, "group": G, "format": "nf4",
+           "config": {"workload": args.workload, "N": N, "K": K, "group": G, "bits": bits, "format": fmt,
                       "batches": batches},
            "roofline": {"bound": "hbm", "achieved": head["achieved_GBps"],
                         "peak": rl.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
@@ -709,8 +721,8 @@ def main():
         run_kv(args)
         calibration_copy(args)
         return
-    if args.nf4:
-        run_nf4(args)
+    if args.format:
+        run_format(args)
         return
     out, batches = run_step_bench(args)
     calibration_copy(args)
