@@ -201,8 +201,14 @@ __global__ __launch_bounds__(256, (BT == 64 && RB == 2) ? 3 : 1) void gemm_mfma_
             const int v = tid + 256 * u;
             const int col = v / SEGS, seg = v % SEGS;
             const int64_t k = st * KS + seg * 8;
-            const uint4 x = (b0 + col < B && k < K && st < st_end) ? xr[u] : uint4{0u, 0u, 0u, 0u};
-            if (v < NVEC) *reinterpret_cast<uint4*>(&xs[buf][col][seg * 8]) = permute8<BITS>(x);
+            // Zero by an opaque mask, not a select: a select of loaded data
+            // lets the compiler move the load into a branch at this point,
+            // after the code loads of later stages, and wait for all of them.
+            uint32_t m = (b0 + col < B && k < K && st < st_end) ? 0xFFFFFFFFu : 0u;
+            asm volatile("" : "+v"(m));
+            const uint4 x = {xr[u].x & m, xr[u].y & m, xr[u].z & m, xr[u].w & m};
+            if (NVEC % 256 == 0 || v < NVEC)
+                *reinterpret_cast<uint4*>(&xs[buf][col][seg * 8]) = permute8<BITS>(x);
         }
         if (!HV && tid < BR * RPS) hdr[buf][tid / BR][tid % BR] = hs | (hz << 16);
     };
@@ -290,6 +296,10 @@ __global__ __launch_bounds__(256, (BT == 64 && RB == 2) ? 3 : 1) void gemm_mfma_
             load_x(st + k + 1, xr);
             load_hdr(st + k + 1, hs, hz);
             load_codes(st + k + 2, cr[(k + 2) & 3]);
+            // Keep the next stage's loads ahead of this stage's math: left to
+            // itself the scheduler sinks them to their use and the X tile's
+            // latency is paid in full every stage.
+            __builtin_amdgcn_sched_barrier(0);
             compute(k & 1, cr[k & 3], k % STT);
             store_stage(st + k + 1, (k & 1) ^ 1, xr, hs, hz);
             __syncthreads();

@@ -9,6 +9,12 @@
 // (k even, k odd: X in its natural order).  The scale enters once per
 // 32-code chunk in fp32: sum_k x_k level[q_k] s = s * sum_k x_k level[q_k].
 //
+// Code bytes are random, so one shared table puts several lanes of a wave on
+// one LDS bank with different addresses.  The table is therefore replicated
+// NCP times, interleaved by entry (entry b of copy c at word b * NCP + c),
+// and lane l reads copy l % NCP: with NCP = 32 every lane of a 32-lane LDS
+// cycle owns its bank.  Larger X tiles (NB = 4) keep fewer copies.
+//
 // Same plan as the other GEMVs: persistent blocks stream 16-byte code chunks
 // non-temporally, X staged once per block in LDS, fp32 accumulation, row sums
 // across the TG lanes of a row by DPP.
@@ -20,8 +26,11 @@ namespace wq {
 
 namespace {
 
-constexpr size_t kNf4LutBytes = 256 * sizeof(uint32_t);
 constexpr size_t kNf4MaxLds = 64 * 1024;
+
+// Table copies per X tile height, and the table's LDS bytes.
+constexpr int nf4_copies(int nb) { return nb == 1 ? 32 : 8; }
+constexpr size_t nf4_lut_bytes(int nb) { return (size_t)256 * nf4_copies(nb) * sizeof(uint32_t); }
 
 // Grid: (persistent row-pass blocks, ceil(B / NB)).  TG threads per row,
 // 256 / TG rows per pass; thread tl owns chunks tl, tl + TG, ... (CPT).
@@ -31,9 +40,10 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(
     const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int64_t B, int64_t N,
     int64_t K, int32_t G) {
     constexpr int RPB = 256 / TG;
+    constexpr int NCP = nf4_copies(NB);
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t* lut = reinterpret_cast<uint32_t*>(smem);
-    uint4* xs = reinterpret_cast<uint4*>(smem + kNf4LutBytes);   // [NB][K/8] uint4
+    uint4* xs = reinterpret_cast<uint4*>(smem + nf4_lut_bytes(NB));   // [NB][K/8] uint4
 
     const int tid = threadIdx.x;
     const int rs = tid / TG;
@@ -44,7 +54,11 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(
     const int nb = (int)((B - b0) < NB ? (B - b0) : NB);
     const int64_t passes = (N + RPB - 1) / RPB;
 
-    lut[tid] = (uint32_t)kNf4LevelBits[tid & 15] | ((uint32_t)kNf4LevelBits[tid >> 4] << 16);
+    for (int e = tid; e < 256 * NCP; e += 256) {
+        const int b = e / NCP;
+        lut[e] = (uint32_t)kNf4LevelBits[b & 15] | ((uint32_t)kNf4LevelBits[b >> 4] << 16);
+    }
+    const uint32_t* lutl = lut + (tid % NCP);  // this lane's copy
     const int xw = (int)(K / 8);               // uint4 per X row
     for (int e = tid; e < NB * xw; e += 256) {
         const int b = e / xw, c = e % xw;
@@ -87,7 +101,7 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) pr[4 * j + k] = lut[(ww[j] >> (8 * k)) & 0xFFu];
+                for (int k = 0; k < 4; ++k) pr[4 * j + k] = lutl[((ww[j] >> (8 * k)) & 0xFFu) * NCP];
             const float s = (row_ok && cin[i]) ? half_bits_to_float((uint16_t)hs[i]) : 0.0f;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
@@ -122,8 +136,8 @@ bool nf4_choose(int64_t B, int64_t K, int32_t G, Nf4Choice& ch) {
     if (K % 32 != 0 || G % 32 != 0) return false;
     const int64_t C = K / 32;
     const size_t row = (size_t)K * 2;
-    ch.nb = B >= 2 && kNf4LutBytes + 4 * row <= kNf4MaxLds ? 4 : 1;
-    if (kNf4LutBytes + ch.nb * row > kNf4MaxLds) return false;
+    ch.nb = B >= 2 && nf4_lut_bytes(4) + 4 * row <= kNf4MaxLds ? 4 : 1;
+    if (nf4_lut_bytes(ch.nb) + ch.nb * row > kNf4MaxLds) return false;
     if (C <= 16) ch.tg = 16, ch.cpt = 1;
     else if (C <= 32) ch.tg = 16, ch.cpt = 2;
     else if (C <= 64) ch.tg = 64, ch.cpt = 1;
@@ -138,7 +152,7 @@ template <int NB, int TG, int CPT>
 hipError_t nf4_launch(const void* X, const void* codes, const void* scales, void* Y, int64_t B,
                       int64_t K, int64_t N, int32_t G, int num_cus, hipStream_t stream) {
     constexpr int RPB = 256 / TG;
-    const size_t lds = kNf4LutBytes + (size_t)NB * K * 2;
+    const size_t lds = nf4_lut_bytes(NB) + (size_t)NB * K * 2;
     static thread_local size_t cached_lds = (size_t)-1;
     static thread_local int cached_per_cu = 1;
     if (cached_lds != lds) {
