@@ -75,17 +75,20 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(
         cidx[i] = c < C ? c : C - 1;
     }
 
-    for (int64_t pass = blockIdx.x; pass < passes; pass += gridDim.x) {
+    // Codes and scales of a pass; rows past N read row N - 1 (their result
+    // is dropped), so every pass issues the same loads.
+    auto load_pass = [&](int64_t pass, uint4* w, uint32_t* hs) {
         int64_t n = pass * RPB + rs;
-        const bool row_ok = n < N;
-        n = row_ok ? n : N - 1;
-        uint4 w[CPT];
-        uint32_t hs[CPT];
+        n = n < N ? n : N - 1;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             w[i] = load_stream(codes + n * C + cidx[i]);
             hs[i] = scales[n * ngrp + ((int64_t)cidx[i] * 32) / G];
         }
+    };
+    auto compute_pass = [&](int64_t pass, const uint4* w, const uint32_t* hs) {
+        const int64_t n = pass * RPB + rs;
+        const bool row_ok = n < N;
         float acc[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
@@ -125,6 +128,20 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(
             for (int b = 0; b < NB; ++b)
                 if (b < nb) Y[(b0 + b) * N + n] = float_to_half_bits_rne(acc[b]);
         }
+    };
+
+    // Ping-pong: the next pass's loads are in flight while this pass computes.
+    const int64_t step = gridDim.x;
+    uint4 wa[CPT], wb[CPT];
+    uint32_t ha[CPT], hb[CPT];
+    int64_t pass = blockIdx.x;
+    load_pass(pass, wa, ha);
+    for (; pass < passes; pass += 2 * step) {
+        load_pass(pass + step, wb, hb);
+        compute_pass(pass, wa, ha);
+        if (pass + step >= passes) break;
+        load_pass(pass + 2 * step, wa, ha);
+        compute_pass(pass + step, wb, hb);
     }
 }
 

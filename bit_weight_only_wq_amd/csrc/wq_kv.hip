@@ -239,13 +239,18 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
         o1 += group_sum<4>(chunk_dot_hl(b.v1, vhq, vlq, m_lo, m_hi)) - CV;
     };
 
+    // Prefetches are unconditional (the index clamps to the split's last
+    // block, which was just read), so the count of loads in flight is the
+    // same on every path and the waits for a block's data leave the next
+    // block's loads outstanding.
     Blk A = {}, B = {};
+    const int jl = j1 - 1;
     if (j0 < j1) load_blk(j0, A);
     for (int j = j0; j < j1; j += 2) {
-        if (j + 1 < j1) load_blk(j + 1, B);
+        load_blk(j + 1 < jl ? j + 1 : jl, B);
         process(A);
         if (j + 1 >= j1) break;
-        if (j + 2 < j1) load_blk(j + 2, A);
+        load_blk(j + 2 < jl ? j + 2 : jl, A);
         process(B);
     }
 
