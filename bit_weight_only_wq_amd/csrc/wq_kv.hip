@@ -166,8 +166,11 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
     // One block's loads for this thread: its four 16-byte code chunks, the K
     // header of channel tid % 128 and the V headers of its two tokens.  Every
     // lane issues the same ten loads in the order they are consumed (lanes
-    // that do not use a header still load it), so the compiler can count the
-    // next block's loads in flight and wait only for the current block's.
+    // that do not use a header still load it), so the K side's waits leave
+    // the next block's loads in flight.  The prefetch is conditional (no
+    // block past the split is read), so the V side's header waits drain them;
+    // an unconditional, clamped prefetch kept them in flight but measured no
+    // faster and re-read one block per split.
     struct Blk {
         uint4 k0, k1, v0, v1;
         uint32_t ks, kz, vs0, vs1, vz0, vz1;
@@ -239,18 +242,13 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(const uint16_t* __restrict
         o1 += group_sum<4>(chunk_dot_hl(b.v1, vhq, vlq, m_lo, m_hi)) - CV;
     };
 
-    // Prefetches are unconditional (the index clamps to the split's last
-    // block, which was just read), so the count of loads in flight is the
-    // same on every path and the waits for a block's data leave the next
-    // block's loads outstanding.
     Blk A = {}, B = {};
-    const int jl = j1 - 1;
     if (j0 < j1) load_blk(j0, A);
     for (int j = j0; j < j1; j += 2) {
-        load_blk(j + 1 < jl ? j + 1 : jl, B);
+        if (j + 1 < j1) load_blk(j + 1, B);
         process(A);
         if (j + 1 >= j1) break;
-        load_blk(j + 2 < jl ? j + 2 : jl, A);
+        if (j + 2 < j1) load_blk(j + 2, A);
         process(B);
     }
 
