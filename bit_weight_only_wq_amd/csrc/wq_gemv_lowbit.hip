@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256) void gemv_lowbit_kernel(
     }
 }
 
-constexpr size_t kLowMaxLds = 64 * 1024;
+constexpr size_t kLowMaxLds = 128 * 1024;   // of the 160 KB a gfx950 workgroup may hold
 
 struct LowChoice {
     int nb, tg, cpt, hpu;

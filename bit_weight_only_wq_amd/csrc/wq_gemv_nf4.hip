@@ -26,7 +26,7 @@ namespace wq {
 
 namespace {
 
-constexpr size_t kNf4MaxLds = 64 * 1024;
+constexpr size_t kNf4MaxLds = 128 * 1024;   // of the 160 KB a gfx950 workgroup may hold
 
 // Table copies per X tile height, and the table's LDS bytes.
 constexpr int nf4_copies(int nb) { return nb == 1 ? 32 : 8; }
