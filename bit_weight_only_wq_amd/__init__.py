@@ -253,3 +253,23 @@ def gemm_offset(X, codes, scales, mins, N: int, K: int, group: int = 128, bits: 
                                    out.data_ptr(), B, K, N, group, bits, _stream_handle(X.device))
     check(st, "wq_gemm_offset")
     return out
+
+
+def dequantize(codes, scales, zeros, N: int, K: int, group: int = 128, bits: int = 4,
+               scheme: str = "asym", out=None):
+    """fp32 [N, K] weights reconstructed from quantize_pack(..., scheme) output
+    (a test aid: the products reconstruct in registers)."""
+    import torch
+    if scheme not in SCHEMES:
+        raise ValueError(f"unknown scheme {scheme!r}")
+    _need(codes, torch.uint8, (N, K * bits // 8), "codes")
+    _need(scales, torch.float16, (N, K // group), "scales")
+    _need(zeros, torch.float16, (N, K // group), "zeros")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=codes.device)
+    _need(out, torch.float32, (N, K), "out")
+    with torch.cuda.device(codes.device):
+        st = load().wq_dequantize(codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, group,
+                                  bits, SCHEMES[scheme], out.data_ptr(), _stream_handle(codes.device))
+    check(st, "wq_dequantize")
+    return out

@@ -53,6 +53,7 @@ SIGNATURES = {
     "wq_kv_attention": (ctypes.c_int, [_P, ctypes.POINTER(KvCache), _P, _P, _P]),
     "wq_gemm_nf4": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "wq_gemm_offset": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P]),
+    "wq_dequantize": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P]),
     "wq_gemv_max_batch": (_I32, []),
     "wq_codes_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
     "wq_num_groups": (_I64, [_I64, _I64, _I32]),

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libwq.so")
-SOURCES = ["wq_api.hip", "wq_quantize.hip", "wq_gemv.hip", "wq_gemv_lowbit.hip", "wq_gemv_nf4.hip", "wq_gemm_mfma.hip", "wq_gemm_xr.hip", "wq_kv.hip", "wq_workspace.hip"]
+SOURCES = ["wq_api.hip", "wq_quantize.hip", "wq_gemv.hip", "wq_gemv_lowbit.hip", "wq_gemv_nf4.hip", "wq_gemm_mfma.hip", "wq_gemm_xr.hip", "wq_kv.hip", "wq_dequant.hip", "wq_workspace.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -107,6 +107,31 @@ wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, i
                                stream);
 }
 
+wq_status wq_dequantize(const void* codes, const void* scales, const void* zeros, int64_t N,
+                        int64_t K, int32_t group, int32_t bits, int32_t scheme, void* W,
+                        void* stream) {
+    g_last_error[0] = '\0';
+    if (N < 0 || K < 1 || group < 1)
+        return fail(WQ_ERR_INVALID_ARG, "wq_dequantize: need N >= 0, K >= 1, group >= 1 (N=%lld K=%lld)", N, K);
+    if (K % group != 0)
+        return fail(WQ_ERR_INVALID_ARG, "wq_dequantize: K=%lld is not a multiple of group=%lld", K, group);
+    if (scheme < WQ_SCHEME_ASYM || scheme > WQ_SCHEME_OFFSET)
+        return fail(WQ_ERR_INVALID_ARG, "wq_dequantize: unknown scheme %lld", scheme);
+    if (bits < 2 || bits > 8)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_dequantize: the codec takes bits 2..8 (got %lld)", bits);
+    if (scheme == WQ_SCHEME_NF4 && bits != 4)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_dequantize: NF4 codes are 4 bits (got %lld)", bits);
+    if (group % 8 != 0)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_dequantize: group=%lld must be a multiple of 8", group);
+    if (N == 0) return WQ_OK;
+    if (!codes || !scales || !zeros || !W) return fail(WQ_ERR_INVALID_ARG, "wq_dequantize: null pointer");
+    if (!aligned(W, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
+        return fail(WQ_ERR_MISALIGNED, "wq_dequantize: W needs 16-byte alignment");
+    return check_hip(wq::launch_dequantize(codes, scales, zeros, W, N, K, group, bits, scheme,
+                                           static_cast<hipStream_t>(stream)),
+                     "wq_dequantize launch");
+}
+
 // Validates one product and picks its kernel family (path on return); does
 // not enqueue anything.  A no-op product (B == 0 or N == 0) returns WQ_OK with
 // path = -1.

@@ -12,6 +12,11 @@ hipError_t launch_quantize_pack(const void* W, int64_t N, int64_t K, int32_t gro
                                 int32_t bits, int32_t scheme, void* codes, void* scales,
                                 void* zeros, hipStream_t stream);
 
+// Codes + headers -> fp32 W [N, K] for any scheme (see wq_dequant.hip).
+hipError_t launch_dequantize(const void* codes, const void* scales, const void* zeros, void* W,
+                             int64_t N, int64_t K, int32_t group, int32_t bits, int32_t scheme,
+                             hipStream_t stream);
+
 // GEMV family: returns hipErrorInvalidValue when the shape is outside what the
 // instantiated tilings cover (the caller maps that to WQ_ERR_UNSUPPORTED).
 bool gemv_supports(int64_t K, int32_t bits);

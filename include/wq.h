@@ -237,6 +237,29 @@ wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream
  * can take the shape. */
 int32_t wq_gemv_max_batch(void);
 
+/*
+ * Reconstruction of the weights from codes and headers, written out as fp32
+ * (a test aid, not the hot path: the products reconstruct in registers).
+ * "Quantization & inference optimisation", "Quantization": the integer and
+ * the group's endpoints give back an approximate float.
+ *     schemes 0-2:  W[n, k] = (q - zeros[g]) * scales[g]
+ *     NF4 (3):      W[n, k] = level[q] * scales[g]        (bits 4; zeros unused)
+ *     offset (4):   W[n, k] = q * scales[g] + zeros[g]    (zeros holds the minimum)
+ * with g = n * (K / group) + k / group, each value rounded once to fp32 (the
+ * first two forms are exact).
+ *
+ * codes, scales, zeros   as written by wq_quantize_pack_ex with the same
+ *                        group, bits and scheme (caller-owned device memory)
+ * W       fp32 [N, K]    output, 16-byte aligned
+ * N >= 0 (0 is a no-op), K >= 1, K % group == 0, group % 8 == 0, bits 2..8.
+ * Errors: WQ_ERR_INVALID_ARG (shape, unknown scheme, null pointer),
+ * WQ_ERR_UNSUPPORTED (bits outside 2..8, NF4 with bits != 4, group not a
+ * multiple of 8), WQ_ERR_MISALIGNED, WQ_ERR_HIP.  Enqueued on `stream`.
+ */
+wq_status wq_dequantize(const void* codes, const void* scales, const void* zeros, int64_t N,
+                        int64_t K, int32_t group, int32_t bits, int32_t scheme, void* W,
+                        void* stream);
+
 /* Bytes of the codes array: N * K * bits / 8 (0 on invalid input). */
 size_t wq_codes_bytes(int64_t N, int64_t K, int32_t bits);
 
@@ -315,7 +338,7 @@ const char* wq_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int32_t wq_version(void);
 
-#define WQ_VERSION 105
+#define WQ_VERSION 106
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = wq.load()
-    assert lib.wq_version() == 105
+    assert lib.wq_version() == 106
     for st in range(5):
         assert lib.wq_status_string(st)
     assert lib.wq_status_string(99) == b"unknown status"
@@ -205,3 +205,27 @@ def test_offset_gemm_validation_errors():
     assert g(M=0) == _lib.WQ_ERR_INVALID_ARG
     assert g(M=FAKE + 1) == _lib.WQ_ERR_MISALIGNED
     assert g(B=0, X=0, Y=0) == _lib.WQ_OK
+
+
+def _deq(scheme=0, N=64, K=256, group=128, bits=4, C=FAKE, S=FAKE, Z=FAKE, W=FAKE):
+    return wq.load().wq_dequantize(C, S, Z, N, K, group, bits, scheme, W, None)
+
+
+def test_dequantize_validation_errors():
+    """Every call here fails validation (or is the N = 0 no-op), so the fake
+    pointers are never used."""
+    for scheme in range(5):
+        assert _deq(scheme, N=0, C=0, S=0, Z=0, W=0) == _lib.WQ_OK
+        assert _deq(scheme, K=250) == _lib.WQ_ERR_INVALID_ARG
+        assert _deq(scheme, N=-1) == _lib.WQ_ERR_INVALID_ARG
+        assert _deq(scheme, bits=1) == _lib.WQ_ERR_UNSUPPORTED
+        assert _deq(scheme, bits=9) == _lib.WQ_ERR_UNSUPPORTED
+        assert _deq(scheme, group=4, K=256) == _lib.WQ_ERR_UNSUPPORTED
+        assert _deq(scheme, C=0) == _lib.WQ_ERR_INVALID_ARG
+        assert _deq(scheme, W=0) == _lib.WQ_ERR_INVALID_ARG
+        assert _deq(scheme, W=FAKE + 4) == _lib.WQ_ERR_MISALIGNED
+        assert _deq(scheme, S=FAKE + 1) == _lib.WQ_ERR_MISALIGNED
+    assert _deq(5) == _lib.WQ_ERR_INVALID_ARG
+    assert _deq(-1) == _lib.WQ_ERR_INVALID_ARG
+    assert _deq(_lib.WQ_SCHEME_NF4, bits=3) == _lib.WQ_ERR_UNSUPPORTED
+    assert b"wq_dequantize" in wq.load().wq_last_error()
