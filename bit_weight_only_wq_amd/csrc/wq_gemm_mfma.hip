@@ -339,6 +339,25 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     Y[i] = float_to_half_bits_rne(s);
 }
 
+// The same sums four outputs per thread (count % 4 == 0, Y 8-byte aligned):
+// 16-byte partial loads and one 8-byte store.
+__global__ __launch_bounds__(256) void split_reduce4_kernel(const float4* __restrict__ part,
+                                                            uint2* __restrict__ Y,
+                                                            int64_t count4, int splits) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count4) return;
+    float4 s = part[i];
+    for (int z = 1; z < splits; ++z) {
+        const float4 v = part[(int64_t)z * count4 + i];
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    Y[i] = make_uint2((uint32_t)float_to_half_bits_rne(s.x) | ((uint32_t)float_to_half_bits_rne(s.y) << 16),
+                      (uint32_t)float_to_half_bits_rne(s.z) | ((uint32_t)float_to_half_bits_rne(s.w) << 16));
+}
+
 template <int BITS, int BT, int KS, int RB>
 hipError_t launch_bt(const void* X, const void* codes, const void* scales, const void* zeros,
                      void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int num_cus,
@@ -379,8 +398,14 @@ hipError_t launch_bt(const void* X, const void* codes, const void* scales, const
     hipError_t e = hipGetLastError();
     if (splits > 1 && e == hipSuccess) {
         const int64_t count = B * N;
-        split_reduce_kernel<<<dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream>>>(
-            part, static_cast<uint16_t*>(Y), count, (int)splits);
+        if (count % 4 == 0 && reinterpret_cast<uintptr_t>(Y) % 8 == 0) {
+            const int64_t count4 = count / 4;
+            split_reduce4_kernel<<<dim3((unsigned)((count4 + 255) / 256)), dim3(256), 0, stream>>>(
+                reinterpret_cast<const float4*>(part), static_cast<uint2*>(Y), count4, (int)splits);
+        } else {
+            split_reduce_kernel<<<dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream>>>(
+                part, static_cast<uint16_t*>(Y), count, (int)splits);
+        }
         e = hipGetLastError();
     }
     return e;

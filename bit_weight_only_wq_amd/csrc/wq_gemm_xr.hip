@@ -102,6 +102,7 @@ struct XrReduceItem {
     int64_t count;        // B * N
     int64_t t0;
     int32_t slices;
+    int32_t vec;          // count % 4 == 0 and Y 8-byte aligned: 16-byte partial loads
 };
 
 struct XrReduce {
@@ -465,18 +466,37 @@ __global__ __launch_bounds__(xr_waves(BTX) * 64) void gemm_xr_kernel(const XrLau
 // Y = fp16(sum over slices of part[z]), slices added in order 0, 1, 2, ...,
 // for every product of the table (one flat index space over their outputs).
 __global__ __launch_bounds__(256) void xr_reduce_kernel(const XrReduce R) {
-    // Products start on 256-thread boundaries, so the product is uniform per block.
-    const int64_t g0 = (int64_t)blockIdx.x * 256;
+    // Each thread sums four consecutive outputs; products start on
+    // 1024-output boundaries, so the product is uniform per block.
+    const int64_t g0 = (int64_t)blockIdx.x * 1024;
     int item = 0;
 #pragma unroll
     for (int j = 1; j < XR_MAX_ITEMS; ++j)
         if (j < R.count && g0 >= R.it[j].t0) item = j;
     const XrReduceItem& P = R.it[item];
-    const int64_t i = g0 - P.t0 + threadIdx.x;
-    if (i >= P.count) return;
-    float s = P.part[i];
-    for (int z = 1; z < P.slices; ++z) s += P.part[(int64_t)z * P.count + i];
-    P.Y[i] = float_to_half_bits_rne(s);
+    const int64_t i0 = g0 - P.t0 + 4 * (int64_t)threadIdx.x;
+    if (i0 >= P.count) return;
+    if (P.vec) {
+        const float4* p4 = reinterpret_cast<const float4*>(P.part);
+        const int64_t c4 = P.count / 4, j = i0 / 4;
+        float4 s = p4[j];
+        for (int z = 1; z < P.slices; ++z) {
+            const float4 v = p4[(int64_t)z * c4 + j];
+            s.x += v.x;
+            s.y += v.y;
+            s.z += v.z;
+            s.w += v.w;
+        }
+        reinterpret_cast<uint2*>(P.Y)[j] =
+            make_uint2((uint32_t)float_to_half_bits_rne(s.x) | ((uint32_t)float_to_half_bits_rne(s.y) << 16),
+                       (uint32_t)float_to_half_bits_rne(s.z) | ((uint32_t)float_to_half_bits_rne(s.w) << 16));
+        return;
+    }
+    for (int e = 0; e < 4 && i0 + e < P.count; ++e) {
+        float s = P.part[i0 + e];
+        for (int z = 1; z < P.slices; ++z) s += P.part[(int64_t)z * P.count + i0 + e];
+        P.Y[i0 + e] = float_to_half_bits_rne(s);
+    }
 }
 
 // Slices, rounds per slice and blocks per slice of one product.  Slices: as
@@ -613,13 +633,14 @@ hipError_t launch_xr_items(const XrProduct* const* prods, int n, int64_t B, int 
             r.count = B * it.N;
             r.t0 = t;
             r.slices = it.slices;
-            t += (r.count + 255) / 256 * 256;
+            r.vec = r.count % 4 == 0 && reinterpret_cast<uintptr_t>(r.Y) % 8 == 0;
+            t += (r.count + 1023) / 1024 * 1024;
         }
     }
     gemm_xr_kernel<BITS, BTX, HM><<<dim3((unsigned)blocks), dim3(XG::WAVES * 64), 0, stream>>>(L);
     hipError_t e = hipGetLastError();
     if (R.count > 0 && e == hipSuccess) {
-        xr_reduce_kernel<<<dim3((unsigned)(t / 256)), dim3(256), 0, stream>>>(R);
+        xr_reduce_kernel<<<dim3((unsigned)(t / 1024)), dim3(256), 0, stream>>>(R);
         e = hipGetLastError();
     }
     return e;
