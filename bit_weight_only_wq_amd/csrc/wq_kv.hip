@@ -336,8 +336,8 @@ __global__ __launch_bounds__(128) void kv_combine_kernel(const float* __restrict
 }
 
 // ---- quantize-on-append ------------------------------------------------------
-// One workgroup per head: the head's block of G tokens of K and V (fp16,
-// token-major [G][D]) becomes block `block` of its cache.  K: min/max per
+// Two workgroups per head (K, V): the head's block of G tokens of K and V
+// (fp16, token-major [G][D]) becomes block `block` of its cache.  K: min/max per
 // channel over the G tokens; V: per token over the D channels; both with the
 // exact decisions of the weight quantizer.
 __device__ __forceinline__ uint32_t encode_one(float x, float s, float rcp, float Z) {
@@ -374,50 +374,54 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
     };
     auto at = [&](int t, int d) { return half_bits_to_float(tile[t * PAD + d]); };
 
-    // ---- K: one group per channel.
-    load_tile(K + (int64_t)h * kG * kD);
-    __syncthreads();
-    {
-        const int d = tid & (kD - 1), half = tid >> 7;
-        float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-        for (int t = half * 64; t < half * 64 + 64; ++t) {
-            const float x = at(t, d);
-            mn = __builtin_fminf(mn, x);
-            mx = __builtin_fmaxf(mx, x);
-        }
-        mnx[half][0][d] = mn;
-        mnx[half][1][d] = mx;
-    }
-    __syncthreads();
-    if (tid < kD) {
-        const GroupHeader g = make_header(__builtin_fminf(mnx[0][0][tid], mnx[1][0][tid]),
-                                          __builtin_fmaxf(mnx[0][1][tid], mnx[1][1][tid]), 15);
-        hs[tid] = g.s;
-        hr[tid] = g.rcp;
-        hzf[tid] = g.Z;
-        ks[blk * kD + tid] = g.sbits;
-        kz[blk * kD + tid] = g.zbits;
-    }
-    __syncthreads();
-    {
-        // Token t = tid / 2, channels [64 * (tid & 1), +64) -> 32 bytes of its row.
-        const int t = tid >> 1, c0 = (tid & 1) * 64;
-        uint32_t w[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const int d = c0 + 8 * i + n;
-                v |= encode_one(at(t, d), hs[d], hr[d], hzf[d]) << (4 * n);
+    // blockIdx.y 0: K, 1: V.  The two sides share no data, so they run as
+    // separate workgroups and their tile loads overlap.
+    if (blockIdx.y == 0) {
+        // ---- K: one group per channel.
+        load_tile(K + (int64_t)h * kG * kD);
+        __syncthreads();
+        {
+            const int d = tid & (kD - 1), half = tid >> 7;
+            float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+            for (int t = half * 64; t < half * 64 + 64; ++t) {
+                const float x = at(t, d);
+                mn = __builtin_fminf(mn, x);
+                mx = __builtin_fmaxf(mx, x);
             }
-            w[i] = v;
+            mnx[half][0][d] = mn;
+            mnx[half][1][d] = mx;
         }
-        uint4* dst = reinterpret_cast<uint4*>(kc + (blk * kG + t) * kRow + c0 / 2);
-        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        __syncthreads();
+        if (tid < kD) {
+            const GroupHeader g = make_header(__builtin_fminf(mnx[0][0][tid], mnx[1][0][tid]),
+                                              __builtin_fmaxf(mnx[0][1][tid], mnx[1][1][tid]), 15);
+            hs[tid] = g.s;
+            hr[tid] = g.rcp;
+            hzf[tid] = g.Z;
+            ks[blk * kD + tid] = g.sbits;
+            kz[blk * kD + tid] = g.zbits;
+        }
+        __syncthreads();
+        {
+            // Token t = tid / 2, channels [64 * (tid & 1), +64) -> 32 bytes of its row.
+            const int t = tid >> 1, c0 = (tid & 1) * 64;
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t v = 0;
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                    const int d = c0 + 8 * i + n;
+                    v |= encode_one(at(t, d), hs[d], hr[d], hzf[d]) << (4 * n);
+                }
+                w[i] = v;
+            }
+            uint4* dst = reinterpret_cast<uint4*>(kc + (blk * kG + t) * kRow + c0 / 2);
+            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+        return;
     }
-    __syncthreads();
 
     // ---- V: one group per token.
     load_tile(V + (int64_t)h * kG * kD);
@@ -503,7 +507,7 @@ hipError_t launch_kv_attention(const void* q, const KvCacheArgs& c, const int32_
 
 hipError_t launch_kv_quantize(const void* K, const void* V, const KvCacheArgs& c, int64_t block,
                               hipStream_t stream) {
-    kv_quantize_kernel<<<dim3((unsigned)c.heads), dim3(256), 0, stream>>>(
+    kv_quantize_kernel<<<dim3((unsigned)c.heads, 2), dim3(256), 0, stream>>>(
         static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), static_cast<uint8_t*>(c.kcodes),
         static_cast<uint16_t*>(c.kscales), static_cast<uint16_t*>(c.kzeros), static_cast<uint8_t*>(c.vcodes),
         static_cast<uint16_t*>(c.vscales), static_cast<uint16_t*>(c.vzeros), c.max_blocks, block);
