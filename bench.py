@@ -19,6 +19,7 @@ same step.
     python bench.py [--steps 20] [--warmup 5] [--no-cpu]
     python bench.py --sweep     # batch sweep across the ridge (K=N=8192), table only
     python bench.py --decode-set   # 7B-class decode step (224 products, B=32), table only
+    python bench.py --ceiling      # plain torch read / copy rates over 1 GiB (context), table only
 """
 
 from __future__ import annotations
@@ -57,6 +58,9 @@ def parse():
                    help="another weight format on the step's workload: NF4 at blocks of 64, or "
                         "the float-offset variant at the workload's group and --bits; quantize + "
                         "GEMV at --batches (default 1) (table line)")
+    p.add_argument("--ceiling", action="store_true",
+                   help="what plain torch kernels read and copy on this GPU over 1 GiB buffers "
+                        "(context for the roofline fractions; table line)")
     p.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
     p.add_argument("--bits", type=int, default=0,
                    help="code width of the step (default: the workload's, 4); 2 and 3 take "
@@ -711,6 +715,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.ceiling:
+        run_ceiling(args)
+        return
     if args.sweep:
         run_sweep(args)
         return
@@ -729,6 +736,47 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.workload, batches, args.bits)
     print(json.dumps(out), flush=True)
+
+
+def run_ceiling(args):
+    """Reachable HBM rates on this GPU for plain torch kernels, as context for
+    the roofline fractions (peak 8 TB/s): a float32-accumulating sum over a
+    1 GiB fp16 buffer (read only), a 1 GiB copy (read + write) and a 1 GiB
+    fill (write only).  Two source
+    buffers alternate, so no call finds its data in the 256 MB Infinity Cache."""
+    import torch
+    n = 1 << 29                                  # fp16 elements: 1 GiB
+    src = [torch.ones(n, dtype=torch.float16, device="cuda:0") for _ in range(2)]
+    dst = torch.empty(n, dtype=torch.float16, device="cuda:0")
+
+    def timed(fn, reps):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps      # us per call
+
+    reps = max(args.steps // 2, 5)
+    read_us = timed(lambda i: torch.sum(src[i % 2], dtype=torch.float32), reps)
+    copy_us = timed(lambda i: dst.copy_(src[i % 2]), reps)
+    write_us = timed(lambda i: dst.fill_(float(i % 3)), reps)
+    nbytes = n * 2
+    row = {"table": "hbm ceiling", "buffer_bytes": nbytes, "calls": reps,
+           "read": {"kernel": "torch.sum (fp16 -> fp32)", "us": round(read_us, 2),
+                    "GBps": round(nbytes / read_us / 1e3, 1)},
+           "copy": {"kernel": "Tensor.copy_", "us": round(copy_us, 2),
+                    "GBps": round(2 * nbytes / copy_us / 1e3, 1)},
+           "write": {"kernel": "Tensor.fill_", "us": round(write_us, 2),
+                     "GBps": round(nbytes / write_us / 1e3, 1)},
+           "peak_GBps": 8000.0}
+    print(json.dumps(row), flush=True)
+    return row
 
 
 def calibration_copy(args):
