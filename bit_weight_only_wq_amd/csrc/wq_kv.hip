@@ -336,8 +336,9 @@ __global__ __launch_bounds__(128) void kv_combine_kernel(const float* __restrict
 }
 
 // ---- quantize-on-append ------------------------------------------------------
-// Two workgroups per head (K, V): the head's block of G tokens of K and V
-// (fp16, token-major [G][D]) becomes block `block` of its cache.  K: min/max per
+// Eight workgroups per head (K by channel quarters, V by token quarters): the
+// head's block of G tokens of K and V (fp16, token-major [G][D]) becomes
+// block `block` of its cache.  K: min/max per
 // channel over the G tokens; V: per token over the D channels; both with the
 // exact decisions of the weight quantizer.
 __device__ __forceinline__ uint32_t encode_one(float x, float s, float rcp, float Z) {
@@ -352,18 +353,26 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
                                                           uint16_t* __restrict__ kz, uint8_t* __restrict__ vc,
                                                           uint16_t* __restrict__ vs, uint16_t* __restrict__ vz,
                                                           int64_t max_blocks, int64_t block) {
-    constexpr int PAD = kD + 2;                  // row stride in halves (4-byte aligned, breaks bank aliasing)
-    __shared__ uint16_t tile[kG * PAD];
-    __shared__ float hs[kD], hr[kD], hzf[kD];
-    __shared__ float mnx[2][2][kD];
+    // blockIdx.y = 4 * side + q.  Side 0 (K) takes channels [32q, 32q + 32)
+    // over all G tokens; side 1 (V) takes tokens [32q, 32q + 32) over all D
+    // channels.  Each group then lies inside one workgroup, which writes a
+    // 16-byte column of every code row it touches.
+    constexpr int Q = 32;                        // channels (K) or tokens (V) per workgroup
+    __shared__ uint16_t tile[kG * (Q + 2)];      // K: [G][Q + 2]; V: [Q][D + 2] (same size)
+    __shared__ float hs[Q], hr[Q], hzf[Q];
+    __shared__ float mnx[8][2][Q];
 
     const int h = blockIdx.x;
+    const int side = blockIdx.y >> 2, q = blockIdx.y & 3;
     const int tid = threadIdx.x;
     const int64_t blk = (int64_t)h * max_blocks + block;
 
-    auto load_tile = [&](const uint16_t* src) {
-        for (int i = tid; i < kG * (kD / 8); i += 256) {
-            const int t = i / (kD / 8), c = i % (kD / 8);
+    if (side == 0) {
+        // ---- K: one group per channel; this workgroup's 32 channels.
+        constexpr int PAD = Q + 2;
+        const uint16_t* src = K + (int64_t)h * kG * kD + Q * q;
+        for (int i = tid; i < kG * (Q / 8); i += 256) {
+            const int t = i / (Q / 8), c = i % (Q / 8);
             const uint4 u = reinterpret_cast<const uint4*>(src + (int64_t)t * kD)[c];
             uint32_t* dst = reinterpret_cast<uint32_t*>(tile + t * PAD + 8 * c);
             dst[0] = u.x;
@@ -371,99 +380,101 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
             dst[2] = u.z;
             dst[3] = u.w;
         }
-    };
-    auto at = [&](int t, int d) { return half_bits_to_float(tile[t * PAD + d]); };
-
-    // blockIdx.y 0: K, 1: V.  The two sides share no data, so they run as
-    // separate workgroups and their tile loads overlap.
-    if (blockIdx.y == 0) {
-        // ---- K: one group per channel.
-        load_tile(K + (int64_t)h * kG * kD);
         __syncthreads();
         {
-            const int d = tid & (kD - 1), half = tid >> 7;
+            const int c = tid & (Q - 1), part = tid >> 5;     // 8 parts of 16 tokens
             float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-            for (int t = half * 64; t < half * 64 + 64; ++t) {
-                const float x = at(t, d);
+            for (int t = part * 16; t < part * 16 + 16; ++t) {
+                const float x = half_bits_to_float(tile[t * PAD + c]);
                 mn = __builtin_fminf(mn, x);
                 mx = __builtin_fmaxf(mx, x);
             }
-            mnx[half][0][d] = mn;
-            mnx[half][1][d] = mx;
+            mnx[part][0][c] = mn;
+            mnx[part][1][c] = mx;
         }
         __syncthreads();
-        if (tid < kD) {
-            const GroupHeader g = make_header(__builtin_fminf(mnx[0][0][tid], mnx[1][0][tid]),
-                                              __builtin_fmaxf(mnx[0][1][tid], mnx[1][1][tid]), 15);
+        if (tid < Q) {
+            float mn = mnx[0][0][tid], mx = mnx[0][1][tid];
+#pragma unroll
+            for (int p2 = 1; p2 < 8; ++p2) {
+                mn = __builtin_fminf(mn, mnx[p2][0][tid]);
+                mx = __builtin_fmaxf(mx, mnx[p2][1][tid]);
+            }
+            const GroupHeader g = make_header(mn, mx, 15);
             hs[tid] = g.s;
             hr[tid] = g.rcp;
             hzf[tid] = g.Z;
-            ks[blk * kD + tid] = g.sbits;
-            kz[blk * kD + tid] = g.zbits;
+            ks[blk * kD + Q * q + tid] = g.sbits;
+            kz[blk * kD + Q * q + tid] = g.zbits;
         }
         __syncthreads();
-        {
-            // Token t = tid / 2, channels [64 * (tid & 1), +64) -> 32 bytes of its row.
-            const int t = tid >> 1, c0 = (tid & 1) * 64;
-            uint32_t w[8];
+        // Token t = tid / 2, channels [16 * (tid & 1), +16) of the quarter -> 8 bytes of its row.
+        const int t = tid >> 1, c0 = (tid & 1) * 16;
+        uint32_t w[2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                uint32_t v = 0;
+        for (int i = 0; i < 2; ++i) {
+            uint32_t v = 0;
 #pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const int d = c0 + 8 * i + n;
-                    v |= encode_one(at(t, d), hs[d], hr[d], hzf[d]) << (4 * n);
-                }
-                w[i] = v;
+            for (int n = 0; n < 8; ++n) {
+                const int c = c0 + 8 * i + n;
+                v |= encode_one(half_bits_to_float(tile[t * PAD + c]), hs[c], hr[c], hzf[c]) << (4 * n);
             }
-            uint4* dst = reinterpret_cast<uint4*>(kc + (blk * kG + t) * kRow + c0 / 2);
-            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            w[i] = v;
         }
+        *reinterpret_cast<uint2*>(kc + (blk * kG + t) * kRow + (Q / 2) * q + c0 / 2) = make_uint2(w[0], w[1]);
         return;
     }
 
-    // ---- V: one group per token.
-    load_tile(V + (int64_t)h * kG * kD);
+    // ---- V: one group per token; this workgroup's 32 tokens.
+    constexpr int PAD = kD + 2;
+    const uint16_t* src = V + ((int64_t)h * kG + Q * q) * kD;
+    for (int i = tid; i < Q * (kD / 8); i += 256) {
+        const int t = i / (kD / 8), c = i % (kD / 8);
+        const uint4 u = reinterpret_cast<const uint4*>(src + (int64_t)t * kD)[c];
+        uint32_t* dst = reinterpret_cast<uint32_t*>(tile + t * PAD + 8 * c);
+        dst[0] = u.x;
+        dst[1] = u.y;
+        dst[2] = u.z;
+        dst[3] = u.w;
+    }
     __syncthreads();
     {
-        const int t = tid >> 1, c0 = (tid & 1) * 64;
+        const int t = tid >> 3, part = tid & 7;              // 8 lanes of 16 channels per token
         float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-        for (int d = c0; d < c0 + 64; ++d) {
-            const float x = at(t, d);
+        for (int d = part * 16; d < part * 16 + 16; ++d) {
+            const float x = half_bits_to_float(tile[t * PAD + d]);
             mn = __builtin_fminf(mn, x);
             mx = __builtin_fmaxf(mx, x);
         }
-        mn = __builtin_fminf(mn, __shfl_xor(mn, 1, 64));
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1, 64));
-        if ((tid & 1) == 0) {
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+            mn = __builtin_fminf(mn, __shfl_xor(mn, o, 64));
+            mx = __builtin_fmaxf(mx, __shfl_xor(mx, o, 64));
+        }
+        if (part == 0) {
             const GroupHeader g = make_header(mn, mx, 15);
             hs[t] = g.s;
             hr[t] = g.rcp;
             hzf[t] = g.Z;
-            vs[blk * kG + t] = g.sbits;
-            vz[blk * kG + t] = g.zbits;
+            vs[blk * kG + Q * q + t] = g.sbits;
+            vz[blk * kG + Q * q + t] = g.zbits;
         }
     }
     __syncthreads();
-    {
-        // Channel d = tid / 2, tokens [64 * (tid & 1), +64) -> 32 bytes of its row.
-        const int d = tid >> 1, t0 = (tid & 1) * 64;
-        uint32_t w[8];
+    // Channel d = tid / 2, tokens [16 * (tid & 1), +16) of the quarter -> 8 bytes of its row.
+    const int d = tid >> 1, t0 = (tid & 1) * 16;
+    uint32_t w[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t v = 0;
+    for (int i = 0; i < 2; ++i) {
+        uint32_t v = 0;
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const int t = t0 + 8 * i + n;
-                v |= encode_one(at(t, d), hs[t], hr[t], hzf[t]) << (4 * n);
-            }
-            w[i] = v;
+        for (int n = 0; n < 8; ++n) {
+            const int t = t0 + 8 * i + n;
+            v |= encode_one(half_bits_to_float(tile[t * PAD + d]), hs[t], hr[t], hzf[t]) << (4 * n);
         }
-        uint4* dst = reinterpret_cast<uint4*>(vc + (blk * kD + d) * kRow + t0 / 2);
-        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        w[i] = v;
     }
+    *reinterpret_cast<uint2*>(vc + (blk * kD + d) * kRow + (Q / 2) * q + t0 / 2) = make_uint2(w[0], w[1]);
 }
 
 }  // namespace
@@ -507,7 +518,7 @@ hipError_t launch_kv_attention(const void* q, const KvCacheArgs& c, const int32_
 
 hipError_t launch_kv_quantize(const void* K, const void* V, const KvCacheArgs& c, int64_t block,
                               hipStream_t stream) {
-    kv_quantize_kernel<<<dim3((unsigned)c.heads, 2), dim3(256), 0, stream>>>(
+    kv_quantize_kernel<<<dim3((unsigned)c.heads, 8), dim3(256), 0, stream>>>(
         static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), static_cast<uint8_t*>(c.kcodes),
         static_cast<uint16_t*>(c.kscales), static_cast<uint16_t*>(c.kzeros), static_cast<uint8_t*>(c.vcodes),
         static_cast<uint16_t*>(c.vscales), static_cast<uint16_t*>(c.vzeros), c.max_blocks, block);
