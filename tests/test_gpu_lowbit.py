@@ -38,10 +38,12 @@ def run_case(N, K, group, bits, B, scheme="asym", seed=0):
 # (K, group): units per row U = K/64 (2 bits) or K/128 (3 bits) pick the
 # tiling: U <= 16 -> 16x1, <= 32 -> 16x2, <= 64 -> 64x1, <= 128 -> 64x2,
 # <= 256 -> 64x4, <= 512 -> 64x8 (2 bits only).
+# K = 32768 puts 68-74 KB of X records in LDS (the 128 KB budget; it did not
+# fit the old 64 KB).
 CASES_2 = [(64, 32), (1024, 32), (1536, 64), (4096, 128), (8192, 128), (8192, 32),
-           (12288, 256), (28672, 128), (4096, 4096)]
+           (12288, 256), (28672, 128), (4096, 4096), (32768, 128)]
 CASES_3 = [(128, 32), (896, 32), (4096, 128), (4096, 64), (8192, 128), (11008, 128),
-           (28672, 128), (3968, 3968)]
+           (28672, 128), (3968, 3968), (32768, 128)]
 
 
 @pytest.mark.parametrize("K,group", CASES_2)
