@@ -738,13 +738,67 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def run_ceiling(args):
-    """Reachable HBM rates on this GPU for plain torch kernels, as context for
-    the roofline fractions (peak 8 TB/s): a float32-accumulating sum over a
-    1 GiB fp16 buffer (read only), a 1 GiB copy (read + write) and a 1 GiB
-    fill (write only).  Two source
-    buffers alternate, so no call finds its data in the 256 MB Infinity Cache."""
+def probe_ceiling(shapes=None, reps=20, log=True):
+    """Read rates of the load-only probe (libwq_probe.so) over the packed codes
+    of the 70B-class up-projection (28672 rows x 4096 bytes), eight distinct
+    buffers in rotation (940 MB, beyond the 256 MB Infinity Cache).  Each shape
+    is (lanes per row, loads in flight per wave, walk order, non-temporal,
+    workgroups per compute unit); returns one row per shape."""
     import torch
+
+    from bit_weight_only_wq_amd import probe
+
+    rows, row_bytes = 28672, 4096
+    nbuf = 8
+    bufs = [torch.empty(rows * row_bytes, dtype=torch.uint8, device="cuda:0") for _ in range(nbuf)]
+    for i, b in enumerate(bufs):
+        b.fill_(i + 1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    hs = stream.cuda_stream
+    if shapes is None:
+        shapes = ([(64, D, o, 1, bpc) for D in (2, 4) for o in (0, 1) for bpc in (1, 2, 4)] +
+                  [(L, D, o, nt, bpc) for L in (32, 16, 8, 4) for D in (4, 8) for o in (0, 1, 2)
+                   for nt in (1, 0) for bpc in (2, 4)])
+    out = []
+    for L, D, o, nt, bpc in shapes:
+        def call(i):
+            probe.read(bufs[i % nbuf].data_ptr(), rows, row_bytes, L, D, o, nt, bpc, sink.data_ptr(), hs)
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        row = {"lanes_per_row": L, "depth": D, "order": o, "nontemporal": nt, "blocks_per_cu": bpc,
+               "us": round(us, 2), "GBps": round(rows * row_bytes / us / 1e3, 1)}
+        if log:
+            print(json.dumps(row), flush=True)
+        out.append(row)
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_ceiling(args):
+    """Reachable HBM read rates on this GPU, as context for the roofline
+    fractions (peak 8 TB/s): the hand-written load-only probe in the access
+    shapes of the product kernels (one 1 KB piece of one row per load
+    instruction, as the GEMVs read; 64 to 256 bytes of each of 4 to 16 rows,
+    as the matrix-core kernels read), plus plain torch read / copy / fill
+    kernels over 1 GiB buffers for comparison."""
+    import torch
+    rows = probe_ceiling(reps=max(args.steps, 10))
+    best = {}
+    for r in rows:
+        L = r["lanes_per_row"]
+        if L not in best or r["GBps"] > best[L]["GBps"]:
+            best[L] = r
     n = 1 << 29                                  # fp16 elements: 1 GiB
     src = [torch.ones(n, dtype=torch.float16, device="cuda:0") for _ in range(2)]
     dst = torch.empty(n, dtype=torch.float16, device="cuda:0")
@@ -767,13 +821,14 @@ def run_ceiling(args):
     copy_us = timed(lambda i: dst.copy_(src[i % 2]), reps)
     write_us = timed(lambda i: dst.fill_(float(i % 3)), reps)
     nbytes = n * 2
-    row = {"table": "hbm ceiling", "buffer_bytes": nbytes, "calls": reps,
-           "read": {"kernel": "torch.sum (fp16 -> fp32)", "us": round(read_us, 2),
-                    "GBps": round(nbytes / read_us / 1e3, 1)},
-           "copy": {"kernel": "Tensor.copy_", "us": round(copy_us, 2),
-                    "GBps": round(2 * nbytes / copy_us / 1e3, 1)},
-           "write": {"kernel": "Tensor.fill_", "us": round(write_us, 2),
-                     "GBps": round(nbytes / write_us / 1e3, 1)},
+    row = {"table": "hbm ceiling", "probe_bytes": 28672 * 4096,
+           "probe_best_by_lanes_per_row": {str(k): v for k, v in sorted(best.items())},
+           "torch_read": {"kernel": "torch.sum (fp16 -> fp32)", "us": round(read_us, 2),
+                          "GBps": round(nbytes / read_us / 1e3, 1)},
+           "torch_copy": {"kernel": "Tensor.copy_", "us": round(copy_us, 2),
+                          "GBps": round(2 * nbytes / copy_us / 1e3, 1)},
+           "torch_write": {"kernel": "Tensor.fill_", "us": round(write_us, 2),
+                           "GBps": round(nbytes / write_us / 1e3, 1)},
            "peak_GBps": 8000.0}
     print(json.dumps(row), flush=True)
     return row

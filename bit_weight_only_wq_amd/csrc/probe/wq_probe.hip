@@ -1,0 +1,152 @@
+// HBM read-stream probe for one MI355X (gfx950).
+//
+// The decode product is bound by how fast the packed weights stream from HBM
+// ("Quantization & inference optimisation", "Bandwidth, not compute"; "What
+// actually happens when you quantize a KV cache" §6: runtime is bytes over
+// bandwidth), so its roofline fractions are quoted against two numbers: the
+// vendor peak and what a load-only kernel actually reaches here.  This kernel
+// is that load-only kernel.  It reads a matrix of `rows` rows of `row_bytes`
+// bytes with 128-bit loads and no arithmetic, in the access shapes the
+// product kernels use:
+//   - a "strip" is 64 / L rows; one wave walks a strip along its rows, and
+//     each of its load instructions reads L consecutive 16-byte vectors of
+//     each of the strip's rows (L = 64: one 1 KB piece of one row, the GEMV's
+//     shape; L = 4: 64 bytes of each of 16 rows, the matrix-core kernels'
+//     shape);
+//   - every wave keeps D loads in flight in a register ring, across strip
+//     boundaries, and takes strips wave-major over a persistent grid;
+//   - loads past a wave's last strip use an out-of-range buffer offset, so
+//     they return zero without touching memory;
+//   - `order` picks how strips map to rows and where a walk starts: 0, the
+//     strip's rows are adjacent and every wave starts at column 0; 1, adjacent
+//     rows, and wave w starts its walk at step w mod steps (wrapping); 2, the
+//     strip's rows are spread over the matrix (row s + i * strips).
+// Nothing is written except, practically never, one word that keeps the
+// loads from being optimized away.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wq_probe.h"
+
+namespace {
+
+constexpr int kBufferWord3 = 0x00020000;   // raw, unswizzled gfx9 buffer
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+template <int L, int D, int AUX, int ORD>
+__global__ __launch_bounds__(256) void probe_read_kernel(const void* __restrict__ buf, uint32_t bytes,
+                                                         int64_t strips, int64_t steps, uint32_t row_bytes,
+                                                         uint32_t* __restrict__ sink) {
+    constexpr int RPI = 64 / L;                        // rows per strip
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(buf), (short)0, (int)bytes, kBufferWord3);
+    // Row of this lane within the strip: adjacent (ORD 0, 1) or spread (ORD 2).
+    const uint32_t lane_row = ORD == 2 ? (uint32_t)(lane / L) * (uint32_t)strips : (uint32_t)(lane / L);
+    const uint32_t lane_off = lane_row * row_bytes + (uint32_t)(lane % L) * 16u;
+    const int64_t rot = ORD == 1 ? gw % steps : 0;     // first step of every walk
+    // Items of this wave: (strip, step) in order, strips gw, gw + nw, ...
+    const int64_t my_strips = gw < strips ? (strips - gw + nw - 1) / nw : 0;
+    const int64_t items = my_strips * steps;
+    int64_t ls = gw, lstep = 0;                        // load cursor
+    auto next_off = [&]() -> uint32_t {
+        int64_t cs = lstep + rot;
+        cs = cs < steps ? cs : cs - steps;
+        const uint32_t first_row = ORD == 2 ? (uint32_t)ls : (uint32_t)(ls * RPI);
+        const uint32_t off = ls < strips
+            ? first_row * row_bytes + (uint32_t)(cs * L * 16) + lane_off
+            : kOutOfRange;
+        if (++lstep == steps) {
+            lstep = 0;
+            ls += nw;
+        }
+        return off;
+    };
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    v4u v[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) v[d] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)next_off(), 0, AUX);
+    uint32_t acc = 0;
+    for (int64_t j = 0; j < items; j += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+            v[d] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)next_off(), 0, AUX);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+template <int L, int D, int ORD>
+hipError_t launch_ldo(bool nt, const void* buf, uint32_t bytes, int64_t strips, int64_t steps,
+                      uint32_t row_bytes, unsigned blocks, uint32_t* sink, hipStream_t st) {
+    // Cache policy: 2 = non-temporal (the GEMVs' code loads), 0 = default.
+    if (nt)
+        probe_read_kernel<L, D, 2, ORD><<<dim3(blocks), dim3(256), 0, st>>>(buf, bytes, strips, steps, row_bytes, sink);
+    else
+        probe_read_kernel<L, D, 0, ORD><<<dim3(blocks), dim3(256), 0, st>>>(buf, bytes, strips, steps, row_bytes, sink);
+    return hipGetLastError();
+}
+
+template <int L, int D>
+hipError_t launch_ld(int order, bool nt, const void* buf, uint32_t bytes, int64_t strips, int64_t steps,
+                     uint32_t row_bytes, unsigned blocks, uint32_t* sink, hipStream_t st) {
+    switch (order) {
+        case 0: return launch_ldo<L, D, 0>(nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
+        case 1: return launch_ldo<L, D, 1>(nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
+        case 2: return launch_ldo<L, D, 2>(nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int L>
+hipError_t launch_l(int depth, int order, bool nt, const void* buf, uint32_t bytes, int64_t strips, int64_t steps,
+                    uint32_t row_bytes, unsigned blocks, uint32_t* sink, hipStream_t st) {
+    switch (depth) {
+        case 2: return launch_ld<L, 2>(order, nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
+        case 4: return launch_ld<L, 4>(order, nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
+        case 8: return launch_ld<L, 8>(order, nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
+        case 16: return launch_ld<L, 16>(order, nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+extern "C" int32_t wq_probe_read(const void* buf, int64_t rows, int64_t row_bytes, int32_t lanes_per_row,
+                                 int32_t depth, int32_t order, int32_t nontemporal, int32_t blocks_per_cu,
+                                 void* sink, void* stream) {
+    const int L = lanes_per_row;
+    if (L != 4 && L != 8 && L != 16 && L != 32 && L != 64) return 2;
+    if (depth != 2 && depth != 4 && depth != 8 && depth != 16) return 2;
+    if (order < 0 || order > 2) return 1;
+    if (!buf || !sink || rows < 1 || row_bytes < 16 || blocks_per_cu < 1 || blocks_per_cu > 32) return 1;
+    const int64_t rpi = 64 / L;
+    if (rows % rpi != 0 || row_bytes % (16 * L) != 0) return 1;
+    if (rows * row_bytes > (int64_t)0xFFFFFF00) return 2;          // 32-bit buffer offsets
+    if ((reinterpret_cast<uintptr_t>(buf) & 15) || (reinterpret_cast<uintptr_t>(sink) & 3)) return 3;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 4;
+    const int64_t strips = rows / rpi;
+    const int64_t steps = row_bytes / (16 * L);
+    const unsigned blocks = (unsigned)cus * (unsigned)blocks_per_cu;
+    const uint32_t bytes = (uint32_t)(rows * row_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t* s = static_cast<uint32_t*>(sink);
+    hipError_t e = hipErrorInvalidValue;
+    const bool nt = nontemporal != 0;
+    switch (L) {
+        case 4: e = launch_l<4>(depth, order, nt, buf, bytes, strips, steps, (uint32_t)row_bytes, blocks, s, st); break;
+        case 8: e = launch_l<8>(depth, order, nt, buf, bytes, strips, steps, (uint32_t)row_bytes, blocks, s, st); break;
+        case 16: e = launch_l<16>(depth, order, nt, buf, bytes, strips, steps, (uint32_t)row_bytes, blocks, s, st); break;
+        case 32: e = launch_l<32>(depth, order, nt, buf, bytes, strips, steps, (uint32_t)row_bytes, blocks, s, st); break;
+        case 64: e = launch_l<64>(depth, order, nt, buf, bytes, strips, steps, (uint32_t)row_bytes, blocks, s, st); break;
+    }
+    return e == hipSuccess ? 0 : 4;
+}
