@@ -3,23 +3,27 @@
 
 One step is one pass of the whole hot path over the 70B-class MLP
 up-projection (K=8192, N=28672, 4-bit codes, group 128 along K):
+    wq_gemm(X[B], codes) for B = 1, 2, 4, 8, 16, 32, 64   decode-step products
     wq_quantize_pack(W)                      fp16 weights -> codes + fp16 headers
-    wq_gemm(X[B], codes) for B = 1, 16, 64   decode-step products
 Each kernel works on its own copy from a pool of packed weights larger than
 1 GiB (two fp16 weight copies for the quantizer), so no call finds its inputs
 in the 256 MB Infinity Cache or the L2: every call streams from HBM.  Inputs
 are resident in HBM before timing starts.
 
-Printed: one JSON line with the whole step's algorithmic bytes per second
-(value, GB/s), the roofline of the B=1 product (the metric's kernel) with
-its duration measured by HIP events on the stream it runs on, the other
-kernels' rooflines, and the CPU oracle timed on a bounded sample of the
-same step.
+Printed: one JSON line whose value is the metric, the products' algorithmic
+bytes per second over B = 1..64 (GB/s, timed inside the K timed steps with
+events on the library's stream); the quantizer as its own kernel entry; the
+roofline of the dominant product with its duration measured by HIP events on
+the stream it runs on; every kernel's fraction of the vendor peak and of the
+read rate the load-only probe measured; and the CPU oracle timed on a bounded
+sample of the same workload.
 
     python bench.py [--steps 20] [--warmup 5] [--no-cpu]
-    python bench.py --sweep     # batch sweep across the ridge (K=N=8192), table only
+    python bench.py --workload gemv_k896_n4864_g32 | mlp7b_up_k4096_n11008_g128   # other configs (table lines)
+    python bench.py --sweep        # batch sweep across the ridge (K=N=8192), table only
     python bench.py --decode-set   # 7B-class decode step (224 products, B=32), table only
-    python bench.py --ceiling      # plain torch read / copy rates over 1 GiB (context), table only
+    python bench.py --kv           # decode attention over an int4 KV cache, table only
+    python bench.py --ceiling      # load-only probe read rates (and plain torch rates), table only
 """
 
 from __future__ import annotations
@@ -36,9 +40,8 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (% of peak) for int4 group-quant decode GEMM at B=1..64"
 WORKLOAD = "mlp70b_up_k8192_n28672_g128"
+METRIC_BATCHES = (1, 2, 4, 8, 16, 32, 64)   # the metric's batch range on the headline workload
 POOL_BYTES = 1 << 30          # packed-weight pool, >= 4x the 256 MB Infinity Cache
-CPU_SAMPLE_ROWS = 28672       # rows of the workload the oracle processes (all of them)
-CPU_MIN_SECONDS = 10.0        # repeat the oracle's step until this much CPU time
 
 
 def parse():
@@ -240,37 +243,68 @@ def write_traffic_summaries(args):
                 write_summary(args, tag, args.workload, fam, name, f, w, fr, wr, algo)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(name, batches, bits=0):
-    import numpy as np
+    """The oracle as it stands, timed on this host: quantize/pack and the
+    double-precision product (at every batch of the step), each on a row
+    sample of the workload, on all the cores the process may use and on one.
+    Rates are algorithmic GB/s of the sample (the unit of `value`); `value`
+    is the product's rate on all cores."""
     import oracle
     import wq_inputs
     from bit_weight_only_wq_amd import roofline as rl
     cfg = wq_inputs.WORKLOADS[name]
-    rows = min(CPU_SAMPLE_ROWS, cfg["N"])
-    W, X = wq_inputs.workload_arrays(name, rows=rows)
     K, G = cfg["K"], cfg["group"]
     bits = bits or cfg["bits"]
     oracle.build(force=False)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        c, s, z = oracle.quantize(W, G, bits)
-        for B in batches:
-            oracle.gemm(X[:B], c, s, z, rows, K, G, bits)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= CPU_MIN_SECONDS:
-            break
-    nbytes = rl.quantize_bytes(rows, K, G, bits) + sum(rl.gemm_bytes(B, rows, K, G, bits)
-                                                      for B in batches)
-    return {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"{rows} of {cfg['N']} rows of {name}, {reps} pass(es): exact "
-                      f"quantize/pack + double-precision GEMM at B={','.join(map(str, batches))}"}
+    all_cores = len(os.sched_getaffinity(0))
+
+    def timed(fn, min_s):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_s:
+                return dt / reps, reps
+
+    out = {}
+    # Sample sizes keep each of the four timings to a few seconds.
+    plan = {"all": (all_cores, min(cfg["N"], 8192), min(cfg["N"], 2048)),
+            "one": (1, min(cfg["N"], 1024), min(cfg["N"], 128))}
+    Wall, X = wq_inputs.workload_arrays(name, rows=max(p[1] for p in plan.values()))
+    for tag, (threads, q_rows, g_rows) in plan.items():
+        oracle.set_num_threads(threads)
+        W = Wall[:q_rows]
+        tq, rq = timed(lambda: oracle.quantize(W, G, bits), 2.0)
+        c, s, z = oracle.quantize(W[:g_rows], G, bits)
+        tg, rg = timed(lambda: [oracle.gemm(X[:B], c, s, z, g_rows, K, G, bits) for B in batches], 3.0)
+        gb = sum(rl.gemm_bytes(B, g_rows, K, G, bits) for B in batches)
+        out[tag] = {"threads": threads,
+                    "quantize_pack": {"rows": q_rows, "s": round(tq, 4), "reps": rq,
+                                      "GBps": round(rl.quantize_bytes(q_rows, K, G, bits) / tq / 1e9, 4)},
+                    "gemm": {"rows": g_rows, "batches": list(batches), "s": round(tg, 4), "reps": rg,
+                             "GBps": round(gb / tg / 1e9, 4)}}
+    oracle.set_num_threads(all_cores)
+    return {"value": out["all"]["gemm"]["GBps"], "unit": "GB/s", "cores": all_cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"rows of {name}: quantize/pack of {plan['all'][1]} rows and the double-precision "
+                      f"product at B={','.join(map(str, batches))} of {plan['all'][2]} rows on "
+                      f"{all_cores} threads; {plan['one'][1]} and {plan['one'][2]} rows on 1 thread",
+            "breakdown": out}
 
 
 def run_step_bench(args):
-    import numpy as np
     import torch
 
     import bit_weight_only_wq_amd as wq
@@ -280,7 +314,8 @@ def run_step_bench(args):
     cfg = wq_inputs.WORKLOADS[args.workload]
     N, K, G, bits = cfg["N"], cfg["K"], cfg["group"], cfg["bits"]
     bits = args.bits or bits
-    batches = [b for b in cfg["batches"] if b <= 64] or [1]
+    # The headline workload runs the metric's batch range; the others their own.
+    batches = list(METRIC_BATCHES) if args.workload == WORKLOAD else [b for b in cfg["batches"] if b <= 64]
     if args.batches:
         batches = [int(b) for b in args.batches.split(",")]
     dev = torch.device("cuda:0")
@@ -293,6 +328,11 @@ def run_step_bench(args):
     P = max(len(batches) + 3, -(-POOL_BYTES // slot_bytes))
     P = max(P, 2 * len(batches) + 3)
     pool = [wq.quantize_pack(Wd[0], G, bits) for _ in range(P)]
+    # One caller-owned workspace serves every product of the step (they run
+    # one after another on the stream).
+    ws_bytes = max(wq.gemm_workspace_bytes(B, K, N, G, bits, args.path) for B in batches)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws_ptr = ws.data_ptr() if ws_bytes else None
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -308,7 +348,7 @@ def run_step_bench(args):
 
     def gemm(j, B, slot):
         c, s, z = slot_ptrs[slot % P]
-        st = lib.wq_gemm_ex(xy[B][0], c, s, z, xy[B][1], B, K, N, G, bits, path_id, hs)
+        st = lib.wq_gemm_ex(xy[B][0], c, s, z, xy[B][1], B, K, N, G, bits, path_id, ws_ptr, ws_bytes, hs)
         if st:
             wq.check(st, "wq_gemm")
 
@@ -318,34 +358,41 @@ def run_step_bench(args):
         if st:
             wq.check(st, "wq_quantize_pack")
 
-    def step(i):
+    def step(i, ev=None):
         # Products first, each on its own pool slot; then the quantizer writes a
         # slot that is next read two steps later (>1 GB of traffic in between).
+        # ev: optional events (before the products, after them, after quantize).
+        if ev:
+            ev[0].record(stream)
         for j, B in enumerate(batches):
             gemm(j, B, nb * i + j)
+        if ev:
+            ev[1].record(stream)
         quant(i, nb * i + 2 * nb + 1)
+        if ev:
+            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region 1: whole steps back to back, no events inside.
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # Timed region: K whole steps back to back.  Events on the stream the
+    # library launches on split each step into its products and its quantize.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
-    end.record(stream)
+        step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_total = start.elapsed_time(end)
+    ms_total = evs[0][0].elapsed_time(evs[-1][2])
     ms_step = ms_total / args.steps
+    ms_gemm = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    ms_quant = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
 
-    # Timed region 2: each kernel of the step launched `steps` times back to
-    # back (every launch on another pool slot), bracketed by one pair of events
-    # on the stream the library launches on; average duration per launch.
+    # Per kernel: each product (and the quantizer) launched `steps` times back
+    # to back, every launch on another pool slot, bracketed by one pair of
+    # events on the library's stream; average duration per launch.
     def burst(fn):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -361,26 +408,35 @@ def run_step_bench(args):
     per = {B: burst(lambda i, j=j, B=B: gemm(j, B, i)) for j, B in enumerate(batches)}
     per_q = burst(lambda i: quant(i, i + nb))
 
-    step_bytes = rl.quantize_bytes(N, K, G, bits) + sum(rl.gemm_bytes(B, N, K, G, bits)
-                                                       for B in batches)
+    gemm_bytes = sum(rl.gemm_bytes(B, N, K, G, bits) for B in batches)
+    gemm_flops = sum(rl.gemm_flops(B, N, K) for B in batches)
+    q_bytes = rl.quantize_bytes(N, K, G, bits)
     kernels = {}
     for B in batches:
         kernels[f"wq_gemm_B{B}"] = kernel_entry(
             f"wq_gemm B={B}", rl.gemm_bytes(B, N, K, G, bits), rl.gemm_flops(B, N, K), [per[B]])
-    kernels["wq_quantize_pack"] = kernel_entry(
-        "wq_quantize_pack", rl.quantize_bytes(N, K, G, bits), 0, [per_q])
+    kernels["wq_quantize_pack"] = kernel_entry("wq_quantize_pack", q_bytes, 0, [per_q])
+    ceiling = read_ceiling()
+    if ceiling:
+        for e in kernels.values():
+            e["frac_measured_read_ceiling"] = round(e["achieved_GBps"] / ceiling["GBps"], 4)
 
-    head = kernels[f"wq_gemm_B{batches[0]}"]
-    # Counter summaries exist for the workload's own code width only.
-    traffic = read_traffic(f"wq_gemm_b{batches[0]}_{args.workload}") if bits == cfg["bits"] else None
+    # The dominant product (longest launch) carries the roofline object.
+    Bd = max(batches, key=lambda B: per[B])
+    head = kernels[f"wq_gemm_B{Bd}"]
+    traffic = read_traffic(f"wq_gemm_b{Bd}_{args.workload}") if bits == cfg["bits"] else None
     roof = {"kernel": head["kernel"], "bound": "hbm", "achieved": head["achieved_GBps"],
             "peak": rl.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
             "frac": round(head["achieved_GBps"] * 1e9 / rl.MI355X_HBM_BYTES_PER_S, 4),
             "traffic": traffic, "avg_us": head["avg_us"], "bytes_per_launch": head["bytes"]}
+    if ceiling:
+        roof["measured_read_ceiling_GBps"] = ceiling["GBps"]
+        roof["frac_measured_read_ceiling"] = round(head["achieved_GBps"] / ceiling["GBps"], 4)
 
+    value = gemm_bytes / (ms_gemm * 1e-3) / 1e9
     out = {
         "metric": METRIC,
-        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -393,15 +449,43 @@ def run_step_bench(args):
         "data": "synthetic",
         "config": {"workload": args.workload, "N": N, "K": K, "group": G, "bits": bits,
                    "batches": batches, "path": args.path,
-                   "step": "wq_quantize_pack + wq_gemm at B=" + ",".join(map(str, batches)),
-                   "step_bytes": int(step_bytes), "pool_slots": P,
-                   "wall_s": round(wall, 4)},
+                   "step": "wq_gemm at B=" + ",".join(map(str, batches)) + " + wq_quantize_pack",
+                   "value": "algorithmic bytes of the step's products / their time inside the timed steps",
+                   "gemm_bytes_per_step": int(gemm_bytes), "quantize_bytes_per_step": int(q_bytes),
+                   "workspace_bytes": int(ws_bytes), "pool_slots": P, "wall_s": round(wall, 4)},
+        "frac_hbm_peak": round(value * 1e9 / rl.MI355X_HBM_BYTES_PER_S, 4),
+        "ms_gemm_per_step": round(ms_gemm, 4),
+        "ms_quantize_per_step": round(ms_quant, 4),
+        "gemm_TFLOPs": round(gemm_flops / (ms_gemm * 1e-3) / 1e12, 2),
+        "step_GBps_with_quantize": round((gemm_bytes + q_bytes) / (ms_step * 1e-3) / 1e9, 1),
         "roofline": roof,
         "kernels": kernels,
     }
+    if ceiling:
+        out["frac_measured_read_ceiling"] = round(value / ceiling["GBps"], 4)
+        out["measured_read_ceiling"] = ceiling
     del pool, Wd
     torch.cuda.empty_cache()
     return out, batches
+
+
+def read_ceiling():
+    """The load-only probe's best read rate (one 1 KB piece of one row per
+    load instruction), from the committed summary
+    profiles/hbm_read_ceiling_probe.txt (None if absent)."""
+    path = os.path.join(ROOT, "profiles", "hbm_read_ceiling_probe.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, _, v = line.partition(":")
+            vals[k.strip()] = v.strip()
+    try:
+        return {"GBps": float(vals["best_GBps"]), "shape": vals.get("best_shape", ""),
+                "source": "profiles/hbm_read_ceiling_probe.txt"}
+    except (KeyError, ValueError):
+        return None
 
 
 def run_sweep(args):
@@ -420,6 +504,9 @@ def run_sweep(args):
     X = torch.from_numpy(Xn).to(dev)
     P = -(-POOL_BYTES // rl.packed_bytes(N, K, G, bits)) + 1
     pool = [wq.quantize_pack(W, G, bits) for _ in range(P)]
+    ws = torch.empty(max(16, max(wq.gemm_workspace_bytes(B, K, N, G, bits, p) for B in cfg["batches"]
+                                 for p in ("gemv", "mfma") if not (p == "gemv" and B > 8))),
+                     dtype=torch.uint8, device=dev)
     rows = []
     for B in cfg["batches"]:
         for path in ("gemv", "mfma"):
@@ -429,7 +516,7 @@ def run_sweep(args):
             Y = torch.empty((B, N), dtype=torch.float16, device=dev)
             for i in range(3):
                 c, s, z = pool[i % P]
-                wq.gemm(Xb, c, s, z, N=N, K=K, group=G, bits=bits, path=path, out=Y)
+                wq.gemm(Xb, c, s, z, N=N, K=K, group=G, bits=bits, path=path, out=Y, workspace=ws)
             torch.cuda.synchronize()
             reps = 30
             e0 = torch.cuda.Event(enable_timing=True)
@@ -437,7 +524,7 @@ def run_sweep(args):
             e0.record()
             for i in range(reps):
                 c, s, z = pool[i % P]
-                wq.gemm(Xb, c, s, z, N=N, K=K, group=G, bits=bits, path=path, out=Y)
+                wq.gemm(Xb, c, s, z, N=N, K=K, group=G, bits=bits, path=path, out=Y, workspace=ws)
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
@@ -502,15 +589,28 @@ def run_decode_set(args):
                 arr[j] = GemmItem(x, c, s, z, y, b, k, n, g, bits)
             layers.append(arr)
 
+        # One caller workspace, sized for the largest call, serves every call
+        # of the step (they run one after another on the stream).
+        import ctypes
+        need = 0
+        for arr in layers:
+            n = ctypes.c_size_t(0)
+            wq.check(lib.wq_gemm_grouped_workspace_size(arr, per_layer, ctypes.byref(n)), "workspace size")
+            need = max(need, n.value)
+        for N, K, G, *_ in mats[:per_layer]:
+            need = max(need, wq.gemm_workspace_bytes(B, K, N, G, bits))
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        ws_ptr = ws.data_ptr() if need else None
+
         def single_on(h):
             for x, c, s, z, y, b, k, n, g in calls:
-                st = lib.wq_gemm(x, c, s, z, y, b, k, n, g, bits, h)
+                st = lib.wq_gemm_ex(x, c, s, z, y, b, k, n, g, bits, 0, ws_ptr, need, h)
                 if st:
                     wq.check(st, "wq_gemm")
 
         def grouped_on(h):
             for arr in layers:
-                st = lib.wq_gemm_grouped(arr, per_layer, h)
+                st = lib.wq_gemm_grouped(arr, per_layer, ws_ptr, need, h)
                 if st:
                     wq.check(st, "wq_gemm_grouped")
 
@@ -526,9 +626,8 @@ def run_decode_set(args):
             return e0.elapsed_time(e1) / reps
 
         def graph_ms(step_on):
-            # Replayed from a HIP graph: no host launch gaps.  The capture
-            # stream's workspace is created by eager calls first, so capture
-            # records kernels only.
+            # Replayed from a HIP graph: no host launch gaps.  The calls
+            # allocate nothing, so capture records kernels only.
             cap = torch.cuda.Stream()
             torch.cuda.synchronize()
             with torch.cuda.stream(cap):
@@ -604,7 +703,12 @@ def run_kv(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    ms_attn = burst(lambda i: wq.kv_attention(q, caches[i % 2], lens, out=out), args.steps)
+    import ctypes
+    n = ctypes.c_size_t(0)
+    desc = caches[0].descriptor()
+    wq.check(wq.load().wq_kv_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "wq_kv_workspace_size")
+    ws = torch.empty(max(16, n.value), dtype=torch.uint8, device="cuda")
+    ms_attn = burst(lambda i: wq.kv_attention(q, caches[i % 2], lens, out=out, workspace=ws), args.steps)
     ms_app = burst(lambda i: wq.kv_quantize_block(Kb, Vb, caches[i % 2], i % nb), args.steps)
     b_attn = rl.kv_attention_bytes(H, T, D)
     b_app = rl.kv_append_bytes(H, G, D)

@@ -15,7 +15,8 @@ from . import roofline  # noqa: F401  (pure arithmetic, no GPU)
 from ._lib import (WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA, WQError,  # noqa: F401
                    LIB_PATH, check, load)
 
-__all__ = ["quantize_pack", "gemm", "gemm_grouped", "codes_bytes", "num_groups", "gemv_max_batch",
+__all__ = ["quantize_pack", "gemm", "gemm_grouped", "gemm_workspace_bytes", "codes_bytes", "num_groups",
+           "gemv_max_batch",
            "gemm_nf4", "gemm_offset", "KVCache", "kv_quantize_block", "kv_attention", "WQError", "LIB_PATH", "load"]
 
 _PATHS = {"auto": WQ_PATH_AUTO, "gemv": WQ_PATH_GEMV, "mfma": WQ_PATH_MFMA}
@@ -24,6 +25,31 @@ _PATHS = {"auto": WQ_PATH_AUTO, "gemv": WQ_PATH_GEMV, "mfma": WQ_PATH_MFMA}
 def _stream_handle(device):
     import torch
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _size_t(query, *args, where=""):
+    """Bytes from a wq_*_workspace_size query (raises on its error status)."""
+    import ctypes
+    n = ctypes.c_size_t(0)
+    check(query(*args, ctypes.byref(n)), where)
+    return int(n.value)
+
+
+def _workspace(nbytes, device, workspace=None):
+    """(pointer, bytes, tensor) of a caller workspace: the given uint8 tensor
+    (checked against nbytes) or a fresh one from torch's allocator, (None, 0,
+    None) when the call needs none.  A fresh tensor goes back to torch's stream-ordered cache
+    when the caller drops it, so reuse by later work on the stream is safe."""
+    import torch
+    if nbytes == 0:
+        return None, 0, None
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    elif (not isinstance(workspace, torch.Tensor) or workspace.device != torch.device(device)
+          or workspace.dtype != torch.uint8 or not workspace.is_contiguous()
+          or workspace.numel() < nbytes):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of >= {nbytes} bytes on {device}")
+    return workspace.data_ptr(), workspace.numel(), workspace
 
 
 def _need(t, dtype, shape, name):
@@ -48,6 +74,11 @@ def num_groups(N: int, K: int, group: int) -> int:
 
 def gemv_max_batch() -> int:
     return int(load().wq_gemv_max_batch())
+
+
+def gemm_workspace_bytes(B: int, K: int, N: int, group: int = 128, bits: int = 4, path: str = "auto") -> int:
+    """Workspace bytes of a gemm() call of this shape on the current device."""
+    return _size_t(load().wq_gemm_workspace_size, B, K, N, group, bits, _PATHS[path], where="wq_gemm")
 
 
 SCHEMES = {"asym": 0, "sym": 1, "sym_tensor": 2, "nf4": 3, "offset": 4}
@@ -81,17 +112,22 @@ def quantize_pack(W, group: int = 128, bits: int = 4, out=None, scheme: str = "a
         _need(scales, torch.float16, (N, K // group), "scales")
         _need(zeros, torch.float16, (N, K // group), "zeros")
     with torch.cuda.device(W.device):
+        need = _size_t(lib.wq_quantize_workspace_size, N, K, group, bits, SCHEMES[scheme],
+                       where="wq_quantize_pack")
+        ws, ws_bytes, _keep = _workspace(need, W.device)
         st = lib.wq_quantize_pack_ex(W.data_ptr(), N, K, group, bits, SCHEMES[scheme],
                                      codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
-                                     _stream_handle(W.device))
+                                     ws, ws_bytes, _stream_handle(W.device))
     check(st, "wq_quantize_pack")
     return codes, scales, zeros
 
 
-def gemm_grouped(items):
+def gemm_grouped(items, workspace=None, use_workspace=True):
     """Several products in one call: items is a sequence of
     (X, codes, scales, zeros, N, K, group, bits[, out]) tuples; returns the Y
-    tensors in order (each exactly what gemm() gives for its item)."""
+    tensors in order (each what gemm() gives for its item, within the product
+    tolerance).  The call's workspace comes from torch (or `workspace`, a
+    uint8 tensor); use_workspace=False runs the plans that need none."""
     import ctypes
     import torch
     from ._lib import GemmItem
@@ -123,14 +159,21 @@ def gemm_grouped(items):
     if not items:
         return outs
     with torch.cuda.device(dev):
-        st = lib.wq_gemm_grouped(arr, len(items), _stream_handle(dev))
+        need = _size_t(lib.wq_gemm_grouped_workspace_size, arr, len(items),
+                       where="wq_gemm_grouped") if use_workspace else 0
+        ws, ws_bytes, _keep = _workspace(need, dev, workspace)
+        st = lib.wq_gemm_grouped(arr, len(items), ws, ws_bytes, _stream_handle(dev))
     check(st, "wq_gemm_grouped")
     return outs
 
 
 def gemm(X, codes, scales, zeros, N: int, K: int, group: int = 128, bits: int = 4,
-         path: str = "auto", out=None):
-    """Y fp16 [B, N] = X fp16 [B, K] times the dequantized [N, K] matrix, transposed."""
+         path: str = "auto", out=None, workspace=None, use_workspace=True):
+    """Y fp16 [B, N] = X fp16 [B, K] times the dequantized [N, K] matrix, transposed.
+
+    The call's workspace (wq_gemm_workspace_size bytes) comes from torch, or
+    from `workspace` (a uint8 tensor); use_workspace=False runs the plan that
+    needs none (wq_gemm's)."""
     import torch
     lib = load()
     if X.dim() != 2:
@@ -145,8 +188,11 @@ def gemm(X, codes, scales, zeros, N: int, K: int, group: int = 128, bits: int = 
     else:
         _need(out, torch.float16, (B, N), "out")
     with torch.cuda.device(X.device):
+        need = _size_t(lib.wq_gemm_workspace_size, B, K, N, group, bits, _PATHS[path],
+                       where="wq_gemm") if use_workspace else 0
+        ws, ws_bytes, _keep = _workspace(need, X.device, workspace)
         st = lib.wq_gemm_ex(X.data_ptr(), codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
-                            out.data_ptr(), B, K, N, group, bits, _PATHS[path],
+                            out.data_ptr(), B, K, N, group, bits, _PATHS[path], ws, ws_bytes,
                             _stream_handle(X.device))
     check(st, "wq_gemm")
     return out
@@ -198,8 +244,10 @@ def kv_quantize_block(K, V, cache: KVCache, block: int):
     check(st, "wq_kv_quantize_block")
 
 
-def kv_attention(q, cache: KVCache, lens, out=None):
-    """q fp16 [heads, 128], lens int32 [heads] (GPU) -> out fp16 [heads, 128]."""
+def kv_attention(q, cache: KVCache, lens, out=None, workspace=None, use_workspace=True):
+    """q fp16 [heads, 128], lens int32 [heads] (GPU) -> out fp16 [heads, 128].
+    The call's workspace (context-split partials) comes from torch or from
+    `workspace`; use_workspace=False runs one workgroup per head."""
     import ctypes
     import torch
     _need(q, torch.float16, (cache.heads, cache.D), "q")
@@ -208,9 +256,13 @@ def kv_attention(q, cache: KVCache, lens, out=None):
         out = torch.empty((cache.heads, cache.D), dtype=torch.float16, device=q.device)
     _need(out, torch.float16, (cache.heads, cache.D), "out")
     desc = cache.descriptor()
+    lib = load()
     with torch.cuda.device(cache.device):
-        st = load().wq_kv_attention(q.data_ptr(), ctypes.byref(desc), lens.data_ptr(), out.data_ptr(),
-                                    _stream_handle(cache.device))
+        need = _size_t(lib.wq_kv_workspace_size, ctypes.byref(desc), where="wq_kv_attention") \
+            if use_workspace else 0
+        ws, ws_bytes, _keep = _workspace(need, cache.device, workspace)
+        st = lib.wq_kv_attention(q.data_ptr(), ctypes.byref(desc), lens.data_ptr(), out.data_ptr(),
+                                 ws, ws_bytes, _stream_handle(cache.device))
     check(st, "wq_kv_attention")
     return out
 

@@ -28,6 +28,7 @@ WQ_SCHEME_OFFSET = 4
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
 
 
 class GemmItem(ctypes.Structure):
@@ -45,12 +46,16 @@ class KvCache(ctypes.Structure):
 
 SIGNATURES = {
     "wq_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _P, _P, _P]),
-    "wq_quantize_pack_ex": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
+    "wq_quantize_pack_ex": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "wq_quantize_workspace_size": (ctypes.c_int, [_I64, _I64, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "wq_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P]),
-    "wq_gemm_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
-    "wq_gemm_grouped": (ctypes.c_int, [ctypes.POINTER(GemmItem), _I32, _P]),
+    "wq_gemm_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _SZ, _P]),
+    "wq_gemm_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
+    "wq_gemm_grouped": (ctypes.c_int, [ctypes.POINTER(GemmItem), _I32, _P, _SZ, _P]),
+    "wq_gemm_grouped_workspace_size": (ctypes.c_int, [ctypes.POINTER(GemmItem), _I32, ctypes.POINTER(_SZ)]),
     "wq_kv_quantize_block": (ctypes.c_int, [_P, _P, ctypes.POINTER(KvCache), _I64, _P]),
-    "wq_kv_attention": (ctypes.c_int, [_P, ctypes.POINTER(KvCache), _P, _P, _P]),
+    "wq_kv_attention": (ctypes.c_int, [_P, ctypes.POINTER(KvCache), _P, _P, _P, _SZ, _P]),
+    "wq_kv_workspace_size": (ctypes.c_int, [ctypes.POINTER(KvCache), ctypes.POINTER(_SZ)]),
     "wq_gemm_nf4": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "wq_gemm_offset": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P]),
     "wq_dequantize": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P]),

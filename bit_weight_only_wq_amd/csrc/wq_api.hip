@@ -1,6 +1,10 @@
 // C ABI of the weight-only group-quantized decode GEMM (declared in include/wq.h).
 // Validation happens here, synchronously, before anything is enqueued; the
 // kernels are then launched on the caller's stream without synchronizing.
+// The library allocates no device memory: scratch (split partials, the
+// per-tensor maximum) comes from a caller-owned workspace sized by the
+// wq_*_workspace_size queries, and calls without one take plans that need
+// none.
 #include <stdio.h>
 #include <string.h>
 
@@ -20,7 +24,8 @@ wq_status fail(wq_status st, const char* fmt, long long a = 0, long long b = 0) 
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Compute units of the current device, cached per device.
+// Compute units of the current device, cached per device (the one lazily
+// cached device property).
 int num_cus() {
     static int cached[64] = {0};
     int dev = 0;
@@ -38,6 +43,39 @@ wq_status check_hip(hipError_t e, const char* what) {
     if (e == hipSuccess) return WQ_OK;
     snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
     return WQ_ERR_HIP;
+}
+
+// A caller's workspace against the bytes the call needs.  Null with size 0
+// means none: the call then takes a plan that needs none.  Otherwise it must
+// be 16-byte aligned and hold at least `need` bytes.
+wq_status check_workspace(const char* who, const void* ws, size_t ws_bytes, size_t need) {
+    if (!ws) {
+        if (ws_bytes == 0) return WQ_OK;
+        snprintf(g_last_error, sizeof(g_last_error), "%s: null workspace with workspace_bytes=%llu", who,
+                 (unsigned long long)ws_bytes);
+        return WQ_ERR_INVALID_ARG;
+    }
+    if (!aligned(ws, 16)) {
+        snprintf(g_last_error, sizeof(g_last_error), "%s: workspace needs 16-byte alignment", who);
+        return WQ_ERR_MISALIGNED;
+    }
+    if (ws_bytes < need) {
+        snprintf(g_last_error, sizeof(g_last_error), "%s: workspace of %llu bytes, the call needs %llu", who,
+                 (unsigned long long)ws_bytes, (unsigned long long)need);
+        return WQ_ERR_INVALID_ARG;
+    }
+    return WQ_OK;
+}
+
+// Runs fn(paths) with a host array of count path slots.
+template <class F>
+wq_status with_paths(int32_t count, F fn) {
+    int32_t paths_small[64];
+    int32_t* paths = count <= 64 ? paths_small : new (std::nothrow) int32_t[count];
+    if (!paths) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_grouped: out of host memory (count=%lld)", count);
+    const wq_status st = fn(paths);
+    if (paths != paths_small) delete[] paths;
+    return st;
 }
 
 }  // namespace
@@ -73,10 +111,10 @@ int64_t wq_num_groups(int64_t N, int64_t K, int32_t group) {
 // kernels from B = 3 on.
 int32_t wq_gemv_max_batch(void) { return 2; }
 
-wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group, int32_t bits,
-                              int32_t scheme, void* codes, void* scales, void* zeros,
-                              void* stream) {
-    g_last_error[0] = '\0';
+// ---- quantize/pack -----------------------------------------------------------
+
+// Shape and scheme checks of a quantize call (no pointers).
+static wq_status check_quant_shape(int64_t N, int64_t K, int32_t group, int32_t bits, int32_t scheme) {
     if (N < 0 || K < 1 || group < 1)
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: need N >= 0, K >= 1, group >= 1 (N=%lld K=%lld)", N, K);
     if (K % group != 0)
@@ -91,19 +129,45 @@ wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group
         return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: the codec takes bits 2..8 (got %lld)", bits);
     if (group % 8 != 0)
         return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_pack: group=%lld must be a multiple of 8", group);
+    return WQ_OK;
+}
+
+wq_status wq_quantize_workspace_size(int64_t N, int64_t K, int32_t group, int32_t bits, int32_t scheme,
+                                     size_t* bytes) {
+    g_last_error[0] = '\0';
+    if (!bytes) return fail(WQ_ERR_INVALID_ARG, "wq_quantize_workspace_size: null bytes");
+    *bytes = 0;
+    const wq_status st = check_quant_shape(N, K, group, bits, scheme);
+    if (st != WQ_OK) return st;
+    *bytes = N == 0 ? 0 : wq::quantize_scratch_bytes(scheme);
+    return WQ_OK;
+}
+
+wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group, int32_t bits,
+                              int32_t scheme, void* codes, void* scales, void* zeros, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    wq_status st = check_quant_shape(N, K, group, bits, scheme);
+    if (st != WQ_OK) return st;
+    const size_t need = wq::quantize_scratch_bytes(scheme);
+    st = check_workspace("wq_quantize_pack", workspace, workspace_bytes, need);
+    if (st != WQ_OK) return st;
     if (N == 0) return WQ_OK;
     if (!W || !codes || !scales || !zeros)
         return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: null pointer");
     if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
         return fail(WQ_ERR_MISALIGNED, "wq_quantize_pack: W and codes need 16-byte alignment");
-    return check_hip(wq::launch_quantize_pack(W, N, K, group, bits, scheme, codes, scales, zeros,
+    if (need > 0 && !workspace)
+        return fail(WQ_ERR_INVALID_ARG, "wq_quantize_pack: the per-tensor scheme needs a workspace of %lld bytes",
+                    (long long)need);
+    return check_hip(wq::launch_quantize_pack(W, N, K, group, bits, scheme, codes, scales, zeros, workspace,
                                               static_cast<hipStream_t>(stream)),
                      "wq_quantize_pack launch");
 }
 
 wq_status wq_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group, int32_t bits,
                            void* codes, void* scales, void* zeros, void* stream) {
-    return wq_quantize_pack_ex(W, N, K, group, bits, WQ_SCHEME_ASYM, codes, scales, zeros,
+    return wq_quantize_pack_ex(W, N, K, group, bits, WQ_SCHEME_ASYM, codes, scales, zeros, nullptr, 0,
                                stream);
 }
 
@@ -132,12 +196,13 @@ wq_status wq_dequantize(const void* codes, const void* scales, const void* zeros
                      "wq_dequantize launch");
 }
 
-// Validates one product and picks its kernel family (path on return); does
-// not enqueue anything.  A no-op product (B == 0 or N == 0) returns WQ_OK with
-// path = -1.
-static wq_status check_gemm(const void* X, const void* codes, const void* scales,
-                            const void* zeros, const void* Y, int64_t B, int64_t K, int64_t N,
-                            int32_t group, int32_t bits, int32_t& path) {
+// ---- products ----------------------------------------------------------------
+
+// Validates the shape of one product and picks its kernel family (path on
+// return); checks no pointer.  A no-op product (B == 0 or N == 0) returns
+// WQ_OK with path = -1.
+static wq_status check_gemm_shape(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                                  int32_t& path) {
     if (B < 0 || N < 0 || K < 1 || group < 1)
         return fail(WQ_ERR_INVALID_ARG, "wq_gemm: need B >= 0, N >= 0, K >= 1, group >= 1 (B=%lld K=%lld)", B, K);
     if (K % group != 0)
@@ -169,11 +234,6 @@ static wq_status check_gemm(const void* X, const void* codes, const void* scales
         path = -1;
         return WQ_OK;
     }
-    if (!X || !codes || !scales || !zeros || !Y)
-        return fail(WQ_ERR_INVALID_ARG, "wq_gemm: null pointer");
-    if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(Y, 2))
-        return fail(WQ_ERR_MISALIGNED, "wq_gemm: X and codes need 16-byte alignment");
-
     if (low) {
         path = WQ_PATH_GEMV;
         return WQ_OK;
@@ -194,13 +254,28 @@ static wq_status check_gemm(const void* X, const void* codes, const void* scales
     return WQ_OK;
 }
 
+// Shape, then pointers.
+static wq_status check_gemm(const void* X, const void* codes, const void* scales,
+                            const void* zeros, const void* Y, int64_t B, int64_t K, int64_t N,
+                            int32_t group, int32_t bits, int32_t& path) {
+    const wq_status st = check_gemm_shape(B, K, N, group, bits, path);
+    if (st != WQ_OK || path < 0) return st;
+    if (!X || !codes || !scales || !zeros || !Y)
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm: null pointer");
+    if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(Y, 2))
+        return fail(WQ_ERR_MISALIGNED, "wq_gemm: X and codes need 16-byte alignment");
+    return WQ_OK;
+}
+
+// Sizes (ws.need set) or launches one validated product on its kernel family.
 static wq_status run_gemm(const void* X, const void* codes, const void* scales, const void* zeros,
                           void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
-                          int32_t use, hipStream_t st) {
+                          int32_t use, const wq::Scratch& ws, hipStream_t st) {
     if (use == WQ_PATH_MFMA)
         return check_hip(wq::launch_gemm_mfma(X, codes, scales, zeros, Y, B, K, N, group, bits,
-                                              num_cus(), st),
+                                              num_cus(), ws, st),
                          "wq_gemm (mfma) launch");
+    if (ws.sizing()) return WQ_OK;   // the GEMVs use no scratch
     if (bits == 2 || bits == 3)
         return check_hip(wq::launch_gemv_lowbit(X, codes, scales, zeros, Y, B, K, N, group, bits, 0,
                                                 num_cus(), st),
@@ -209,30 +284,55 @@ static wq_status run_gemm(const void* X, const void* codes, const void* scales, 
                      "wq_gemm (gemv) launch");
 }
 
-wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales, const void* zeros,
-                     void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
-                     int32_t path, void* stream) {
+wq_status wq_gemm_workspace_size(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                                 int32_t path, size_t* bytes) {
     g_last_error[0] = '\0';
+    if (!bytes) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_workspace_size: null bytes");
+    *bytes = 0;
     int32_t use = path;
-    const wq_status st = check_gemm(X, codes, scales, zeros, Y, B, K, N, group, bits, use);
+    const wq_status st = check_gemm_shape(B, K, N, group, bits, use);
     if (st != WQ_OK || use < 0) return st;
-    return run_gemm(X, codes, scales, zeros, Y, B, K, N, group, bits, use, static_cast<hipStream_t>(stream));
+    size_t need = 0;
+    wq::Scratch ws;
+    ws.need = &need;
+    // Sizing launches nothing; the pointers are never read.
+    const wq_status s2 = run_gemm(nullptr, nullptr, nullptr, nullptr, nullptr, B, K, N, group, bits, use, ws,
+                                  nullptr);
+    if (s2 != WQ_OK) return s2;
+    *bytes = need;
+    return WQ_OK;
 }
 
-wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream) {
+wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales, const void* zeros,
+                     void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                     int32_t path, void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error[0] = '\0';
-    if (count < 0 || (count > 0 && !items))
-        return fail(WQ_ERR_INVALID_ARG, "wq_gemm_grouped: count=%lld, items=%lld (null)", count,
-                    (long long)(items != nullptr));
-    // Validate everything before enqueuing anything.
-    int32_t paths_small[64];
-    int32_t* paths = count <= 64 ? paths_small : new (std::nothrow) int32_t[count];
-    if (!paths) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_grouped: out of host memory (count=%lld)", count);
-    struct Release {
-        int32_t* p;
-        int32_t* small;
-        ~Release() { if (p != small) delete[] p; }
-    } release{paths, paths_small};
+    int32_t use = path;
+    wq_status st = check_gemm(X, codes, scales, zeros, Y, B, K, N, group, bits, use);
+    if (st != WQ_OK) return st;
+    if (use < 0) return check_workspace("wq_gemm", workspace, workspace_bytes, 0);
+    size_t need = 0;
+    if (workspace) {
+        wq::Scratch sz;
+        sz.need = &need;
+        st = run_gemm(X, codes, scales, zeros, Y, B, K, N, group, bits, use, sz, nullptr);
+        if (st != WQ_OK) return st;
+    }
+    st = check_workspace("wq_gemm", workspace, workspace_bytes, need);
+    if (st != WQ_OK) return st;
+    wq::Scratch ws;
+    ws.ptr = need > 0 ? workspace : nullptr;
+    return run_gemm(X, codes, scales, zeros, Y, B, K, N, group, bits, use, ws, static_cast<hipStream_t>(stream));
+}
+
+wq_status wq_gemm(const void* X, const void* codes, const void* scales, const void* zeros,
+                  void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                  void* stream) {
+    return wq_gemm_ex(X, codes, scales, zeros, Y, B, K, N, group, bits, WQ_PATH_AUTO, nullptr, 0, stream);
+}
+
+// Validates every item (paths[i] receives its kernel family, -1 for a no-op).
+static wq_status check_items(const wq_gemm_item* items, int32_t count, int32_t* paths) {
     for (int32_t i = 0; i < count; ++i) {
         const wq_gemm_item& it = items[i];
         paths[i] = WQ_PATH_AUTO;
@@ -245,9 +345,15 @@ wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream
             return st;
         }
     }
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    // X-resident products of one (B, bits) go out together, in item order;
-    // every other product is one wq_gemm.
+    return WQ_OK;
+}
+
+// Sizes or launches a validated item list: X-resident products of one
+// (B, bits) go out together, in item order; every other product is one
+// wq_gemm.  Launches follow one another on the stream, so they share the
+// scratch (its size is the largest any of them needs).
+static wq_status run_items(const wq_gemm_item* items, int32_t count, int32_t* paths, const wq::Scratch& ws,
+                           hipStream_t st) {
     wq::XrProduct group_buf[64];
     for (int32_t i = 0; i < count; ++i) {
         const wq_gemm_item& it = items[i];
@@ -255,7 +361,7 @@ wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream
         const bool xr = paths[i] == WQ_PATH_MFMA && wq::xr_groupable(it.B, it.K, it.group, it.bits);
         if (!xr) {
             const wq_status s2 = run_gemm(it.X, it.codes, it.scales, it.zeros, it.Y, it.B, it.K, it.N,
-                                          it.group, it.bits, paths[i], st);
+                                          it.group, it.bits, paths[i], ws, st);
             if (s2 != WQ_OK) return s2;
             continue;
         }
@@ -270,21 +376,74 @@ wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream
             paths[j] = -1;  // issued
         }
         // (A product left alone in a launch keeps the single-call kernel.)
-        const wq_status s2 = check_hip(wq::launch_gemm_xr_many(group_buf, n, it.B, it.bits, num_cus(), st),
+        const wq_status s2 = check_hip(wq::launch_gemm_xr_many(group_buf, n, it.B, it.bits, num_cus(), ws, st),
                                        "wq_gemm_grouped (x-resident) launch");
         if (s2 != WQ_OK) return s2;
     }
     return WQ_OK;
 }
 
-// Validates a cache descriptor (not its contents) and copies it into `a`.
-static wq_status check_kv_cache(const wq_kv_cache* c, wq::KvCacheArgs& a) {
+wq_status wq_gemm_grouped_workspace_size(const wq_gemm_item* items, int32_t count, size_t* bytes) {
+    g_last_error[0] = '\0';
+    if (!bytes) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_grouped_workspace_size: null bytes");
+    *bytes = 0;
+    if (count < 0 || (count > 0 && !items))
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm_grouped: count=%lld, items=%lld (null)", count,
+                    (long long)(items != nullptr));
+    return with_paths(count, [&](int32_t* paths) {
+        wq_status st = check_items(items, count, paths);
+        if (st != WQ_OK) return st;
+        size_t need = 0;
+        wq::Scratch ws;
+        ws.need = &need;
+        st = run_items(items, count, paths, ws, nullptr);
+        if (st == WQ_OK) *bytes = need;
+        return st;
+    });
+}
+
+wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    g_last_error[0] = '\0';
+    if (count < 0 || (count > 0 && !items))
+        return fail(WQ_ERR_INVALID_ARG, "wq_gemm_grouped: count=%lld, items=%lld (null)", count,
+                    (long long)(items != nullptr));
+    return with_paths(count, [&](int32_t* paths) {
+        // Validate everything (and size the scratch) before enqueuing anything.
+        wq_status st = check_items(items, count, paths);
+        if (st != WQ_OK) return st;
+        size_t need = 0;
+        if (workspace) {
+            // Sizing marks issued items in paths; run it on a copy.
+            int32_t copy_small[64];
+            int32_t* copy = count <= 64 ? copy_small : new (std::nothrow) int32_t[count];
+            if (!copy) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_grouped: out of host memory (count=%lld)", count);
+            memcpy(copy, paths, sizeof(int32_t) * (size_t)count);
+            wq::Scratch sz;
+            sz.need = &need;
+            st = run_items(items, count, copy, sz, nullptr);
+            if (copy != copy_small) delete[] copy;
+            if (st != WQ_OK) return st;
+        }
+        st = check_workspace("wq_gemm_grouped", workspace, workspace_bytes, need);
+        if (st != WQ_OK) return st;
+        wq::Scratch ws;
+        ws.ptr = need > 0 ? workspace : nullptr;
+        return run_items(items, count, paths, ws, static_cast<hipStream_t>(stream));
+    });
+}
+
+// ---- KV cache ------------------------------------------------------------------
+
+// Validates a cache descriptor (not its contents) and copies it into `a`;
+// buffers are checked only when `buffers` is set.
+static wq_status check_kv_cache(const wq_kv_cache* c, wq::KvCacheArgs& a, bool buffers = true) {
     if (!c) return fail(WQ_ERR_INVALID_ARG, "kv cache: null descriptor");
     if (c->heads < 0 || c->max_blocks < 1 || c->heads > ((int64_t)1 << 31) - 1 ||
         c->max_blocks > ((int64_t)1 << 24))
         return fail(WQ_ERR_INVALID_ARG, "kv cache: need heads >= 0, 1 <= max_blocks <= 2^24 (heads=%lld max_blocks=%lld)",
                     c->heads, c->max_blocks);
-    if (c->heads > 0) {
+    if (buffers && c->heads > 0) {
         if (!c->kcodes || !c->kscales || !c->kzeros || !c->vcodes || !c->vscales || !c->vzeros || !c->kres ||
             !c->vres)
             return fail(WQ_ERR_INVALID_ARG, "kv cache: null buffer");
@@ -313,19 +472,49 @@ wq_status wq_kv_quantize_block(const void* K, const void* V, const wq_kv_cache* 
                      "wq_kv_quantize_block launch");
 }
 
+wq_status wq_kv_workspace_size(const wq_kv_cache* cache, size_t* bytes) {
+    g_last_error[0] = '\0';
+    if (!bytes) return fail(WQ_ERR_INVALID_ARG, "wq_kv_workspace_size: null bytes");
+    *bytes = 0;
+    wq::KvCacheArgs a;
+    const wq_status st = check_kv_cache(cache, a, false);
+    if (st != WQ_OK || a.heads == 0) return st;
+    size_t need = 0;
+    wq::Scratch ws;
+    ws.need = &need;
+    const wq_status s2 = check_hip(wq::launch_kv_attention(nullptr, a, nullptr, nullptr, num_cus(), ws, nullptr),
+                                   "wq_kv_workspace_size");
+    if (s2 == WQ_OK) *bytes = need;
+    return s2;
+}
+
 wq_status wq_kv_attention(const void* q, const wq_kv_cache* cache, const int32_t* lens, void* out,
-                          void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error[0] = '\0';
     wq::KvCacheArgs a;
-    const wq_status st = check_kv_cache(cache, a);
+    wq_status st = check_kv_cache(cache, a);
+    if (st != WQ_OK) return st;
+    size_t need = 0;
+    if (workspace && a.heads > 0) {
+        wq::Scratch sz;
+        sz.need = &need;
+        st = check_hip(wq::launch_kv_attention(nullptr, a, nullptr, nullptr, num_cus(), sz, nullptr),
+                       "wq_kv_attention sizing");
+        if (st != WQ_OK) return st;
+    }
+    st = check_workspace("wq_kv_attention", workspace, workspace_bytes, need);
     if (st != WQ_OK) return st;
     if (a.heads == 0) return WQ_OK;
     if (!q || !lens || !out) return fail(WQ_ERR_INVALID_ARG, "wq_kv_attention: null q, lens or out");
     if (!aligned(q, 2) || !aligned(out, 2) || !aligned(lens, 4))
         return fail(WQ_ERR_MISALIGNED, "wq_kv_attention: q/out need 2-byte and lens 4-byte alignment");
-    return check_hip(wq::launch_kv_attention(q, a, lens, out, num_cus(), static_cast<hipStream_t>(stream)),
+    wq::Scratch ws;
+    ws.ptr = need > 0 ? workspace : nullptr;
+    return check_hip(wq::launch_kv_attention(q, a, lens, out, num_cus(), ws, static_cast<hipStream_t>(stream)),
                      "wq_kv_attention launch");
 }
+
+// ---- other weight formats ------------------------------------------------------
 
 wq_status wq_gemm_offset(const void* X, const void* codes, const void* scales, const void* mins,
                          void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
@@ -365,12 +554,6 @@ wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void
     return check_hip(wq::launch_gemv_nf4(X, codes, scales, Y, B, K, N, group, num_cus(),
                                          static_cast<hipStream_t>(stream)),
                      "wq_gemm_nf4 launch");
-}
-
-wq_status wq_gemm(const void* X, const void* codes, const void* scales, const void* zeros,
-                  void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
-                  void* stream) {
-    return wq_gemm_ex(X, codes, scales, zeros, Y, B, K, N, group, bits, WQ_PATH_AUTO, stream);
 }
 
 }  // extern "C"

@@ -361,27 +361,28 @@ __global__ __launch_bounds__(256) void split_reduce4_kernel(const float4* __rest
 template <int BITS, int BT, int KS, int RB>
 hipError_t launch_bt(const void* X, const void* codes, const void* scales, const void* zeros,
                      void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int num_cus,
-                     hipStream_t stream) {
+                     const Scratch& ws, hipStream_t stream) {
     constexpr int RPS = KS / MfmaGeom<BITS>::KR;
     constexpr int BR = 64 * RB;
     const int64_t tiles = ((N + BR - 1) / BR) * ((B + BT - 1) / BT);
     const int64_t stages = (K / MfmaGeom<BITS>::KR + RPS - 1) / RPS;
     // Split K until about two blocks per compute unit are in flight, keeping
-    // at least two stages per split so that loads overlap compute.
+    // at least two stages per split so that loads overlap compute; the fp32
+    // partials of the splits go to the caller's scratch (one split without).
     int64_t want = (2 * (int64_t)num_cus + tiles - 1) / tiles;
     int64_t max_split = stages / 2 > 0 ? stages / 2 : 1;
     if (want > max_split) want = max_split;
     if (want < 1) want = 1;
+    if (!ws.sizing() && !ws.ptr) want = 1;
     int64_t sps = (stages + want - 1) / want;
     sps = (sps + 7) / 8 * 8;                          // whole 8-step loop bodies
     const int64_t splits = (stages + sps - 1) / sps;
-    const dim3 grid((unsigned)((N + BR - 1) / BR), (unsigned)((B + BT - 1) / BT), (unsigned)splits);
-    float* part = nullptr;
-    if (splits > 1) {
-        uint32_t* unused = nullptr;
-        hipError_t e = workspace_get(stream, 0, (size_t)splits * B * N * sizeof(float), &unused, &part);
-        if (e != hipSuccess) return e;
+    if (ws.sizing()) {
+        ws.want(splits > 1 ? (size_t)splits * B * N * sizeof(float) : 0);
+        return hipSuccess;
     }
+    const dim3 grid((unsigned)((N + BR - 1) / BR), (unsigned)((B + BT - 1) / BT), (unsigned)splits);
+    float* part = splits > 1 ? static_cast<float*>(ws.ptr) : nullptr;
     const bool hv = G == MfmaGeom<BITS>::KR && (K / G) % 8 == 0 &&
                     reinterpret_cast<uintptr_t>(scales) % 16 == 0 &&
                     reinterpret_cast<uintptr_t>(zeros) % 16 == 0;
@@ -418,16 +419,16 @@ hipError_t launch_bt(const void* X, const void* codes, const void* scales, const
 template <int BITS>
 hipError_t launch_bits(const void* X, const void* codes, const void* scales, const void* zeros,
                        void* Y, int64_t B, int64_t K, int64_t N, int32_t G, int cus,
-                       hipStream_t st) {
+                       const Scratch& ws, hipStream_t st) {
     constexpr int KR = MfmaGeom<BITS>::KR;
     const bool tall = N >= 64 * (int64_t)cus;
-    if (B <= 16) return launch_bt<BITS, 16, 2 * KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+    if (B <= 16) return launch_bt<BITS, 16, 2 * KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, ws, st);
     if (B <= 32) {
-        if (tall) return launch_bt<BITS, 32, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
-        return launch_bt<BITS, 32, KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+        if (tall) return launch_bt<BITS, 32, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, ws, st);
+        return launch_bt<BITS, 32, KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, ws, st);
     }
-    if (tall) return launch_bt<BITS, 64, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
-    return launch_bt<BITS, 64, KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, st);
+    if (tall) return launch_bt<BITS, 64, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, ws, st);
+    return launch_bt<BITS, 64, KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, ws, st);
 }
 
 }  // namespace
@@ -439,11 +440,17 @@ bool mfma_supports(int64_t K, int32_t group, int32_t bits) {
 
 hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales,
                             const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
-                            int32_t group, int32_t bits, int num_cus, hipStream_t stream) {
-    if (xr_supports(B, K, group, bits))
-        return launch_gemm_xr(X, codes, scales, zeros, Y, B, K, N, group, bits, num_cus, stream);
-    if (bits == 4) return launch_bits<4>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
-    return launch_bits<8>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+                            int32_t group, int32_t bits, int num_cus, const Scratch& ws,
+                            hipStream_t stream) {
+    // The X-resident kernel takes its shapes, but without scratch only when
+    // one K-slice holds all of X (its slices meet in fp32 partials).
+    const bool no_scratch = !ws.sizing() && !ws.ptr;
+    if (xr_supports(B, K, group, bits) && (!no_scratch || xr_single_slice(B, K, bits))) {
+        const XrProduct p{X, codes, scales, zeros, Y, K, N, group};
+        return launch_gemm_xr_many(&p, 1, B, bits, num_cus, ws, stream);
+    }
+    if (bits == 4) return launch_bits<4>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, ws, stream);
+    return launch_bits<8>(X, codes, scales, zeros, Y, B, K, N, group, num_cus, ws, stream);
 }
 
 }  // namespace wq

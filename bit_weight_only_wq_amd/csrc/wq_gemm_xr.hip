@@ -501,15 +501,17 @@ __global__ __launch_bounds__(256) void xr_reduce_kernel(const XrReduce R) {
 
 // Slices, rounds per slice and blocks per slice of one product.  Slices: as
 // few as LDS allows, more when the tiles alone cannot give every compute
-// unit's waves work (each slice keeps at least one ring turn).
+// unit's waves work (each slice keeps at least one ring turn), unless
+// `fewest` (no scratch for partials) holds them to the LDS minimum.
 template <int BITS, int BTX>
-bool xr_plan(int64_t K, int64_t N, int num_cus, int64_t& slices, int64_t& rs, int64_t& per_slice) {
+bool xr_plan(int64_t K, int64_t N, int num_cus, bool fewest, int64_t& slices, int64_t& rs,
+             int64_t& per_slice) {
     typedef XrGeom<BITS, BTX> XG;
     const int64_t rounds = K / XG::KR;
     const int64_t ntiles = (N + 15) / 16;
     slices = (rounds + XG::RMAX - 1) / XG::RMAX;
     const int64_t want_items = (int64_t)num_cus * XG::WAVES / 2;
-    if (ntiles * slices < want_items) {
+    if (!fewest && ntiles * slices < want_items) {
         const int64_t s = (want_items + ntiles - 1) / ntiles;
         const int64_t smax = (rounds + XR_SLOTS - 1) / XR_SLOTS;
         slices = s < smax ? s : smax;
@@ -560,10 +562,11 @@ int xr_mode(const XrProduct& p) {
 
 // One launch for up to XR_MAX_ITEMS products of one header mode, plus one
 // reduction launch for those of them that have several K-slices.  The fp32
-// partials of all of them share the stream's workspace.
+// partials of all of them share the caller's scratch (sized, not launched, in
+// sizing mode).
 template <int BITS, int BTX, int HM>
 hipError_t launch_xr_items(const XrProduct* const* prods, int n, int64_t B, int num_cus,
-                           hipStream_t stream) {
+                           const Scratch& ws, hipStream_t stream) {
     typedef XrGeom<BITS, BTX> XG;
     XrLaunch L{};
     XrReduce R{};
@@ -588,8 +591,9 @@ hipError_t launch_xr_items(const XrProduct* const* prods, int n, int64_t B, int 
     for (int i = 0; i < n; ++i) {
         const XrProduct& p = *prods[i];
         int64_t slices = 0, rs = 0, per_slice = 0;
+        const bool fewest = !ws.sizing() && !ws.ptr;
         const bool ok = n > 1 ? xr_plan_grouped<BITS, BTX>(p.K, p.N, per_wave, slices, rs, per_slice)
-                              : xr_plan<BITS, BTX>(p.K, p.N, num_cus, slices, rs, per_slice);
+                              : xr_plan<BITS, BTX>(p.K, p.N, num_cus, fewest, slices, rs, per_slice);
         if (!ok) return hipErrorInvalidValue;
         XrItem& it = L.it[i];
         it.X = static_cast<const uint16_t*>(p.X);
@@ -616,12 +620,12 @@ hipError_t launch_xr_items(const XrProduct* const* prods, int n, int64_t B, int 
     L.B = B;
     L.count = n;
     if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    float* base = nullptr;
-    if (part_total > 0) {
-        uint32_t* unused = nullptr;
-        const hipError_t e = workspace_get(stream, 0, part_total, &unused, &base);
-        if (e != hipSuccess) return e;
+    if (ws.sizing()) {
+        ws.want(part_total);
+        return hipSuccess;
     }
+    if (part_total > 0 && !ws.ptr) return hipErrorInvalidValue;   // callers route these elsewhere
+    float* base = static_cast<float*>(ws.ptr);
     int64_t t = 0;
     for (int i = 0; i < n; ++i) {
         XrItem& it = L.it[i];
@@ -650,12 +654,25 @@ hipError_t launch_xr_items(const XrProduct* const* prods, int n, int64_t B, int 
 // launches of at most XR_MAX_ITEMS products (in the given order within a mode).
 template <int BITS, int BTX>
 hipError_t launch_xr_bt(const XrProduct* prods, int count, int64_t B, int num_cus,
-                        hipStream_t stream) {
+                        const Scratch& ws, hipStream_t stream) {
+    // Without scratch, products whose X needs several K-slices run alone on
+    // the tiled kernel (one split); the others share launches as usual.
+    const bool no_scratch = !ws.sizing() && !ws.ptr;
+    if (no_scratch) {
+        for (int i = 0; i < count; ++i) {
+            const XrProduct& p = prods[i];
+            if (xr_single_slice(B, p.K, BITS)) continue;
+            const hipError_t e = launch_gemm_mfma(p.X, p.codes, p.scales, p.zeros, p.Y, B, p.K, p.N,
+                                                  p.group, BITS, num_cus, ws, stream);
+            if (e != hipSuccess) return e;
+        }
+    }
     for (int hm = 0; hm < 3; ++hm) {
         const XrProduct* sel[XR_MAX_ITEMS];
         int n = 0;
         for (int i = 0; i <= count; ++i) {
-            const bool take = i < count && xr_mode<BITS, BTX>(prods[i]) == hm;
+            const bool take = i < count && xr_mode<BITS, BTX>(prods[i]) == hm &&
+                              (!no_scratch || xr_single_slice(B, prods[i].K, BITS));
             if (take) sel[n++] = &prods[i];
             if (n == XR_MAX_ITEMS || (i == count && n > 0)) {
                 hipError_t e = hipSuccess;
@@ -663,10 +680,10 @@ hipError_t launch_xr_bt(const XrProduct* prods, int count, int64_t B, int num_cu
                 if (n == 1 && !xr_supports(B, p0.K, p0.group, BITS))
                     // Alone in its launch: the single-call choice of kernel.
                     e = launch_gemm_mfma(p0.X, p0.codes, p0.scales, p0.zeros, p0.Y, B, p0.K, p0.N,
-                                         p0.group, BITS, num_cus, stream);
-                else if (hm == XR_HDR_ROUND) e = launch_xr_items<BITS, BTX, XR_HDR_ROUND>(sel, n, B, num_cus, stream);
-                else if (hm == XR_HDR_TURN) e = launch_xr_items<BITS, BTX, XR_HDR_TURN>(sel, n, B, num_cus, stream);
-                else e = launch_xr_items<BITS, BTX, XR_HDR_ROW>(sel, n, B, num_cus, stream);
+                                         p0.group, BITS, num_cus, ws, stream);
+                else if (hm == XR_HDR_ROUND) e = launch_xr_items<BITS, BTX, XR_HDR_ROUND>(sel, n, B, num_cus, ws, stream);
+                else if (hm == XR_HDR_TURN) e = launch_xr_items<BITS, BTX, XR_HDR_TURN>(sel, n, B, num_cus, ws, stream);
+                else e = launch_xr_items<BITS, BTX, XR_HDR_ROW>(sel, n, B, num_cus, ws, stream);
                 if (e != hipSuccess) return e;
                 n = 0;
             }
@@ -692,24 +709,24 @@ bool xr_supports(int64_t B, int64_t K, int32_t group, int32_t bits) {
     return B <= 16 || K <= 4 * XrGeom<4, 32>::KSL;
 }
 
-hipError_t launch_gemm_xr_many(const XrProduct* prods, int count, int64_t B, int32_t bits,
-                               int num_cus, hipStream_t stream) {
-    if (count <= 0) return hipSuccess;
-    if (bits == 4) {
-        if (B <= 8) return launch_xr_bt<4, 8>(prods, count, B, num_cus, stream);
-        if (B <= 16) return launch_xr_bt<4, 16>(prods, count, B, num_cus, stream);
-        return launch_xr_bt<4, 32>(prods, count, B, num_cus, stream);
-    }
-    if (B <= 8) return launch_xr_bt<8, 8>(prods, count, B, num_cus, stream);
-    if (B <= 16) return launch_xr_bt<8, 16>(prods, count, B, num_cus, stream);
-    return launch_xr_bt<8, 32>(prods, count, B, num_cus, stream);
+bool xr_single_slice(int64_t B, int64_t K, int32_t bits) {
+    // The slice length of the batch tile wq_gemm_xr_many picks for B.
+    const int64_t ksl = B <= 8 ? XrGeom<4, 8>::KSL : B <= 16 ? XrGeom<4, 16>::KSL : XrGeom<4, 32>::KSL;
+    (void)bits;   // the slice holds k values, whatever their code width
+    return K <= ksl;
 }
 
-hipError_t launch_gemm_xr(const void* X, const void* codes, const void* scales,
-                          const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
-                          int32_t group, int32_t bits, int num_cus, hipStream_t stream) {
-    const XrProduct p{X, codes, scales, zeros, Y, K, N, group};
-    return launch_gemm_xr_many(&p, 1, B, bits, num_cus, stream);
+hipError_t launch_gemm_xr_many(const XrProduct* prods, int count, int64_t B, int32_t bits,
+                               int num_cus, const Scratch& ws, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    if (bits == 4) {
+        if (B <= 8) return launch_xr_bt<4, 8>(prods, count, B, num_cus, ws, stream);
+        if (B <= 16) return launch_xr_bt<4, 16>(prods, count, B, num_cus, ws, stream);
+        return launch_xr_bt<4, 32>(prods, count, B, num_cus, ws, stream);
+    }
+    if (B <= 8) return launch_xr_bt<8, 8>(prods, count, B, num_cus, ws, stream);
+    if (B <= 16) return launch_xr_bt<8, 16>(prods, count, B, num_cus, ws, stream);
+    return launch_xr_bt<8, 32>(prods, count, B, num_cus, ws, stream);
 }
 
 }  // namespace wq

@@ -493,15 +493,17 @@ int kv_splits(int64_t heads, int64_t max_blocks, int num_cus) {
 }
 
 hipError_t launch_kv_attention(const void* q, const KvCacheArgs& c, const int32_t* lens, void* out,
-                               int num_cus, hipStream_t stream) {
-    const int splits = kv_splits(c.heads, c.max_blocks, num_cus);
-    float* part = nullptr;
-    if (splits > 1) {
-        uint32_t* unused = nullptr;
-        const hipError_t e = workspace_get(stream, 0, (size_t)c.heads * splits * (kD + 4) * sizeof(float),
-                                           &unused, &part);
-        if (e != hipSuccess) return e;
+                               int num_cus, const Scratch& ws, hipStream_t stream) {
+    // Context splits write (max, sum, output row) partials into the scratch;
+    // without scratch every head is one split.
+    const int planned = kv_splits(c.heads, c.max_blocks, num_cus);
+    const size_t part_bytes = planned > 1 ? (size_t)c.heads * planned * (kD + 4) * sizeof(float) : 0;
+    if (ws.sizing()) {
+        ws.want(part_bytes);
+        return hipSuccess;
     }
+    const int splits = ws.ptr ? planned : 1;
+    float* part = splits > 1 ? static_cast<float*>(ws.ptr) : nullptr;
     const KvPtrs P{static_cast<const uint8_t*>(c.kcodes), static_cast<const uint16_t*>(c.kscales),
                    static_cast<const uint16_t*>(c.kzeros), static_cast<const uint8_t*>(c.vcodes),
                    static_cast<const uint16_t*>(c.vscales), static_cast<const uint16_t*>(c.vzeros),

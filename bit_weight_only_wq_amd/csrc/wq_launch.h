@@ -6,11 +6,31 @@
 
 namespace wq {
 
+// Caller-owned scratch of one call.  Every launcher that can use scratch runs
+// in one of two modes:
+//   - sizing (need != nullptr): nothing is launched; *need is raised to the
+//     bytes the call's preferred plan uses (the largest of its launches, which
+//     run one after another on the stream and so share the buffer);
+//   - launching (need == nullptr): with ptr set (at least the sized bytes,
+//     16-byte aligned) the preferred plan runs; with ptr null a plan that
+//     needs no scratch runs instead.
+// Both modes take the same decisions, so the size always matches the launch.
+struct Scratch {
+    void* ptr = nullptr;
+    size_t* need = nullptr;
+    bool sizing() const { return need != nullptr; }
+    void want(size_t bytes) const {
+        if (need && *need < bytes) *need = bytes;
+    }
+};
+
 // scheme: 0 asymmetric, 1 symmetric per group, 2 symmetric per tensor (the
-// last takes the stream's workspace for its maximum).
+// last needs scratch for its maximum: quantize_scratch_bytes), 3 NF4,
+// 4 float offset.
+size_t quantize_scratch_bytes(int32_t scheme);
 hipError_t launch_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
                                 int32_t bits, int32_t scheme, void* codes, void* scales,
-                                void* zeros, hipStream_t stream);
+                                void* zeros, void* scratch, hipStream_t stream);
 
 // Codes + headers -> fp32 W [N, K] for any scheme (see wq_dequant.hip).
 hipError_t launch_dequantize(const void* codes, const void* scales, const void* zeros, void* W,
@@ -43,13 +63,14 @@ bool xr_supports(int64_t B, int64_t K, int32_t group, int32_t bits);
 // Shapes the X-resident kernel can take at all (a superset of xr_supports:
 // beyond it, it is chosen only when other products share the launch).
 bool xr_groupable(int64_t B, int64_t K, int32_t group, int32_t bits);
-hipError_t launch_gemm_xr(const void* X, const void* codes, const void* scales,
-                          const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
-                          int32_t group, int32_t bits, int num_cus, hipStream_t stream);
+// Whether the X-resident kernel takes the product without scratch (one
+// K-slice holds all of X).
+bool xr_single_slice(int64_t B, int64_t K, int32_t bits);
 // Several X-resident products of one batch size and bit width (each must
 // satisfy xr_groupable): products sharing a header mode go into one launch of
 // up to eight, with one reduction launch for their K-slices; a product alone
-// in its launch that xr_supports rejects runs on the tiled kernel instead.
+// in its launch that xr_supports rejects runs on the tiled kernel instead, and
+// so does, without scratch, a product whose X needs several K-slices.
 struct XrProduct {
     const void* X;
     const void* codes;
@@ -60,11 +81,14 @@ struct XrProduct {
     int32_t group;
 };
 hipError_t launch_gemm_xr_many(const XrProduct* prods, int count, int64_t B, int32_t bits,
-                               int num_cus, hipStream_t stream);
+                               int num_cus, const Scratch& ws, hipStream_t stream);
 bool mfma_supports(int64_t K, int32_t group, int32_t bits);
+// Matrix-core product (X-resident kernel when it takes the shape, else the
+// tiled kernel); scratch holds fp32 split-K partials.
 hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales,
                             const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
-                            int32_t group, int32_t bits, int num_cus, hipStream_t stream);
+                            int32_t group, int32_t bits, int num_cus, const Scratch& ws,
+                            hipStream_t stream);
 
 // int4 KV cache of `heads` heads (head dimension 128, blocks of 128 tokens,
 // `max_blocks` blocks per head); layouts in wq_kv.hip.
@@ -80,15 +104,11 @@ struct KvCacheArgs {
     int64_t heads, max_blocks;
 };
 int kv_splits(int64_t heads, int64_t max_blocks, int num_cus);
+// Scratch holds the fp32 partials of the context splits; without it every
+// head runs as one split.
 hipError_t launch_kv_attention(const void* q, const KvCacheArgs& c, const int32_t* lens, void* out,
-                               int num_cus, hipStream_t stream);
+                               int num_cus, const Scratch& ws, hipStream_t stream);
 hipError_t launch_kv_quantize(const void* K, const void* V, const KvCacheArgs& c, int64_t block,
                               hipStream_t stream);
-
-// Split-K workspace of the calling device and `stream`: counter_words zeroed
-// 32-bit counters (a kernel that uses them leaves them at zero) and part_bytes
-// of fp32 partials, reused by later calls on the same stream.
-hipError_t workspace_get(hipStream_t stream, size_t counter_words, size_t part_bytes,
-                         uint32_t** counters, float** part);
 
 }  // namespace wq

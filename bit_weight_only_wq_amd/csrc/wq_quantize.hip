@@ -500,24 +500,26 @@ hipError_t launch_bits(const void* W, int64_t N, int64_t K, int32_t G, void* cod
 
 }  // namespace
 
+size_t quantize_scratch_bytes(int32_t scheme) {
+    return scheme == 2 ? (size_t)(kAmaxBlocks + 1) * sizeof(uint32_t) : 0;
+}
+
 hipError_t launch_quantize_pack(const void* W, int64_t N, int64_t K, int32_t group,
                                 int32_t bits, int32_t scheme, void* codes, void* scales,
-                                void* zeros, hipStream_t stream) {
+                                void* zeros, void* scratch, hipStream_t stream) {
     const uint32_t* amax = nullptr;
     if (scheme == 2) {
-        // Two reduction launches into the stream's workspace: kAmaxBlocks
+        // Two reduction launches into the caller's scratch: kAmaxBlocks
         // partials, then the maximum in the word after them.
-        uint32_t* unused = nullptr;
-        float* part = nullptr;
-        hipError_t e = workspace_get(stream, 0, (kAmaxBlocks + 1) * sizeof(uint32_t), &unused, &part);
-        if (e != hipSuccess) return e;
-        uint32_t* words = reinterpret_cast<uint32_t*>(part);
+        if (!scratch) return hipErrorInvalidValue;
+        uint32_t* words = static_cast<uint32_t*>(scratch);
         const int64_t nchunks = N * K / 8;
         const int64_t want = (nchunks + 255) / 256;
         const int blocks = (int)(want < kAmaxBlocks ? (want < 1 ? 1 : want) : kAmaxBlocks);
         amax_partial_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
             static_cast<const uint16_t*>(W), nchunks, words);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
         amax_final_kernel<<<dim3(1), dim3(256), 0, stream>>>(words, blocks, words + kAmaxBlocks);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         amax = words + kAmaxBlocks;

@@ -25,15 +25,23 @@
  *
  * Conventions shared by every entry point:
  *   - All array pointers are DEVICE pointers to row-major, contiguous buffers
- *     that the caller allocates, owns and frees.  The only memory the library
- *     allocates itself is a workspace: the fp32 split-K partials of the MFMA
- *     paths (B * N * 4 bytes per K split) and the few KB of the per-tensor
- *     maximum of wq_quantize_pack_ex: one buffer per (device, stream), taken in
- *     stream order (hipMallocAsync on `stream`) the first time a call on that
- *     stream needs it, grown the same way when a later call needs more, and
- *     kept for reuse until the process ends.  Calls on one stream reuse it in
- *     stream order; calls on different streams never share it.  A failure
- *     there is reported as WQ_ERR_HIP.
+ *     that the caller allocates, owns and frees.  The library allocates no
+ *     device memory and keeps no state beyond a lazily cached device property
+ *     (the compute-unit count).
+ *   - Workspace.  Some calls can use scratch memory (fp32 partial sums when
+ *     the product or the attention splits its work, the per-tensor maximum of
+ *     the symmetric quantizer).  They take `workspace` (a device pointer,
+ *     16-byte aligned) and `workspace_bytes`, and a matching
+ *     wq_*_workspace_size query returns the bytes the call needs on the
+ *     current device (0 if none).  workspace = NULL with workspace_bytes = 0
+ *     means none: the call then takes a plan that needs no scratch (fewer work
+ *     splits; same results within the product tolerance), except the
+ *     per-tensor quantizer, which then fails with WQ_ERR_INVALID_ARG.  A
+ *     workspace smaller than the query's answer is WQ_ERR_INVALID_ARG, a
+ *     misaligned one WQ_ERR_MISALIGNED, both before any launch.  Its contents
+ *     on entry do not matter; the call overwrites what it uses.  The
+ *     workspace belongs to the call until the stream has run it: calls that
+ *     may overlap (different streams) need different workspaces.
  *   - `stream` is a hipStream_t (NULL means the default stream).  Work is
  *     enqueued on it and the call returns at once; the library never
  *     synchronizes.  Buffers must stay alive until the stream has run the work.
@@ -117,7 +125,8 @@ typedef enum {
  * repeated in every group header), so wq_gemm multiplies by q * s unchanged.
  * Arguments, layout and errors as wq_quantize_pack; an unknown scheme is
  * WQ_ERR_INVALID_ARG.  WQ_SCHEME_SYM_TENSOR enqueues two small reduction
- * launches before the quantize launch and uses the stream's workspace.
+ * launches before the quantize launch and needs a workspace
+ * (wq_quantize_workspace_size; 4100 bytes), the other schemes none.
  *
  * WQ_SCHEME_NF4 ("Gör inference billig: KV cache, batching och
  * kvantisering", the NF4 paragraph; bits must be 4, else
@@ -136,7 +145,14 @@ typedef enum {
  */
 wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group,
                               int32_t bits, int32_t scheme, void* codes, void* scales,
-                              void* zeros, void* stream);
+                              void* zeros, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Workspace bytes wq_quantize_pack_ex needs for these arguments (0 unless
+ * scheme is WQ_SCHEME_SYM_TENSOR); errors as wq_quantize_pack_ex's shape
+ * checks, *bytes = 0 then. */
+wq_status wq_quantize_workspace_size(int64_t N, int64_t K, int32_t group, int32_t bits,
+                                     int32_t scheme, size_t* bytes);
 
 /*
  * Decode-step product with in-register dequantization ("Quantization &
@@ -159,17 +175,28 @@ wq_status wq_quantize_pack_ex(const void* W, int64_t N, int64_t K, int32_t group
  * batch rows, so large batches are correct but not fast); bits 1, 5, 6 and 7
  * are WQ_ERR_UNSUPPORTED.
  * Results are deterministic: no atomics, fixed reduction order.
+ * wq_gemm takes no workspace: it runs plans that need none (the matrix-core
+ * kernels without K splits).  wq_gemm_ex with a workspace is faster where
+ * splitting K pays (few rows, or X too large for one block's LDS).
  */
 wq_status wq_gemm(const void* X, const void* codes, const void* scales,
                   const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                   int32_t group, int32_t bits, void* stream);
 
 /* wq_gemm with an explicit kernel family (for benchmarks and parity tests of
- * each path).  Returns WQ_ERR_UNSUPPORTED if the forced path cannot take the
- * shape. */
+ * each path) and a workspace (see the conventions above; size from
+ * wq_gemm_workspace_size with the same shape and path).  Returns
+ * WQ_ERR_UNSUPPORTED if the forced path cannot take the shape. */
 wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales,
                      const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
-                     int32_t group, int32_t bits, int32_t path, void* stream);
+                     int32_t group, int32_t bits, int32_t path, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Workspace bytes wq_gemm_ex needs for this shape and path on the current
+ * device (0: none).  Errors as wq_gemm_ex's shape checks (no pointers are
+ * involved); *bytes = 0 then. */
+wq_status wq_gemm_workspace_size(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                                 int32_t path, size_t* bytes);
 
 /*
  * Product with NF4 weights (codes and scales from wq_quantize_pack_ex with
@@ -229,9 +256,16 @@ typedef struct wq_gemm_item {
  * Every item is validated as by wq_gemm before anything is enqueued; the
  * first invalid item's status is returned (wq_last_error names the item) and
  * nothing runs.  An item's Y must not overlap any item's inputs or another
- * item's Y.  Items share the stream's split-K workspace.
+ * item's Y.  The launches of a call run one after another and share the
+ * workspace (wq_gemm_grouped_workspace_size); without one, products whose X
+ * needs several K-slices run alone, as wq_gemm.
  */
-wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* stream);
+wq_status wq_gemm_grouped(const wq_gemm_item* items, int32_t count, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes wq_gemm_grouped needs for this item list on the current
+ * device (0: none).  Items are validated as by wq_gemm_grouped. */
+wq_status wq_gemm_grouped_workspace_size(const wq_gemm_item* items, int32_t count, size_t* bytes);
 
 /* Largest batch that WQ_PATH_AUTO sends to the GEMV path when the MFMA path
  * can take the shape. */
@@ -321,13 +355,18 @@ wq_status wq_kv_quantize_block(const void* K, const void* V, const wq_kv_cache* 
  * q, out  fp16 [heads][128] (q 2-byte aligned, out 2-byte aligned)
  * lens    int32 [heads], DEVICE memory: tokens held by each head; values are
  *         clamped to [0, max_blocks * 128 + 127] (a head with 0 tokens gives 0)
- * fp32 scores, softmax and accumulation; the context is split over several
- * workgroups per head when there are few heads (the partials use the
- * stream's workspace).  Tolerance against the float64 oracle: the product
- * tolerance (max|d| <= 1e-2 max|ref|, rel L2 <= 1e-3).
+ * fp32 scores, softmax and accumulation; with a workspace
+ * (wq_kv_workspace_size) the context is split over several workgroups per
+ * head when there are few heads, without one each head is one workgroup.
+ * Tolerance against the float64 oracle: the product tolerance
+ * (max|d| <= 1e-2 max|ref|, rel L2 <= 1e-3).
  */
 wq_status wq_kv_attention(const void* q, const wq_kv_cache* cache, const int32_t* lens,
-                          void* out, void* stream);
+                          void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes wq_kv_attention needs for this cache on the current device
+ * (only heads and max_blocks are read; 0: none). */
+wq_status wq_kv_workspace_size(const wq_kv_cache* cache, size_t* bytes);
 
 /* Static description of a status code. */
 const char* wq_status_string(wq_status s);
@@ -338,7 +377,7 @@ const char* wq_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int32_t wq_version(void);
 
-#define WQ_VERSION 106
+#define WQ_VERSION 200
 
 #ifdef __cplusplus
 }

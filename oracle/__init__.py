@@ -83,6 +83,8 @@ def _load():
             f.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -98,6 +100,11 @@ def _check(rc: int):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of later oracle calls (for timing; results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 SCHEMES = ("asym", "sym", "sym_tensor", "offset")

@@ -549,3 +549,15 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads later calls use (timing of the oracle on
+ * one core and on all of them; no effect on any result). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

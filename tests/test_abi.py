@@ -15,8 +15,8 @@ from bit_weight_only_wq_amd import _lib  # noqa: E402
 HEADER = os.path.join(ROOT, "include", "wq.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", text)))
 
@@ -31,9 +31,31 @@ def test_library_exports_every_declared_symbol():
     assert sorted(_lib.SIGNATURES) == names
 
 
+def test_probe_library_exports_its_header():
+    """include/wq_probe.h is the read-stream probe's own library."""
+    from bit_weight_only_wq_amd import probe
+    lib = probe.load()
+    names = declared_functions(os.path.join(ROOT, "include", "wq_probe.h"))
+    assert names == ["wq_probe_read"]
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(probe.SIGNATURES) == names
+    # Rejected before any launch: bad lane count, depth, order, shape, alignment.
+    r = lambda **kw: lib.wq_probe_read(kw.get("buf", FAKE), kw.get("rows", 64), kw.get("row_bytes", 4096),
+                                       kw.get("L", 16), kw.get("D", 8), kw.get("order", 0), 1, 2,
+                                       kw.get("sink", FAKE), None)
+    assert r(L=12) == 2
+    assert r(D=3) == 2
+    assert r(order=3) == 1
+    assert r(rows=63) == 1                     # 4 rows per strip at L = 16
+    assert r(row_bytes=4000) == 1
+    assert r(buf=FAKE + 8) == 3
+    assert r(buf=0) == 1
+
+
 def test_version_and_status_strings():
     lib = wq.load()
-    assert lib.wq_version() == 106
+    assert lib.wq_version() == 200
     for st in range(5):
         assert lib.wq_status_string(st)
     assert lib.wq_status_string(99) == b"unknown status"
@@ -52,7 +74,7 @@ FAKE = 0x100000  # 16-byte aligned, never dereferenced (validation fails first)
 
 
 def _gemm(B=4, K=256, N=64, group=128, bits=4, path=0, X=FAKE, C=FAKE, S=FAKE, Z=FAKE, Y=FAKE):
-    return wq.load().wq_gemm_ex(X, C, S, Z, Y, B, K, N, group, bits, path, None)
+    return wq.load().wq_gemm_ex(X, C, S, Z, Y, B, K, N, group, bits, path, None, 0, None)
 
 
 def _quant(N=64, K=256, group=128, bits=4, W=FAKE, C=FAKE, S=FAKE, Z=FAKE):
@@ -105,7 +127,7 @@ def test_quantize_validation_errors():
 
 
 def _quant_ex(scheme, N=64, K=256, group=128, bits=4, W=FAKE, C=FAKE, S=FAKE, Z=FAKE):
-    return wq.load().wq_quantize_pack_ex(W, N, K, group, bits, scheme, C, S, Z, None)
+    return wq.load().wq_quantize_pack_ex(W, N, K, group, bits, scheme, C, S, Z, None, 0, None)
 
 
 def test_quantize_ex_validation_errors():
@@ -136,14 +158,14 @@ def test_grouped_validates_every_item_first():
     for bad, st in [(dict(K=200), _lib.WQ_ERR_INVALID_ARG), (dict(bits=5), _lib.WQ_ERR_UNSUPPORTED),
                     (dict(X=FAKE + 2), _lib.WQ_ERR_MISALIGNED), (dict(Y=0), _lib.WQ_ERR_INVALID_ARG)]:
         arr = (_lib.GemmItem * 3)(_item(), _item(B=32), _item(**bad))
-        assert lib.wq_gemm_grouped(arr, 3, None) == st
+        assert lib.wq_gemm_grouped(arr, 3, None, 0, None) == st
         assert b"item 2" in lib.wq_last_error()
-    assert lib.wq_gemm_grouped(None, 2, None) == _lib.WQ_ERR_INVALID_ARG
-    assert lib.wq_gemm_grouped(None, -1, None) == _lib.WQ_ERR_INVALID_ARG
-    assert lib.wq_gemm_grouped(None, 0, None) == _lib.WQ_OK
+    assert lib.wq_gemm_grouped(None, 2, None, 0, None) == _lib.WQ_ERR_INVALID_ARG
+    assert lib.wq_gemm_grouped(None, -1, None, 0, None) == _lib.WQ_ERR_INVALID_ARG
+    assert lib.wq_gemm_grouped(None, 0, None, 0, None) == _lib.WQ_OK
     # No-op items (B == 0 or N == 0) are valid and enqueue nothing.
     arr = (_lib.GemmItem * 2)(_item(B=0), _item(N=0))
-    assert lib.wq_gemm_grouped(arr, 2, None) == _lib.WQ_OK
+    assert lib.wq_gemm_grouped(arr, 2, None, 0, None) == _lib.WQ_OK
 
 
 def _cache(heads=4, max_blocks=2, **kw):
@@ -160,7 +182,7 @@ def test_kv_validation_errors():
     q = lib.wq_kv_quantize_block
     a = lib.wq_kv_attention
     assert q(FAKE, FAKE, None, 0, None) == _lib.WQ_ERR_INVALID_ARG
-    assert a(FAKE, None, FAKE, FAKE, None) == _lib.WQ_ERR_INVALID_ARG
+    assert a(FAKE, None, FAKE, FAKE, None, 0, None) == _lib.WQ_ERR_INVALID_ARG
     assert q(FAKE, FAKE, ctypes.byref(_cache(max_blocks=0)), 0, None) == _lib.WQ_ERR_INVALID_ARG
     assert q(FAKE, FAKE, ctypes.byref(_cache(heads=-1)), 0, None) == _lib.WQ_ERR_INVALID_ARG
     assert q(FAKE, FAKE, ctypes.byref(_cache()), 2, None) == _lib.WQ_ERR_INVALID_ARG
@@ -169,12 +191,12 @@ def test_kv_validation_errors():
     assert q(FAKE + 8, FAKE, ctypes.byref(_cache()), 0, None) == _lib.WQ_ERR_MISALIGNED
     assert q(FAKE, FAKE, ctypes.byref(_cache(vcodes=0)), 0, None) == _lib.WQ_ERR_INVALID_ARG
     assert q(FAKE, FAKE, ctypes.byref(_cache(kres=FAKE + 2)), 0, None) == _lib.WQ_ERR_MISALIGNED
-    assert a(FAKE, ctypes.byref(_cache()), 0, FAKE, None) == _lib.WQ_ERR_INVALID_ARG
-    assert a(FAKE, ctypes.byref(_cache()), FAKE + 2, FAKE, None) == _lib.WQ_ERR_MISALIGNED
-    assert a(FAKE + 1, ctypes.byref(_cache()), FAKE, FAKE, None) == _lib.WQ_ERR_MISALIGNED
+    assert a(FAKE, ctypes.byref(_cache()), 0, FAKE, None, 0, None) == _lib.WQ_ERR_INVALID_ARG
+    assert a(FAKE, ctypes.byref(_cache()), FAKE + 2, FAKE, None, 0, None) == _lib.WQ_ERR_MISALIGNED
+    assert a(FAKE + 1, ctypes.byref(_cache()), FAKE, FAKE, None, 0, None) == _lib.WQ_ERR_MISALIGNED
     # No heads: nothing to do.
     assert q(0, 0, ctypes.byref(_cache(heads=0, kcodes=0)), 0, None) == _lib.WQ_OK
-    assert a(0, ctypes.byref(_cache(heads=0)), 0, 0, None) == _lib.WQ_OK
+    assert a(0, ctypes.byref(_cache(heads=0)), 0, 0, None, 0, None) == _lib.WQ_OK
 
 
 def test_nf4_validation_errors():
@@ -229,3 +251,95 @@ def test_dequantize_validation_errors():
     assert _deq(-1) == _lib.WQ_ERR_INVALID_ARG
     assert _deq(_lib.WQ_SCHEME_NF4, bits=3) == _lib.WQ_ERR_UNSUPPORTED
     assert b"wq_dequantize" in wq.load().wq_last_error()
+
+
+# ---- caller-owned workspace -------------------------------------------------
+
+
+def _gemm_ws_size(B, K=8192, N=28672, group=128, bits=4, path=0):
+    import ctypes
+    n = ctypes.c_size_t(123)
+    st = wq.load().wq_gemm_workspace_size(B, K, N, group, bits, path, ctypes.byref(n))
+    return st, n.value
+
+
+def test_gemm_workspace_size_queries():
+    """The size query validates the shape like the call and reports the bytes
+    of the split partials the preferred plan writes (0 when it has none)."""
+    st, n = _gemm_ws_size(1)
+    assert st == _lib.WQ_OK and n == 0                   # GEMV: no scratch
+    st, n = _gemm_ws_size(16)
+    assert st == _lib.WQ_OK and n > 0 and n % (16 * 28672 * 4) == 0   # X needs two K-slices
+    st, n = _gemm_ws_size(0)
+    assert st == _lib.WQ_OK and n == 0                   # no-op
+    st, n = _gemm_ws_size(16, K=250)
+    assert st == _lib.WQ_ERR_INVALID_ARG and n == 0
+    st, n = _gemm_ws_size(2, bits=5)
+    assert st == _lib.WQ_ERR_UNSUPPORTED and n == 0
+    assert wq.load().wq_gemm_workspace_size(1, 256, 64, 128, 4, 0, None) == _lib.WQ_ERR_INVALID_ARG
+
+
+def test_gemm_workspace_rejected_before_launch():
+    """An undersized, misaligned, or null-with-a-size workspace is refused
+    before anything is enqueued (the fake pointers are never used)."""
+    lib = wq.load()
+    st, need = _gemm_ws_size(16)
+    assert need > 0
+    call = lambda ws, n: lib.wq_gemm_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8192, 28672, 128, 4, 0, ws, n, None)
+    assert call(FAKE, need - 1) == _lib.WQ_ERR_INVALID_ARG
+    assert b"needs" in lib.wq_last_error()
+    assert call(FAKE, 0) == _lib.WQ_ERR_INVALID_ARG
+    assert call(None, 64) == _lib.WQ_ERR_INVALID_ARG
+    assert call(FAKE + 8, need) == _lib.WQ_ERR_MISALIGNED
+    # A no-op call accepts no workspace and rejects a bad one.
+    noop = lambda ws, n: lib.wq_gemm_ex(0, FAKE, FAKE, FAKE, 0, 0, 8192, 28672, 128, 4, 0, ws, n, None)
+    assert noop(None, 0) == _lib.WQ_OK
+    assert noop(None, 8) == _lib.WQ_ERR_INVALID_ARG
+
+
+def test_grouped_workspace_size_and_rejection():
+    import ctypes
+    lib = wq.load()
+    arr = (_lib.GemmItem * 2)(_item(B=16, K=8192, N=28672), _item(B=1, K=8192, N=28672))
+    n = ctypes.c_size_t(0)
+    assert lib.wq_gemm_grouped_workspace_size(arr, 2, ctypes.byref(n)) == _lib.WQ_OK
+    assert n.value > 0
+    assert lib.wq_gemm_grouped(arr, 2, FAKE, n.value - 16, None) == _lib.WQ_ERR_INVALID_ARG
+    bad = (_lib.GemmItem * 1)(_item(K=200))
+    assert lib.wq_gemm_grouped_workspace_size(bad, 1, ctypes.byref(n)) == _lib.WQ_ERR_INVALID_ARG
+    assert b"item 0" in lib.wq_last_error()
+
+
+def test_kv_and_quantize_workspace():
+    import ctypes
+    lib = wq.load()
+    n = ctypes.c_size_t(0)
+    # Few heads, long context: the attention splits the context.
+    assert lib.wq_kv_workspace_size(ctypes.byref(_cache(heads=32, max_blocks=256)), ctypes.byref(n)) == _lib.WQ_OK
+    assert n.value > 0 and n.value % (32 * (128 + 4) * 4) == 0
+    need = n.value
+    a = lib.wq_kv_attention
+    assert a(FAKE, ctypes.byref(_cache(heads=32, max_blocks=256)), FAKE, FAKE, FAKE, need - 4, None) == \
+        _lib.WQ_ERR_INVALID_ARG
+    assert lib.wq_kv_workspace_size(ctypes.byref(_cache(heads=0)), ctypes.byref(n)) == _lib.WQ_OK and n.value == 0
+    # The per-tensor symmetric quantizer needs scratch for its maximum.
+    for scheme, want in ((_lib.WQ_SCHEME_ASYM, 0), (_lib.WQ_SCHEME_SYM_TENSOR, 4100)):
+        assert lib.wq_quantize_workspace_size(64, 256, 128, 4, scheme, ctypes.byref(n)) == _lib.WQ_OK
+        assert n.value == want
+    q = lambda ws, nb: lib.wq_quantize_pack_ex(FAKE, 64, 256, 128, 4, _lib.WQ_SCHEME_SYM_TENSOR, FAKE, FAKE,
+                                               FAKE, ws, nb, None)
+    assert q(None, 0) == _lib.WQ_ERR_INVALID_ARG
+    assert b"workspace" in lib.wq_last_error()
+    assert q(FAKE, 4099) == _lib.WQ_ERR_INVALID_ARG
+
+
+def test_library_sources_allocate_nothing():
+    """The HIP sources call no device or host allocator: every buffer is the
+    caller's."""
+    src = os.path.join(ROOT, "bit_weight_only_wq_amd", "csrc")
+    pat = re.compile(r"\b(hipMalloc\w*|hipFree\w*|hipHostMalloc|hipMallocManaged|hipExtMallocWithFlags)\s*\(")
+    for dirpath, _, files in os.walk(src):
+        for f in files:
+            if f.endswith((".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not pat.search(text), f

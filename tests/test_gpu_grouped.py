@@ -87,6 +87,11 @@ def test_mixed_items_match_single_calls():
     outs = wq.gemm_grouped(items)
     assert_matches_single(outs, items)
     assert_matches_oracle(outs, items, [m[1] for m in made], rng)
+    # Without a workspace every product takes a plan with no K-split partials.
+    note(f"grouped mixed without workspace: {len(items)} items")
+    bare = wq.gemm_grouped(items, use_workspace=False)
+    torch.cuda.synchronize()
+    assert_matches_oracle(bare, items, [m[1] for m in made], rng)
 
 
 def test_more_than_eight_grouped_products():
@@ -101,8 +106,9 @@ def test_more_than_eight_grouped_products():
     assert_matches_oracle(outs, items, [m[1] for m in made], rng)
 
 
+@pytest.mark.parametrize("use_ws", [True, False])
 @pytest.mark.parametrize("bits,group", [(4, 128), (8, None)])
-def test_decode_layer_at_b32(bits, group):
+def test_decode_layer_at_b32(bits, group, use_ws):
     """The seven matrices of a 7B-class layer (int4 g128 or 8-bit per-channel)
     at B = 32 in one call, each checked against the oracle on sampled rows."""
     device()
@@ -114,9 +120,10 @@ def test_decode_layer_at_b32(bits, group):
         it, h = make_item(rng, 32, N, K, G, bits, host=True)
         items.append(it)
         hosts.append(h)
-    note(f"grouped decode layer b={bits}")
-    outs = wq.gemm_grouped(items)
-    assert_matches_single(outs, items)
+    note(f"grouped decode layer b={bits} workspace={use_ws}")
+    outs = wq.gemm_grouped(items, use_workspace=use_ws)
+    if use_ws:
+        assert_matches_single(outs, items)
     assert_matches_oracle(outs, items, hosts, rng, nrows=48)
 
 

@@ -90,9 +90,11 @@ def test_quantize_block_bit_exact():
     assert not cache.kcodes[:, 1].any() and not cache.vcodes[:, 1].any()
 
 
+@pytest.mark.parametrize("use_ws", [True, False])
 @pytest.mark.parametrize("max_blocks", [32, 1])
-def test_attention_ragged_lengths(max_blocks):
-    """max_blocks 32: many splits per head (some empty); 1: one split."""
+def test_attention_ragged_lengths(max_blocks, use_ws):
+    """max_blocks 32: many splits per head (some empty) with a workspace, one
+    workgroup per head without; max_blocks 1: one split."""
     device()
     rng = np.random.default_rng(2 + max_blocks)
     lens = [0, 1, 5, 127, 128, 129, 255, 256, 300, 1000, 4096]
@@ -100,14 +102,15 @@ def test_attention_ragged_lengths(max_blocks):
         lens = [0, 1, 127, 128, 129, 200, 255]
     heads = [draw_kv(rng, T) for T in lens]
     q = rng.standard_normal((len(lens), D)).astype(np.float16)
-    note(f"kv attention lens={lens} max_blocks={max_blocks}")
+    note(f"kv attention lens={lens} max_blocks={max_blocks} workspace={use_ws}")
     cache, nblk = build(heads, max_blocks)
-    out = wq.kv_attention(to_dev(q), cache, to_dev(np.array(lens, np.int32)))
+    out = wq.kv_attention(to_dev(q), cache, to_dev(np.array(lens, np.int32)), use_workspace=use_ws)
     ref = np.stack([oracle_out(q[h], K, V, nblk[h]) for h, (K, V) in enumerate(heads)])
     got = out.cpu().numpy().astype(np.float64)
     assert not got[0].any()                         # empty cache -> zeros
     assert_close(got, ref, "ragged")
-    again = wq.kv_attention(to_dev(q), cache, to_dev(np.array(lens, np.int32))).cpu().numpy()
+    again = wq.kv_attention(to_dev(q), cache, to_dev(np.array(lens, np.int32)),
+                            use_workspace=use_ws).cpu().numpy()
     assert np.array_equal(again.view(np.uint16), out.cpu().numpy().view(np.uint16))
 
 

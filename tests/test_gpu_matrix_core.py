@@ -5,9 +5,10 @@ LDS, so these tests cover: K that is not a multiple of the slice (rounds past
 K inside the last slice), several slices added in slice order, each way of
 reading group headers (one group per 128-k round, several rounds per group,
 one group per row), rows not a multiple of the 16-row tile, and groups whose
-zero point lies far outside the code range.  They also check that the split-K
-workspace, cached per (device, stream), gives identical results when reused,
-grown, and used from two streams.
+zero point lies far outside the code range, each with the caller's workspace
+(split partials) and without one (plans that need none).  They also check that
+one workspace reused across calls of different shapes, and separate
+workspaces on two streams, give results identical to fresh ones.
 """
 
 import numpy as np
@@ -34,15 +35,16 @@ def packed(W, group, bits):
                                           (16384, 128, 4), (4480, 4480, 8), (11008, 64, 8),
                                           (4096, 512, 8)])
 @pytest.mark.parametrize("B", [3, 8, 9, 16, 17, 32])
-def test_ragged_slices_and_header_modes(K, group, bits, B):
+@pytest.mark.parametrize("use_ws", [True, False])
+def test_ragged_slices_and_header_modes(K, group, bits, B, use_ws):
     device()
     rng = np.random.default_rng(K + 7 * B + bits)
     N = 61
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
     X = rng.standard_normal((B, K)).astype(np.float16)
     host, dev = packed(W, group, bits)
-    note(f"matrix-core N={N} K={K} G={group} b={bits} B={B}")
-    Y = wq.gemm(to_dev(X), *dev, N=N, K=K, group=group, bits=bits, path="mfma")
+    note(f"matrix-core N={N} K={K} G={group} b={bits} B={B} workspace={use_ws}")
+    Y = wq.gemm(to_dev(X), *dev, N=N, K=K, group=group, bits=bits, path="mfma", use_workspace=use_ws)
     assert_close(Y, oracle.gemm(X, *host, N, K, group, bits), f"K={K} G={group} B={B}")
 
 
@@ -69,30 +71,68 @@ def test_extreme_groups(bits, B):
     ok = np.all(np.abs(ref) < 60000, axis=0)
     assert ok.sum() >= R // 2
     assert_close(y[:, ok], ref[:, ok], "crafted")
+    # Each kept row on its own, against what the kernels' arithmetic can lose:
+    #   - the tiled kernel's fp16 dequantization of each weight, (512 + q/2)
+    #     minus the fp16 (512 + z/2) times s: at most three fp16 roundings,
+    #     under 2^-9 of |x w| per term, or 2^-25 |x| for a subnormal weight;
+    #   - fp32 sums of terms offset by up to 1040 * s per code (the exact-code
+    #     kernels subtract the offset after summing), 2^-24 of the running
+    #     magnitude per addition over K terms;
+    #   - one fp16 rounding of the output, 2^-11 |y| (2^-25 absolute below the
+    #     normal range).
+    # Rows whose outputs are small are then held to their own size, not to
+    # 1e-2 of the largest output of the whole test.
+    What = oracle.dequantize(*host, R, K, G, bits)
+    Xa = np.abs(X.astype(np.float64))
+    s_full = np.repeat(host[1].astype(np.float64), G, axis=1)          # [R, K] scale of each weight
+    mag = Xa @ np.abs(What).T
+    offs = Xa @ (1040.0 * s_full).T
+    bound = (2.0**-9 * mag + 2.0**-25 * Xa.sum(axis=1)[:, None] + K * 2.0**-24 * (mag + offs)
+             + 2.0**-11 * np.abs(ref) + 2.0**-25)
+    err = np.abs(y - ref)
+    bad = (err > bound)[:, ok]
+    assert not bad.any(), f"per-row bound exceeded at {np.argwhere(bad)[:5]}: err {err[:, ok][bad][:5]}"
 
 
-def test_workspace_reuse_and_growth():
-    """Repeated, smaller and larger split-K calls on one stream reuse the same
-    workspace and agree bit for bit with the first call of each shape."""
+def test_workspace_reuse_across_shapes():
+    """One caller workspace, sized for the largest call, serves repeated,
+    smaller and larger split-K calls in stream order; each result is identical
+    to the same call with a fresh workspace, and within tolerance of the
+    oracle."""
     device()
-    shapes = [(300, 16384, 16), (40, 16384, 5), (900, 16384, 16), (300, 16384, 16)]
-    first = {}
+    shapes = [(300, 16384, 16), (40, 16384, 5), (900, 16384, 16), (300, 16384, 16), (4096, 11008, 40)]
+    need = max(wq.gemm_workspace_bytes(B, K, N, 128, 4, "mfma") for N, K, B in shapes)
+    assert need > 0
+    shared = torch.empty(need, dtype=torch.uint8, device=device())
+    shared.fill_(0xA5)                               # contents on entry do not matter
     for N, K, B in shapes:
         W = (np.random.default_rng(N).standard_normal((N, K)) * 0.02).astype(np.float16)
         X = np.random.default_rng(B + N).standard_normal((B, K)).astype(np.float16)
         host, dev = packed(W, 128, 4)
-        note(f"workspace N={N} K={K} B={B}")
-        Y = wq.gemm(to_dev(X), *dev, N=N, K=K, group=128, bits=4, path="mfma").cpu().numpy()
-        if (N, B) in first:
-            assert np.array_equal(Y.view(np.uint16), first[(N, B)].view(np.uint16))
-        else:
-            assert_close(Y.astype(np.float64), oracle.gemm(X, *host, N, K, 128, 4), "workspace")
-            first[(N, B)] = Y
+        note(f"workspace reuse N={N} K={K} B={B}")
+        Xd = to_dev(X)
+        Y = wq.gemm(Xd, *dev, N=N, K=K, group=128, bits=4, path="mfma", workspace=shared).cpu().numpy()
+        fresh = wq.gemm(Xd, *dev, N=N, K=K, group=128, bits=4, path="mfma").cpu().numpy()
+        assert np.array_equal(Y.view(np.uint16), fresh.view(np.uint16))
+        assert_close(Y.astype(np.float64), oracle.gemm(X, *host, N, K, 128, 4), "workspace")
+
+
+def test_undersized_workspace_raises():
+    device()
+    N, K, B = 300, 16384, 16
+    need = wq.gemm_workspace_bytes(B, K, N, 128, 4, "mfma")
+    assert need > 0
+    W = (np.random.default_rng(5).standard_normal((N, K)) * 0.02).astype(np.float16)
+    _, dev = packed(W, 128, 4)
+    Xd = to_dev(np.ones((B, K), np.float16))
+    small = torch.empty(need - 256, dtype=torch.uint8, device=device())
+    with pytest.raises(ValueError):
+        wq.gemm(Xd, *dev, N=N, K=K, group=128, bits=4, path="mfma", workspace=small)
 
 
 def test_two_streams():
-    """Split-K calls on two streams (own workspaces) match the same calls on
-    the default stream."""
+    """Split-K calls on two streams, each with its own workspace, match the
+    same call on the default stream bit for bit."""
     device()
     N, K, B = 500, 16384, 12
     W = (np.random.default_rng(31).standard_normal((N, K)) * 0.02).astype(np.float16)
@@ -100,12 +140,15 @@ def test_two_streams():
     _, dev = packed(W, 128, 4)
     Xd = to_dev(X)
     ref = wq.gemm(Xd, *dev, N=N, K=K, group=128, bits=4, path="mfma").cpu().numpy()
+    need = wq.gemm_workspace_bytes(B, K, N, 128, 4, "mfma")
+    assert need > 0
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ws = [torch.empty(need, dtype=torch.uint8, device=device()) for _ in range(2)]
     torch.cuda.synchronize()
     outs = []
-    for s in (s1, s2):
+    for s, w in zip((s1, s2), ws):
         with torch.cuda.stream(s):
-            outs.append(wq.gemm(Xd, *dev, N=N, K=K, group=128, bits=4, path="mfma"))
+            outs.append(wq.gemm(Xd, *dev, N=N, K=K, group=128, bits=4, path="mfma", workspace=w))
     torch.cuda.synchronize()
     for y in outs:
         assert np.array_equal(y.cpu().numpy().view(np.uint16), ref.view(np.uint16))
