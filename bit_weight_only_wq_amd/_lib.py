@@ -50,6 +50,7 @@ SIGNATURES = {
     "wq_quantize_workspace_size": (ctypes.c_int, [_I64, _I64, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "wq_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P]),
     "wq_gemm_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _SZ, _P]),
+    "wq_gemm_static": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
     "wq_gemm_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "wq_gemm_grouped": (ctypes.c_int, [ctypes.POINTER(GemmItem), _I32, _P, _SZ, _P]),
     "wq_gemm_grouped_workspace_size": (ctypes.c_int, [ctypes.POINTER(GemmItem), _I32, ctypes.POINTER(_SZ)]),

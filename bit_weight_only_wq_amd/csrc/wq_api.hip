@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "wq.h"
@@ -76,6 +77,45 @@ wq_status with_paths(int32_t count, F fn) {
     const wq_status st = fn(paths);
     if (paths != paths_small) delete[] paths;
     return st;
+}
+
+}  // namespace
+
+// ---- the static scratch of wq_gemm_static -------------------------------------
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops, harnesses that forbid it): split partials live in this fixed device
+// array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, so its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// ever passed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+wq_status static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return check_hip(e, "wq_gemm_static: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm_static: device %lld beyond the %lld the library tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return check_hip(e, "wq_gemm_static: hipGetSymbolAddress(scratch)");
+        if (!p) return fail(WQ_ERR_HIP, "wq_gemm_static: null address for the static scratch");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return WQ_OK;
 }
 
 }  // namespace
@@ -329,6 +369,30 @@ wq_status wq_gemm(const void* X, const void* codes, const void* scales, const vo
                   void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
                   void* stream) {
     return wq_gemm_ex(X, codes, scales, zeros, Y, B, K, N, group, bits, WQ_PATH_AUTO, nullptr, 0, stream);
+}
+
+wq_status wq_gemm_static(const void* X, const void* codes, const void* scales, const void* zeros,
+                         void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
+                         int32_t path, void* stream) {
+    g_last_error[0] = '\0';
+    int32_t use = path;
+    wq_status st = check_gemm(X, codes, scales, zeros, Y, B, K, N, group, bits, use);
+    if (st != WQ_OK || use < 0) return st;
+    // The plan wq_gemm_ex takes with a workspace, sized first.
+    size_t need = 0;
+    wq::Scratch sz;
+    sz.need = &need;
+    st = run_gemm(X, codes, scales, zeros, Y, B, K, N, group, bits, use, sz, nullptr);
+    if (st != WQ_OK) return st;
+    if (need > kStaticScratchBytes)
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm_static: the call needs %lld bytes of scratch, the static array "
+                    "holds %lld (use wq_gemm_ex with a workspace)", (long long)need, (long long)kStaticScratchBytes);
+    wq::Scratch ws;
+    if (need > 0) {
+        st = static_scratch(&ws.ptr);
+        if (st != WQ_OK) return st;
+    }
+    return run_gemm(X, codes, scales, zeros, Y, B, K, N, group, bits, use, ws, static_cast<hipStream_t>(stream));
 }
 
 // Validates every item (paths[i] receives its kernel family, -1 for a no-op).

@@ -192,6 +192,25 @@ wq_status wq_gemm_ex(const void* X, const void* codes, const void* scales,
                      int32_t group, int32_t bits, int32_t path, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * wq_gemm_ex without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  It runs the plan
+ * wq_gemm_ex runs with a workspace (same kernels, bit-identical results), and
+ * takes the scratch that plan needs from a static device array of 16 MiB
+ * (16777216 bytes), one per GPU, held from the first call on that GPU until
+ * the process ends.  A call whose plan needs more (wq_gemm_workspace_size
+ * above 16 MiB, e.g. B = 64 on a 28672 x 8192 matrix) returns
+ * WQ_ERR_UNSUPPORTED before any launch.  Every call on one GPU shares that
+ * GPU's array: calls that may overlap on one GPU (different streams, or
+ * threads enqueuing concurrently) race on it and must be serialized by the
+ * caller.  Nothing in the array needs to start at any particular value.
+ * Arguments, validation and errors otherwise as wq_gemm_ex.
+ */
+wq_status wq_gemm_static(const void* X, const void* codes, const void* scales,
+                         const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
+                         int32_t group, int32_t bits, int32_t path, void* stream);
+
 /* Workspace bytes wq_gemm_ex needs for this shape and path on the current
  * device (0: none).  Errors as wq_gemm_ex's shape checks (no pointers are
  * involved); *bytes = 0 then. */
