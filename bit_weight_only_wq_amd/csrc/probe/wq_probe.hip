@@ -20,7 +20,10 @@
 //   - `order` picks how strips map to rows and where a walk starts: 0, the
 //     strip's rows are adjacent and every wave starts at column 0; 1, adjacent
 //     rows, and wave w starts its walk at step w mod steps (wrapping); 2, the
-//     strip's rows are spread over the matrix (row s + i * strips).
+//     strip's rows are spread over the matrix (row s + i * strips); 3, as 1
+//     with the lanes of a row interleaved (lane l reads row l mod (64 / L),
+//     vector l / (64 / L) of the row's piece, the layout of the 4 x 4 x 4
+//     matrix-core blocks).
 // Nothing is written except, practically never, one word that keeps the
 // loads from being optimized away.
 #include <hip/hip_runtime.h>
@@ -44,9 +47,11 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const void* __restrict_
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(buf), (short)0, (int)bytes, kBufferWord3);
     // Row of this lane within the strip: adjacent (ORD 0, 1) or spread (ORD 2).
-    const uint32_t lane_row = ORD == 2 ? (uint32_t)(lane / L) * (uint32_t)strips : (uint32_t)(lane / L);
-    const uint32_t lane_off = lane_row * row_bytes + (uint32_t)(lane % L) * 16u;
-    const int64_t rot = ORD == 1 ? gw % steps : 0;     // first step of every walk
+    const uint32_t lane_row = ORD == 2 ? (uint32_t)(lane / L) * (uint32_t)strips
+                            : ORD == 3 ? (uint32_t)(lane % RPI) : (uint32_t)(lane / L);
+    const uint32_t lane_vec = ORD == 3 ? (uint32_t)(lane / RPI) : (uint32_t)(lane % L);
+    const uint32_t lane_off = lane_row * row_bytes + lane_vec * 16u;
+    const int64_t rot = (ORD == 1 || ORD == 3) ? gw % steps : 0;     // first step of every walk
     // Items of this wave: (strip, step) in order, strips gw, gw + nw, ...
     const int64_t my_strips = gw < strips ? (strips - gw + nw - 1) / nw : 0;
     const int64_t items = my_strips * steps;
@@ -99,6 +104,7 @@ hipError_t launch_ld(int order, bool nt, const void* buf, uint32_t bytes, int64_
         case 0: return launch_ldo<L, D, 0>(nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
         case 1: return launch_ldo<L, D, 1>(nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
         case 2: return launch_ldo<L, D, 2>(nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
+        case 3: return launch_ldo<L, D, 3>(nt, buf, bytes, strips, steps, row_bytes, blocks, sink, st);
     }
     return hipErrorInvalidValue;
 }
@@ -123,7 +129,7 @@ extern "C" int32_t wq_probe_read(const void* buf, int64_t rows, int64_t row_byte
     const int L = lanes_per_row;
     if (L != 4 && L != 8 && L != 16 && L != 32 && L != 64) return 2;
     if (depth != 2 && depth != 4 && depth != 8 && depth != 16) return 2;
-    if (order < 0 || order > 2) return 1;
+    if (order < 0 || order > 3) return 1;
     if (!buf || !sink || rows < 1 || row_bytes < 16 || blocks_per_cu < 1 || blocks_per_cu > 32) return 1;
     const int64_t rpi = 64 / L;
     if (rows % rpi != 0 || row_bytes % (16 * L) != 0) return 1;

@@ -279,7 +279,7 @@ static wq_status check_gemm_shape(int64_t B, int64_t K, int64_t N, int32_t group
         return WQ_OK;
     }
     const bool gemv_ok = wq::gemv_supports(K, bits);
-    const bool mfma_ok = wq::mfma_supports(K, group, bits);
+    const bool mfma_ok = wq::mfma_path_takes(B, K, N, group, bits);
     int use = path;
     if (use == WQ_PATH_AUTO) {
         if (mfma_ok && (B > wq_gemv_max_batch() || !gemv_ok)) use = WQ_PATH_MFMA;

@@ -438,10 +438,28 @@ bool mfma_supports(int64_t K, int32_t group, int32_t bits) {
     return (bits == 4 || bits == 8) && group % kr == 0 && K % kr == 0;
 }
 
+bool q4_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits) {
+    return q4_supports(B, K, N, group, bits) && N >= 1024;
+}
+
+bool mfma_path_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits) {
+    return q4_takes(B, K, N, group, bits) || mfma_supports(K, group, bits);
+}
+
 hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales,
                             const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                             int32_t group, int32_t bits, int num_cus, const Scratch& ws,
                             hipStream_t stream) {
+    // Tall matrices at B <= 8 take the quad-row kernel, at B <= 16 the
+    // streaming 16-row kernel; neither needs scratch.
+    if (q4_takes(B, K, N, group, bits)) {
+        if (ws.sizing()) return hipSuccess;
+        return launch_gemm_q4(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+    }
+    if (sk_supports(B, K, N, group, bits) && (N + 15) / 16 >= (int64_t)num_cus / 2) {
+        if (ws.sizing()) return hipSuccess;
+        return launch_gemm_sk(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+    }
     // The X-resident kernel takes its shapes, but without scratch only when
     // one K-slice holds all of X (its slices meet in fp32 partials).
     const bool no_scratch = !ws.sizing() && !ws.ptr;

@@ -83,6 +83,18 @@ struct XrProduct {
 hipError_t launch_gemm_xr_many(const XrProduct* prods, int count, int64_t B, int32_t bits,
                                int num_cus, const Scratch& ws, hipStream_t stream);
 bool mfma_supports(int64_t K, int32_t group, int32_t bits);
+// Whether launch_gemm_mfma takes the product (the quad-row kernel's shapes,
+// with any group % 32, or the tiled kernels' group % 128 (bits 4) / 64 (8)).
+bool q4_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
+bool mfma_path_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
+// Quad-row 4x4x4 matrix-core kernel for B <= 8 (wq_gemm_q4.hip): needs no scratch.
+bool q4_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
+hipError_t launch_gemm_q4(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,
+                          int64_t B, int64_t K, int64_t N, int32_t group, int num_cus, hipStream_t stream);
+// Streaming matrix-core kernel for B <= 16 (wq_gemm_sk.hip): needs no scratch.
+bool sk_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
+hipError_t launch_gemm_sk(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,
+                          int64_t B, int64_t K, int64_t N, int32_t group, int num_cus, hipStream_t stream);
 // Matrix-core product (X-resident kernel when it takes the shape, else the
 // tiled kernel); scratch holds fp32 split-K partials.
 hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales,

@@ -28,14 +28,17 @@ extern "C" {
  * strip's rows are adjacent and every walk starts at column 0; 1, adjacent
  * rows, wave w starts its walk at step w mod (row_bytes / (16 *
  * lanes_per_row)) and wraps; 2, a strip's rows are spread over the matrix
- * (strip s holds rows s, s + S, s + 2S, ... with S = rows * lanes_per_row / 64).
+ * (strip s holds rows s, s + S, s + 2S, ... with S = rows * lanes_per_row / 64);
+ * 3, as 1 but with the lanes of a row interleaved: lane l reads row
+ * l mod (64 / lanes_per_row) of the strip, 16-byte vector l / (64 /
+ * lanes_per_row) of the row's piece.
  *
  * buf            device pointer, 16-byte aligned, rows * row_bytes bytes
  *                (< 4 GiB), caller-owned, only read
  * lanes_per_row  4, 8, 16, 32 or 64; rows % (64 / lanes_per_row) == 0 and
  *                row_bytes % (16 * lanes_per_row) == 0
  * depth          2, 4, 8 or 16
- * order          0, 1 or 2 (above)
+ * order          0, 1, 2 or 3 (above)
  * nontemporal    nonzero: loads with the non-temporal cache policy
  * blocks_per_cu  1..32
  * sink           device pointer to one 32-bit word (4-byte aligned); written

@@ -46,7 +46,7 @@ def test_probe_library_exports_its_header():
                                        kw.get("sink", FAKE), None)
     assert r(L=12) == 2
     assert r(D=3) == 2
-    assert r(order=3) == 1
+    assert r(order=4) == 1
     assert r(rows=63) == 1                     # 4 rows per strip at L = 16
     assert r(row_bytes=4000) == 1
     assert r(buf=FAKE + 8) == 3
@@ -269,7 +269,11 @@ def test_gemm_workspace_size_queries():
     st, n = _gemm_ws_size(1)
     assert st == _lib.WQ_OK and n == 0                   # GEMV: no scratch
     st, n = _gemm_ws_size(16)
-    assert st == _lib.WQ_OK and n > 0 and n % (16 * 28672 * 4) == 0   # X needs two K-slices
+    assert st == _lib.WQ_OK and n == 0                   # tall matrix at B = 16: streaming kernel, no scratch
+    st, n = _gemm_ws_size(16, K=16384, N=300)
+    assert st == _lib.WQ_OK and n > 0 and n % (16 * 300 * 4) == 0     # few rows: K-slices in partials
+    st, n = _gemm_ws_size(64)
+    assert st == _lib.WQ_OK and n > 0 and n % (64 * 28672 * 4) == 0   # tiled kernel's K splits
     st, n = _gemm_ws_size(0)
     assert st == _lib.WQ_OK and n == 0                   # no-op
     st, n = _gemm_ws_size(16, K=250)
@@ -283,9 +287,9 @@ def test_gemm_workspace_rejected_before_launch():
     """An undersized, misaligned, or null-with-a-size workspace is refused
     before anything is enqueued (the fake pointers are never used)."""
     lib = wq.load()
-    st, need = _gemm_ws_size(16)
+    st, need = _gemm_ws_size(64)
     assert need > 0
-    call = lambda ws, n: lib.wq_gemm_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8192, 28672, 128, 4, 0, ws, n, None)
+    call = lambda ws, n: lib.wq_gemm_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 8192, 28672, 128, 4, 0, ws, n, None)
     assert call(FAKE, need - 1) == _lib.WQ_ERR_INVALID_ARG
     assert b"needs" in lib.wq_last_error()
     assert call(FAKE, 0) == _lib.WQ_ERR_INVALID_ARG
@@ -300,7 +304,7 @@ def test_gemm_workspace_rejected_before_launch():
 def test_grouped_workspace_size_and_rejection():
     import ctypes
     lib = wq.load()
-    arr = (_lib.GemmItem * 2)(_item(B=16, K=8192, N=28672), _item(B=1, K=8192, N=28672))
+    arr = (_lib.GemmItem * 2)(_item(B=16, K=16384, N=300), _item(B=1, K=8192, N=28672))
     n = ctypes.c_size_t(0)
     assert lib.wq_gemm_grouped_workspace_size(arr, 2, ctypes.byref(n)) == _lib.WQ_OK
     assert n.value > 0

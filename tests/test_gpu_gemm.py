@@ -164,3 +164,23 @@ def test_decode_set_layer0_b32(index):
         Y = wq.gemm(to_dev(X), codes, scales, zeros, N=N, K=K, group=group, bits=bits)
         ref = oracle.gemm(X, *oracle.quantize(W[rows], group, bits), len(rows), K, group, bits)
         assert_close(Y.cpu().numpy()[:, rows].astype(np.float64), ref, f"#{index} b={bits}")
+
+
+def test_mlp70b_all_rows_every_metric_batch():
+    """Every output of the 70B-class up-projection (28672 x 8192, group 128)
+    at every batch size of the measured step, automatic path with and without
+    a workspace, against the oracle's double-precision product."""
+    device()
+    name = "mlp70b_up_k8192_n28672_g128"
+    cfg = wq_inputs.WORKLOADS[name]
+    N, K, G = cfg["N"], cfg["K"], cfg["group"]
+    W, X = workload(name)
+    codes, scales, zeros = wq.quantize_pack(to_dev(W), G, 4)
+    hc, hs, hz = oracle.quantize(W, G, 4)
+    assert np.array_equal(codes.cpu().numpy(), hc)
+    for B in (1, 2, 4, 8, 16, 32, 64):
+        ref = oracle.gemm(X[:B], hc, hs, hz, N, K, G, 4)
+        for use_ws in (True, False):
+            note(f"{name} all rows B={B} workspace={use_ws}")
+            Y = wq.gemm(to_dev(X[:B]), codes, scales, zeros, N=N, K=K, group=G, bits=4, use_workspace=use_ws)
+            assert_close(Y, ref, f"{name} B={B} ws={use_ws}")
