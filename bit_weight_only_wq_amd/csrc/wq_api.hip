@@ -149,7 +149,7 @@ int64_t wq_num_groups(int64_t N, int64_t K, int32_t group) {
 
 // Measured crossover on MI355X: the GEMV path wins at B <= 2, the matrix-core
 // kernels from B = 3 on.
-int32_t wq_gemv_max_batch(void) { return 2; }
+int32_t wq_gemv_max_batch(void) { return 1; }
 
 // ---- quantize/pack -----------------------------------------------------------
 
@@ -241,8 +241,10 @@ wq_status wq_dequantize(const void* codes, const void* scales, const void* zeros
 // Validates the shape of one product and picks its kernel family (path on
 // return); checks no pointer.  A no-op product (B == 0 or N == 0) returns
 // WQ_OK with path = -1.
+// The header pointers (null for a size query: taken as aligned) decide
+// between kernels that need aligned header arrays and those that do not.
 static wq_status check_gemm_shape(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
-                                  int32_t& path) {
+                                  const void* scales, const void* zeros, int32_t& path) {
     if (B < 0 || N < 0 || K < 1 || group < 1)
         return fail(WQ_ERR_INVALID_ARG, "wq_gemm: need B >= 0, N >= 0, K >= 1, group >= 1 (B=%lld K=%lld)", B, K);
     if (K % group != 0)
@@ -279,7 +281,7 @@ static wq_status check_gemm_shape(int64_t B, int64_t K, int64_t N, int32_t group
         return WQ_OK;
     }
     const bool gemv_ok = wq::gemv_supports(K, bits);
-    const bool mfma_ok = wq::mfma_path_takes(B, K, N, group, bits);
+    const bool mfma_ok = wq::mfma_path_takes(B, K, N, group, bits, scales, zeros);
     int use = path;
     if (use == WQ_PATH_AUTO) {
         if (mfma_ok && (B > wq_gemv_max_batch() || !gemv_ok)) use = WQ_PATH_MFMA;
@@ -288,7 +290,8 @@ static wq_status check_gemm_shape(int64_t B, int64_t K, int64_t N, int32_t group
     if (use == WQ_PATH_GEMV && !gemv_ok)
         return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: GEMV path does not take K=%lld at bits=%lld", K, bits);
     if (use == WQ_PATH_MFMA && !mfma_ok)
-        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: MFMA path needs group %% %lld == 0 (group=%lld)",
+        return fail(WQ_ERR_UNSUPPORTED,
+                    "wq_gemm: MFMA path needs group %% %lld == 0 (group=%lld), or B <= 4 with aligned header arrays",
                     bits == 4 ? 128 : 64, group);
     path = use;
     return WQ_OK;
@@ -298,7 +301,7 @@ static wq_status check_gemm_shape(int64_t B, int64_t K, int64_t N, int32_t group
 static wq_status check_gemm(const void* X, const void* codes, const void* scales,
                             const void* zeros, const void* Y, int64_t B, int64_t K, int64_t N,
                             int32_t group, int32_t bits, int32_t& path) {
-    const wq_status st = check_gemm_shape(B, K, N, group, bits, path);
+    const wq_status st = check_gemm_shape(B, K, N, group, bits, scales, zeros, path);
     if (st != WQ_OK || path < 0) return st;
     if (!X || !codes || !scales || !zeros || !Y)
         return fail(WQ_ERR_INVALID_ARG, "wq_gemm: null pointer");
@@ -330,7 +333,7 @@ wq_status wq_gemm_workspace_size(int64_t B, int64_t K, int64_t N, int32_t group,
     if (!bytes) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_workspace_size: null bytes");
     *bytes = 0;
     int32_t use = path;
-    const wq_status st = check_gemm_shape(B, K, N, group, bits, use);
+    const wq_status st = check_gemm_shape(B, K, N, group, bits, nullptr, nullptr, use);
     if (st != WQ_OK || use < 0) return st;
     size_t need = 0;
     wq::Scratch ws;

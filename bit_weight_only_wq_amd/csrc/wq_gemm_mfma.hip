@@ -438,21 +438,39 @@ bool mfma_supports(int64_t K, int32_t group, int32_t bits) {
     return (bits == 4 || bits == 8) && group % kr == 0 && K % kr == 0;
 }
 
-bool q4_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits) {
-    return q4_supports(B, K, N, group, bits) && N >= 1024;
+static bool aligned_to(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+bool q4_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
+              const void* zeros) {
+    return q4_supports(B, K, N, group, bits) && N >= 1024 && aligned_to(scales, 8) && aligned_to(zeros, 8);
 }
 
-bool mfma_path_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits) {
-    return q4_takes(B, K, N, group, bits) || mfma_supports(K, group, bits);
+// The quad-stream kernel takes B <= 4 on tall matrices (past 4 batch rows
+// the 16-row kernels do more work per code byte for less).
+bool qs_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
+              const void* zeros) {
+    return B <= 4 && qs_supports(B, K, N, group, bits) && N >= 1024 && aligned_to(scales, 16) &&
+           aligned_to(zeros, 16);
+}
+
+bool mfma_path_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
+                     const void* zeros) {
+    return qs_takes(B, K, N, group, bits, scales, zeros) || q4_takes(B, K, N, group, bits, scales, zeros) ||
+           mfma_supports(K, group, bits);
 }
 
 hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales,
                             const void* zeros, void* Y, int64_t B, int64_t K, int64_t N,
                             int32_t group, int32_t bits, int num_cus, const Scratch& ws,
                             hipStream_t stream) {
-    // Tall matrices at B <= 8 take the quad-row kernel, at B <= 16 the
-    // streaming 16-row kernel; neither needs scratch.
-    if (q4_takes(B, K, N, group, bits)) {
+    // Tall matrices at B <= 4 take the quad-stream kernel (groups of 64 and
+    // more) or the quad-row kernel, at B <= 16 the streaming 16-row kernel;
+    // none of them needs scratch.
+    if (qs_takes(B, K, N, group, bits, scales, zeros)) {
+        if (ws.sizing()) return hipSuccess;
+        return launch_gemm_qs(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+    }
+    if (q4_takes(B, K, N, group, bits, scales, zeros)) {
         if (ws.sizing()) return hipSuccess;
         return launch_gemm_q4(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
     }

@@ -83,11 +83,23 @@ struct XrProduct {
 hipError_t launch_gemm_xr_many(const XrProduct* prods, int count, int64_t B, int32_t bits,
                                int num_cus, const Scratch& ws, hipStream_t stream);
 bool mfma_supports(int64_t K, int32_t group, int32_t bits);
-// Whether launch_gemm_mfma takes the product (the quad-row kernel's shapes,
-// with any group % 32, or the tiled kernels' group % 128 (bits 4) / 64 (8)).
-bool q4_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
-bool mfma_path_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
-// Quad-row 4x4x4 matrix-core kernel for B <= 8 (wq_gemm_q4.hip): needs no scratch.
+// Whether launch_gemm_mfma takes the product: the quad-stream or quad-row
+// kernels' shapes (B <= 4, groups of 64 or 32 and up, header arrays 16- or
+// 8-byte aligned; null header pointers count as aligned), or the tiled
+// kernels' group % 128 (bits 4) / 64 (8).
+bool qs_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
+              const void* zeros);
+bool q4_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
+              const void* zeros);
+bool mfma_path_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
+                     const void* zeros);
+// Quad-stream 4x4x4 matrix-core kernel for B <= 4 (wq_gemm_qs.hip): needs no
+// scratch; its header arrays must be 16-byte aligned.
+bool qs_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
+hipError_t launch_gemm_qs(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,
+                          int64_t B, int64_t K, int64_t N, int32_t group, int num_cus, hipStream_t stream);
+// Quad-row 4x4x4 matrix-core kernel for B <= 4 (wq_gemm_q4.hip): needs no
+// scratch; its header arrays must be 8-byte aligned.
 bool q4_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
 hipError_t launch_gemm_q4(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,
                           int64_t B, int64_t K, int64_t N, int32_t group, int num_cus, hipStream_t stream);

@@ -1,13 +1,14 @@
-"""GPU parity of the quad-row 4x4x4 matrix-core kernel (B <= 4 on matrices of
-at least 1024 rows; wq_gemm_q4.hip) against the CPU oracle.
+"""GPU parity of the 4x4x4 matrix-core kernels at B <= 4 on matrices of at
+least 1024 rows against the CPU oracle: the quad-row kernel (wq_gemm_q4.hip)
+takes groups of 32 (and group counts the quad-stream kernel cannot stage),
+the quad-stream kernel (wq_gemm_qs.hip, its own tests) the rest.
 
-What its geometry makes special: a wave walks 4 rows in 512-k windows
-(K = 896 and 640 leave a partial last window, whose chunks past K read
-nothing), each lane's 32-code chunk takes its own group header (groups of 32,
-64, 128 and 256), batch rows past B are zero lanes of the A operand (B = 5..8
-adds a second accumulator), N that is not a multiple of 4 leaves a partial
-last quad, waves take several quads in turn and start their walks at
-different windows.  Every output is compared.
+What the geometry makes special: 4 rows walked in 512-k windows (K = 896 and
+640 leave a partial last window, whose chunks past K read nothing), each
+lane's 32-code chunk taking its own group header (groups of 32, 64, 128 and
+256), batch rows past B as zero lanes of the A operand, N that is not a
+multiple of 4 leaving a partial last quad, waves taking several quads in
+turn.  Every output is compared.
 """
 
 import numpy as np
