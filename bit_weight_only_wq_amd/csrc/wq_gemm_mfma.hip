@@ -302,7 +302,13 @@ __global__ __launch_bounds__(256, (BT == 64 && RB == 2) ? 3 : 1) void gemm_mfma_
             __builtin_amdgcn_sched_barrier(0);
             compute(k & 1, cr[k & 3], k % STT);
             store_stage(st + k + 1, (k & 1) ^ 1, xr, hs, hz);
-            __syncthreads();
+            // The next stage's X (and headers) are in LDS once this block's
+            // LDS writes are done; the code loads stay in flight (a full
+            // workgroup barrier would wait for them too, every stage).
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
         }
     }
 
@@ -453,6 +459,13 @@ bool qs_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, cons
            aligned_to(zeros, 16);
 }
 
+// The tile-stream kernel takes B <= 16 on tall matrices (at B <= 4 where the
+// quad kernels do not).
+bool ts_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
+              const void* zeros) {
+    return ts_supports(B, K, N, group, bits) && N >= 2048 && aligned_to(scales, 8) && aligned_to(zeros, 8);
+}
+
 bool mfma_path_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
                      const void* zeros) {
     return qs_takes(B, K, N, group, bits, scales, zeros) || q4_takes(B, K, N, group, bits, scales, zeros) ||
@@ -464,8 +477,9 @@ hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales
                             int32_t group, int32_t bits, int num_cus, const Scratch& ws,
                             hipStream_t stream) {
     // Tall matrices at B <= 4 take the quad-stream kernel (groups of 64 and
-    // more) or the quad-row kernel, at B <= 16 the streaming 16-row kernel;
-    // none of them needs scratch.
+    // more) or the quad-row kernel, at B <= 16 the tile-stream kernel or (with
+    // header arrays it cannot stage) the streaming 16-row kernel; none of
+    // them needs scratch.
     if (qs_takes(B, K, N, group, bits, scales, zeros)) {
         if (ws.sizing()) return hipSuccess;
         return launch_gemm_qs(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
@@ -473,6 +487,10 @@ hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales
     if (q4_takes(B, K, N, group, bits, scales, zeros)) {
         if (ws.sizing()) return hipSuccess;
         return launch_gemm_q4(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
+    }
+    if (ts_takes(B, K, N, group, bits, scales, zeros)) {
+        if (ws.sizing()) return hipSuccess;
+        return launch_gemm_ts(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
     }
     if (sk_supports(B, K, N, group, bits) && (N + 15) / 16 >= (int64_t)num_cus / 2) {
         if (ws.sizing()) return hipSuccess;

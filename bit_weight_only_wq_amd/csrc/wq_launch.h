@@ -93,6 +93,13 @@ bool q4_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, cons
               const void* zeros);
 bool mfma_path_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
                      const void* zeros);
+bool ts_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
+              const void* zeros);
+// Tile-stream 16x16x32 matrix-core kernel for B <= 16 (wq_gemm_ts.hip): needs
+// no scratch; group 128, K % 512 == 0, header arrays 8-byte aligned.
+bool ts_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
+hipError_t launch_gemm_ts(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,
+                          int64_t B, int64_t K, int64_t N, int32_t group, int num_cus, hipStream_t stream);
 // Quad-stream 4x4x4 matrix-core kernel for B <= 4 (wq_gemm_qs.hip): needs no
 // scratch; its header arrays must be 16-byte aligned.
 bool qs_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
