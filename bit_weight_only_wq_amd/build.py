@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libwq.so")
 PROBE_LIB = os.path.join(HERE, "libwq_probe.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = ["wq_api.hip", "wq_quantize.hip", "wq_gemv.hip", "wq_gemv_lowbit.hip", "wq_gemv_nf4.hip",
-           "wq_gemm_mfma.hip", "wq_gemm_xr.hip", "wq_gemm_sk.hip", "wq_gemm_q4.hip", "wq_gemm_qs.hip", "wq_gemm_ts.hip", "wq_kv.hip", "wq_dequant.hip"]
+           "wq_gemm_mfma.hip", "wq_gemm_xr.hip", "wq_gemm_sk.hip", "wq_gemm_q4.hip", "wq_gemm_qs.hip", "wq_gemm_ts.hip", "wq_gemm_kw.hip", "wq_kv.hip", "wq_dequant.hip"]
 PROBE_SOURCES = ["probe/wq_probe.hip"]
 
 HIPCC_FLAGS = [

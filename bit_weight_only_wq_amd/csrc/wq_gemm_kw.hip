@@ -1,0 +1,387 @@
+// Matrix-core product for batches of up to 64 rows on tall matrices, with the
+// waves of a block splitting K between them.
+//
+// Every weight is read once per call and serves the whole batch ("Serving many
+// users at once", "Batching: one read, many users"); below the ridge the code
+// stream sets the time ("Quantization & inference optimisation", "Bandwidth,
+// not compute"), so the design keeps that stream whole and moves as little
+// else as it can:
+//   - a block (4 waves, one per SIMD) owns TPB 16-row tiles of W across all of
+//     K; wave w takes the w-th quarter of K, so each X value reaches the
+//     compute unit once, and the waves' fp32 sums are added in LDS, in wave
+//     order, at the end: no partial sums leave the compute unit;
+//   - K is walked in rounds of 128 k (one group): lane (r16, g4) of tile t
+//     holds the 16-byte code chunk of row 16 t + r16 at k [32 g4, 32 g4 + 32)
+//     of the round, the weight operand of v_mfma_f32_16x16x32_f16 for the
+//     round's 4 k-steps, dequantized in registers to fp16 (q - z) * s / 2;
+//   - code chunks and group headers come two rounds at a time (the two halves
+//     of each 128-byte line of a row together) into a two-deep register ring;
+//   - a wave copies its rounds of X [16 NCB rows x 128 k] into a two-round
+//     LDS ring with LDS-DMA loads that read whole lines (4 rows x 256 bytes
+//     per instruction); chunk p of row r goes to position p ^ (r & 15), so the
+//     X-operand reads (16 rows, one chunk each, per 16 lanes) hit distinct
+//     banks;
+//   - a wave's loads complete in issue order, so X and codes are issued with
+//     the same lead: X of round r + 2 after round r, the codes of step d + 2
+//     (rounds 2d + 4, 2d + 5) after round 2d + 1, behind X of round 2d + 3.
+// Needs group 128, K = 2048, 4096 or 8192, X 16-byte aligned; it uses no
+// scratch.
+#include "wq_device.h"
+#include "wq_launch.h"
+#include "wq_mfma_dq.h"
+
+namespace wq {
+
+namespace {
+
+constexpr int kKwBufWord3 = 0x00020000;     // raw, unswizzled gfx9 buffer
+constexpr uint32_t kKwFar = 0x80000000u;    // a per-lane offset past every buffer the kernel reads
+
+typedef __attribute__((address_space(3))) void kw_lds_void;
+typedef unsigned int kw_v4u __attribute__((ext_vector_type(4)));
+
+struct KwArgs {
+    const uint16_t* X;
+    const uint8_t* codes;
+    const uint16_t* scales;
+    const uint16_t* zeros;
+    uint16_t* Y;
+    int32_t B, N, K;
+    int32_t ngrp;      // groups per row (K / 128)
+    int32_t cpr;       // 16-byte header chunks per row (ngrp / 8, a power of two)
+    int32_t nd;        // two-round steps per wave (K / (256 W))
+};
+
+// s_waitcnt with vmcnt(n) (bits 3:0 and 15:14) and no wait on the other counters.
+constexpr int kw_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// The loads that may still be in flight when round r starts (steady state),
+// for the issue order of the kernel: at the end of round e, X of round e + DX,
+// then, if e is odd, the codes of step (e - 1) / 2 + 2 (NXL and NSL
+// loads).  Round r needs X of round r (issued at the end of round r - DX) and
+// its step r / 2 (issued at the end of round 2 (r / 2) - 3, after that round's
+// X); everything issued after the later of the two may be outstanding.
+constexpr int kw_inflight(int DX, int NXL, int NSL, int r) {
+    const int ex = r - DX, es = 2 * (r / 2) - 3;
+    const bool step_later = es >= ex;
+    const int e = step_later ? es : ex;
+    int n = (!step_later && (e & 1)) ? NSL : 0;
+    for (int q = e + 1; q < r; ++q) n += NXL + ((q & 1) ? NSL : 0);
+    return n < 63 ? n : 63;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kw_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kKwBufWord3);
+}
+
+// NCB: 16-row batch blocks (B <= 16 NCB).  TPB: 16-row weight tiles per block.
+// DX: rounds in the X ring (2 or 4): X is issued DX - 1 rounds before use,
+// the codes of a step two rounds before its first round.  W: waves per block
+// (one per SIMD), each taking a W-th of K.
+template <int NCB, int TPB, int DX, int W>
+__global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
+    static_assert(DX == 2 || DX == 4, "an X ring of 2 or 4 rounds");
+    constexpr int XR = NCB * 16 * 16;   // 16-byte X chunks per round
+    // The rounds of the ring are separate objects, so that the compiler can
+    // tell the LDS-DMA writes of one from those of another and waits only for
+    // the round that is read.
+    __shared__ __align__(16) uint4 xs0[W * XR];
+    __shared__ __align__(16) uint4 xs1[W * XR];
+    __shared__ __align__(16) uint4 xs2[DX > 2 ? W * XR : 1];
+    __shared__ __align__(16) uint4 xs3[DX > 2 ? W * XR : 1];
+    // The block's group headers (scales, zero points), up to 64 groups per
+    // row: row r's 16-byte chunk p (8 groups) at position r * cpr +
+    // (p ^ (r & (cpr - 1))), so that 16 rows read at one group hit distinct
+    // banks.
+    constexpr int HCH = TPB * 16 * 8;
+    __shared__ __align__(16) uint4 hs[HCH];
+    __shared__ __align__(16) uint4 hz[HCH];
+    constexpr int NXL = NCB * 4;        // LDS-DMA loads per round (4 rows each)
+    constexpr int NSL = 2 * TPB;        // code loads per two-round step
+    constexpr int WAIT_EVEN = kw_vmcnt(kw_inflight(DX, NXL, NSL, 100));
+    constexpr int WAIT_ODD = kw_vmcnt(kw_inflight(DX, NXL, NSL, 101));
+
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint4* const xw[4] = {xs0 + w * XR, xs1 + w * XR, xs2 + (DX > 2 ? w * XR : 0),
+                          xs3 + (DX > 2 ? w * XR : 0)};   // this wave's rounds (slot = round % DX)
+
+    const int tile0 = blockIdx.x * TPB;
+    const int rows_blk = a.N - tile0 * 16 < TPB * 16 ? a.N - tile0 * 16 : TPB * 16;
+    const uint32_t row_bytes = (uint32_t)a.K / 2;
+    const __amdgpu_buffer_rsrc_t crs =
+        kw_rsrc(a.codes + (size_t)tile0 * 16 * row_bytes, (uint32_t)rows_blk * row_bytes);
+    const size_t hbase = (size_t)tile0 * 16 * a.ngrp;
+    const uint32_t hbytes = (uint32_t)rows_blk * a.ngrp * 2;
+    // Batch rows past B lie past the end of X and read as zeros.
+    const __amdgpu_buffer_rsrc_t xrs = kw_rsrc(a.X, (uint32_t)a.B * a.K * 2);
+
+    // This lane's row in each tile (rows past N reread the block's last row;
+    // their sums are not stored).
+    uint32_t coff[TPB];
+    int hrow[TPB], hswz[TPB];
+#pragma unroll
+    for (int t = 0; t < TPB; ++t) {
+        int rl = t * 16 + r16;
+        rl = rl < rows_blk ? rl : rows_blk - 1;
+        coff[t] = (uint32_t)rl * row_bytes + 16u * g4;
+        hrow[t] = rl * a.cpr;
+        hswz[t] = rl & (a.cpr - 1);
+    }
+    const int d0 = w * a.nd;   // the wave's first two-round step
+    const int nr = 2 * a.nd;   // the wave's rounds
+
+    // X of local round rl: instruction q covers rows 4q .. 4q + 3; lane l takes
+    // chunk (l & 15) ^ (row & 15) of row 4q + l / 16 and writes position l.
+    uint32_t xoff[NXL];
+#pragma unroll
+    for (int q = 0; q < NXL; ++q) {
+        const int row = 4 * q + (lane >> 4);
+        const int chunk = (lane & 15) ^ (row & 15);
+        xoff[q] = (uint32_t)row * a.K * 2 + (uint32_t)chunk * 16 + (uint32_t)d0 * 512;
+    }
+    // Rounds past the wave's range are issued too, at an offset past the end
+    // of the buffer: they read nothing and write zeros into a free slot, and
+    // every round of the loop issues the same loads (one wait count holds).
+    auto load_x = [&](int rl, int slot) {   // slot = rl % DX, a compile-time constant at every call
+        const uint32_t far = rl < nr ? 0u : kKwFar;   // offsets stay below 2^31 otherwise
+#pragma unroll
+        for (int q = 0; q < NXL; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (kw_lds_void*)(xw[slot] + q * 64), 16,
+                                                     (int)((xoff[q] + (uint32_t)rl * 256) | far), 0, 0, 0);
+    };
+
+    struct Step {
+        kw_v4u c[TPB][2];   // code chunks of the step's two rounds
+    };
+    auto load_step = [&](int dl, Step& st) {
+        const uint32_t far = dl < a.nd ? 0u : kKwFar;
+        const uint32_t dg = (uint32_t)(d0 + dl);
+#pragma unroll
+        for (int t = 0; t < TPB; ++t) {
+            const uint32_t o = (coff[t] + 128u * dg) | far;
+            st.c[t][0] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)o, 0, 0);
+            st.c[t][1] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)(o + 64u), 0, 0);
+        }
+    };
+
+    const dq::DqConsts cst{vgpr_const(0x000F000Fu), vgpr_const(0x00F000F0u), vgpr_const(0x60006000u),
+                           vgpr_const(0x50005000u)};
+    const h2_t zmul = {(_Float16)0.5f, (_Float16)0.5f};
+    const h2_t zadd = {(_Float16)512.0f, (_Float16)32.0f};
+
+    f4_t acc[TPB][NCB];
+#pragma unroll
+    for (int t = 0; t < TPB; ++t)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[t][cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // One round: half h of a step's codes and headers, X from LDS slot xr.
+    auto compute = [&](const Step& st, const uint32_t* hsv, const uint32_t* hzv, int h, const uint4* xr) {
+        h2_t nz[TPB], ss[TPB];
+        const uint32_t sel = h ? 0x07060706u : 0x05040504u;   // that group's half, twice
+#pragma unroll
+        for (int t = 0; t < TPB; ++t) {
+            nz[t] = as_h2(__builtin_amdgcn_perm(hzv[t], hzv[t], sel)) * zmul + zadd;   // (512 + z/2, 32 + z/2)
+            ss[t] = as_h2(__builtin_amdgcn_perm(hsv[t], hsv[t], sel));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h8_t xo[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                xo[cb] = __builtin_bit_cast(h8_t, dq::permute8<4>(xr[(cb * 16 + r16) * 16 + ((4 * g4 + j) ^ r16)]));
+#pragma unroll
+            for (int t = 0; t < TPB; ++t) {
+                const uint4 cw = __builtin_bit_cast(uint4, st.c[t][h]);
+                const h8_t bop = dq::dequant<4>(cw, j, cst, nz[t], ss[t]);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[t][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xo[cb], bop, acc[t][cb], 0, 0, 0);
+            }
+        }
+    };
+
+    // Two rounds of one step from ring slot st, each followed by the loads of
+    // its issue slot (X DX rounds later; after the odd round, the codes two
+    // steps later).  dl is even for ring0 and odd for ring1, and the loop
+    // below starts every pair of steps at a round that is a multiple of 4, so
+    // the X slots are compile-time constants.
+    auto step = [&](Step& st, int dl, int pos) {   // pos: dl % 2
+        const int r = 2 * dl;
+        __builtin_amdgcn_s_waitcnt(WAIT_EVEN);
+        asm volatile("" ::: "memory");
+        // The step's two groups (2 dg, 2 dg + 1) share one 8-group chunk.
+        const int dg = d0 + dl;
+        uint32_t hsv[TPB], hzv[TPB];
+#pragma unroll
+        for (int t = 0; t < TPB; ++t) {
+            const int at = (hrow[t] + ((dg >> 2) ^ hswz[t])) * 4 + (dg & 3);
+            hsv[t] = reinterpret_cast<const uint32_t*>(hs)[at];
+            hzv[t] = reinterpret_cast<const uint32_t*>(hz)[at];
+        }
+        compute(st, hsv, hzv, 0, xw[(2 * pos) % DX]);
+        asm volatile("" ::: "memory");
+        load_x(r + DX, (2 * pos) % DX);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(WAIT_ODD);
+        asm volatile("" ::: "memory");
+        compute(st, hsv, hzv, 1, xw[(2 * pos + 1) % DX]);
+        asm volatile("" ::: "memory");
+        load_x(r + 1 + DX, (2 * pos + 1) % DX);
+        // The wait counts need X of a round issued wholly before the next
+        // step's codes: keep the two groups of loads in program order.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(dl + 2, st);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // The headers first (the oldest loads: complete at the first wait), shared
+    // between the waves: instruction i fills positions 64 i .. 64 i + 63.
+    {
+        const __amdgpu_buffer_rsrc_t srs = kw_rsrc(a.scales + hbase, hbytes);
+        const __amdgpu_buffer_rsrc_t zrs = kw_rsrc(a.zeros + hbase, hbytes);
+        const int total = rows_blk * a.cpr;
+        for (int i = w; i * 64 < total; i += W) {
+            const int flat = i * 64 + lane;
+            const int row = flat / a.cpr, p = flat & (a.cpr - 1);
+            const uint32_t src = flat < total ? (uint32_t)(row * a.cpr + (p ^ (row & (a.cpr - 1)))) * 16u : kKwFar;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (kw_lds_void*)(hs + i * 64), 16, (int)src, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, (kw_lds_void*)(hz + i * 64), 16, (int)src, 0, 0, 0);
+        }
+    }
+    Step ring0, ring1;
+    // The prologue issues what the steady state would have issued at the
+    // ends of rounds -4 .. -1.
+    if constexpr (DX == 4) {
+        load_x(0, 0);
+        load_x(1, 1);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(0, ring0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(DX - 2, DX - 2);
+    load_x(DX - 1, DX - 1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(1, ring1);
+    __builtin_amdgcn_sched_barrier(0);
+    // Every wave's header loads are done once its first wait has passed.
+    __builtin_amdgcn_s_waitcnt(WAIT_EVEN);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    for (int dl = 0; dl < a.nd; dl += 2) {
+        step(ring0, dl, 0);
+        step(ring1, dl + 1, 1);
+    }
+
+    // The waves' sums, added in wave order (the ring is free once every wave
+    // is past its last round).  Accumulator lane layout: batch row
+    // 16 cb + 4 g4 + i, weight row r16 of tile t; the operand carried a 1/2.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Wave w's sums go to ring object w & 1 at float offset (w >> 1) * PER * 64
+    // (W / 2 waves of TPB * NCB KB in each object of W * NCB * 4 KB: TPB <= 8).
+    constexpr int PER = TPB * NCB * 4;   // floats per lane per wave
+    static_assert((W / 2) * PER * 64 * 4 <= W * XR * 16, "partial sums must fit the ring");
+    auto red_of = [&](int ww) {
+        return reinterpret_cast<float*>((ww & 1) ? xs1 : xs0) + (ww >> 1) * PER * 64;
+    };
+    {
+        float* red = red_of(w);
+#pragma unroll
+        for (int t = 0; t < TPB; ++t)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) red[((t * NCB + cb) * 4 + i) * 64 + lane] = acc[t][cb][i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = (int)threadIdx.x; e < PER * 64; e += 64 * W) {   // e = ((t * NCB + cb) * 4 + i) * 64 + lane
+        float v = red_of(0)[e];
+#pragma unroll
+        for (int ww = 1; ww < W; ++ww) v += red_of(ww)[e];
+        const int q = e >> 6, l = e & 63;
+        const int t = q / (NCB * 4), cb = (q / 4) % NCB, i = q % 4;
+        const int row = tile0 * 16 + t * 16 + (l & 15);
+        const int b = cb * 16 + 4 * (l >> 4) + i;
+        if (row < a.N && b < a.B) a.Y[(size_t)b * a.N + row] = float_to_half_bits_rne(2.0f * v);
+    }
+}
+
+template <int NCB, int TPB>
+hipError_t launch_tpb(KwArgs a, hipStream_t stream) {
+    const int ntiles = (a.N + 15) / 16;
+    const dim3 grid((unsigned)((ntiles + TPB - 1) / TPB));
+    // Four waves (eight would double the row streams each compute unit keeps
+    // open, and the code stream slows down); four rounds of X in flight
+    // where they fit in LDS (4 * NCB * 16 KB).
+    constexpr int DX = NCB <= 2 ? 4 : 2;
+    a.nd = a.K / (256 * 4);
+    gemm_kw_kernel<NCB, TPB, DX, 4><<<grid, dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int NCB>
+hipError_t launch_ncb(const KwArgs& a, int tpb, hipStream_t stream) {
+    switch (tpb) {
+        case 4: return launch_tpb<NCB, 4>(a, stream);
+        case 5: return launch_tpb<NCB, 5>(a, stream);
+        case 6: return launch_tpb<NCB, 6>(a, stream);
+        case 7: return launch_tpb<NCB, 7>(a, stream);
+        default: return launch_tpb<NCB, 8>(a, stream);
+    }
+}
+
+}  // namespace
+
+// Tiles per block: the fewest that keep one block per compute unit, at least 4
+// (fewer would make the X stream, whole for every block, outweigh the codes).
+int kw_tiles_per_block(int64_t N, int num_cus) {
+    const int64_t ntiles = (N + 15) / 16;
+    int64_t tpb = (ntiles + num_cus - 1) / num_cus;
+    return tpb < 4 ? 4 : tpb > 8 ? 8 : (int)tpb;
+}
+
+bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits) {
+    // K = 2048, 4096 or 8192: 16, 32 or 64 groups per row (a power-of-two
+    // number of 16-byte header chunks, all of them in LDS).
+    return bits == 4 && group == 128 && B >= 1 && B <= 64 && (K == 2048 || K == 4096 || K == 8192) &&
+           N >= 16 && N <= (1 << 24);
+}
+
+// Taken past 8 batch rows (at 8 and below the tile-stream kernel is as fast
+// and reads no more X than it needs) on matrices of more than three tiles per
+// compute unit.
+bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* X, int num_cus) {
+    return B > 8 && kw_supports(B, K, N, group, bits) && reinterpret_cast<uintptr_t>(X) % 16 == 0 &&
+           (N + 15) / 16 > 3 * (int64_t)num_cus;
+}
+
+hipError_t launch_gemm_kw(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,
+                          int64_t B, int64_t K, int64_t N, int32_t group, int num_cus, hipStream_t stream) {
+    if (!kw_supports(B, K, N, group, 4) || reinterpret_cast<uintptr_t>(X) % 16 != 0) return hipErrorInvalidValue;
+    KwArgs a;
+    a.X = static_cast<const uint16_t*>(X);
+    a.codes = static_cast<const uint8_t*>(codes);
+    a.scales = static_cast<const uint16_t*>(scales);
+    a.zeros = static_cast<const uint16_t*>(zeros);
+    a.Y = static_cast<uint16_t*>(Y);
+    a.B = (int32_t)B;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.ngrp = (int32_t)(K / 128);
+    a.cpr = a.ngrp / 8;
+    const int tpb = kw_tiles_per_block(N, num_cus);
+    if (B <= 16) return launch_ncb<1>(a, tpb, stream);
+    if (B <= 32) return launch_ncb<2>(a, tpb, stream);
+    return launch_ncb<4>(a, tpb, stream);
+}
+
+}  // namespace wq

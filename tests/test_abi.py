@@ -273,6 +273,8 @@ def test_gemm_workspace_size_queries():
     st, n = _gemm_ws_size(16, K=16384, N=300)
     assert st == _lib.WQ_OK and n > 0 and n % (16 * 300 * 4) == 0     # few rows: K-slices in partials
     st, n = _gemm_ws_size(64)
+    assert st == _lib.WQ_OK and n == 0                   # tall matrix at B = 64: K-split waves, no scratch
+    st, n = _gemm_ws_size(64, K=16384)
     assert st == _lib.WQ_OK and n > 0 and n % (64 * 28672 * 4) == 0   # tiled kernel's K splits
     st, n = _gemm_ws_size(0)
     assert st == _lib.WQ_OK and n == 0                   # no-op
@@ -287,9 +289,9 @@ def test_gemm_workspace_rejected_before_launch():
     """An undersized, misaligned, or null-with-a-size workspace is refused
     before anything is enqueued (the fake pointers are never used)."""
     lib = wq.load()
-    st, need = _gemm_ws_size(64)
+    st, need = _gemm_ws_size(64, K=16384)
     assert need > 0
-    call = lambda ws, n: lib.wq_gemm_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 8192, 28672, 128, 4, 0, ws, n, None)
+    call = lambda ws, n: lib.wq_gemm_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 16384, 28672, 128, 4, 0, ws, n, None)
     assert call(FAKE, need - 1) == _lib.WQ_ERR_INVALID_ARG
     assert b"needs" in lib.wq_last_error()
     assert call(FAKE, 0) == _lib.WQ_ERR_INVALID_ARG

@@ -58,12 +58,13 @@ def test_static_scratch_matches_workspace_entry_point():
 
 
 def test_static_scratch_refuses_oversized_plans():
-    """B = 64 on the 70B-class up-projection needs about 22 MB of partials:
-    refused with WQ_ERR_UNSUPPORTED before anything is enqueued (real, if
-    uninitialized, buffers, so nothing could go wrong even if it launched)."""
+    """B = 64 on a 28672 x 16384 matrix (the tiled kernel, K split three ways)
+    needs about 22 MB of partials: refused with WQ_ERR_UNSUPPORTED before
+    anything is enqueued (real, if uninitialized, buffers, so nothing could go
+    wrong even if it launched)."""
     dev = device()
     lib = wq.load()
-    N, K, B = 28672, 8192, 64
+    N, K, B = 28672, 16384, 64
     need = wq.gemm_workspace_bytes(B, K, N, 128, 4)
     note(f"no-alloc refusal need={need}")
     assert need > STATIC_BYTES
