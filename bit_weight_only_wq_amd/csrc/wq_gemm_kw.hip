@@ -110,12 +110,11 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     const int tile0 = blockIdx.x * TPB;
     const int rows_blk = a.N - tile0 * 16 < TPB * 16 ? a.N - tile0 * 16 : TPB * 16;
     const uint32_t row_bytes = (uint32_t)a.K / 2;
-    const __amdgpu_buffer_rsrc_t crs =
-        kw_rsrc(a.codes + (size_t)tile0 * 16 * row_bytes, (uint32_t)rows_blk * row_bytes);
+    const uint8_t* const cbase = a.codes + (size_t)tile0 * 16 * row_bytes;
+    const uint32_t cbytes = (uint32_t)rows_blk * row_bytes;
     const size_t hbase = (size_t)tile0 * 16 * a.ngrp;
     const uint32_t hbytes = (uint32_t)rows_blk * a.ngrp * 2;
-    // Batch rows past B lie past the end of X and read as zeros.
-    const __amdgpu_buffer_rsrc_t xrs = kw_rsrc(a.X, (uint32_t)a.B * a.K * 2);
+    const uint32_t xbytes = (uint32_t)a.B * a.K * 2;
 
     // This lane's row in each tile (rows past N reread the block's last row;
     // their sums are not stored).
@@ -139,30 +138,36 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     for (int q = 0; q < NXL; ++q) {
         const int row = 4 * q + (lane >> 4);
         const int chunk = (lane & 15) ^ (row & 15);
-        xoff[q] = (uint32_t)row * a.K * 2 + (uint32_t)chunk * 16 + (uint32_t)d0 * 512;
+        xoff[q] = (uint32_t)row * a.K * 2 + (uint32_t)chunk * 16;
     }
-    // Rounds past the wave's range are issued too, at an offset past the end
-    // of the buffer: they read nothing and write zeros into a free slot, and
-    // every round of the loop issues the same loads (one wait count holds).
+    // Each round's loads go through a buffer whose base is the round's first
+    // byte (the per-lane offsets stay fixed, and the address arithmetic is
+    // scalar).  Batch rows past B lie past its end and read as zeros.  Rounds
+    // past the wave's range are issued too, with an empty buffer: they read
+    // nothing and write zeros into a free slot, and every round of the loop
+    // issues the same loads (one wait count holds).
     auto load_x = [&](int rl, int slot) {   // slot = rl % DX, a compile-time constant at every call
-        const uint32_t far = rl < nr ? 0u : kKwFar;   // offsets stay below 2^31 otherwise
+        const uint32_t rg = (uint32_t)(2 * d0 + rl);
+        const __amdgpu_buffer_rsrc_t xrs =
+            kw_rsrc(reinterpret_cast<const uint8_t*>(a.X) + 256u * rg, rl < nr ? xbytes - 256u * rg : 0u);
 #pragma unroll
         for (int q = 0; q < NXL; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (kw_lds_void*)(xw[slot] + q * 64), 16,
-                                                     (int)((xoff[q] + (uint32_t)rl * 256) | far), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (kw_lds_void*)(xw[slot] + q * 64), 16, (int)xoff[q], 0, 0,
+                                                     0);
     };
 
     struct Step {
         kw_v4u c[TPB][2];   // code chunks of the step's two rounds
     };
+    // The same for the code chunks of a step (128 bytes of every row from
+    // byte 128 dg on; the last row's last chunk ends within the buffer).
     auto load_step = [&](int dl, Step& st) {
-        const uint32_t far = dl < a.nd ? 0u : kKwFar;
         const uint32_t dg = (uint32_t)(d0 + dl);
+        const __amdgpu_buffer_rsrc_t crs = kw_rsrc(cbase + 128u * dg, dl < a.nd ? cbytes - 128u * dg : 0u);
 #pragma unroll
         for (int t = 0; t < TPB; ++t) {
-            const uint32_t o = (coff[t] + 128u * dg) | far;
-            st.c[t][0] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)o, 0, 0);
-            st.c[t][1] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)(o + 64u), 0, 0);
+            st.c[t][0] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)coff[t], 0, 0);
+            st.c[t][1] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)(coff[t] + 64u), 0, 0);
         }
     };
 
