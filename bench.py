@@ -102,8 +102,13 @@ def kernel_entry(name, nbytes, flops, ms_list, bound="hbm"):
 # while these files are unchanged.
 KERNEL_SOURCES = {
     "gemv": ["wq_gemv.hip", "wq_device.h"],
-    "mfma": ["wq_gemm_mfma.hip", "wq_device.h"],
+    "mfma": ["wq_gemm_mfma.hip", "wq_mfma_dq.h", "wq_device.h"],
     "xr": ["wq_gemm_xr.hip", "wq_device.h"],
+    "qs": ["wq_gemm_qs.hip", "wq_device.h"],
+    "q4": ["wq_gemm_q4.hip", "wq_device.h"],
+    "ts": ["wq_gemm_ts.hip", "wq_device.h"],
+    "sk": ["wq_gemm_sk.hip", "wq_device.h"],
+    "kw": ["wq_gemm_kw.hip", "wq_mfma_dq.h", "wq_device.h"],
     "quantize": ["wq_quantize.hip", "wq_device.h"],
     "kv_attn": ["wq_kv.hip", "wq_device.h"],
     "kv_quantize": ["wq_kv.hip", "wq_device.h"],
@@ -111,7 +116,8 @@ KERNEL_SOURCES = {
 KV_WORKLOAD = "kv_decode_7b_ctx4096"
 KV_SHAPE = (1024, 4096, 128, 128)   # heads (32 layers x 32), tokens, head dim, block
 # rocprofv3 kernel-name fragment of each family.
-KERNEL_NAMES = {"gemv": "gemv_", "mfma": "gemm_mfma_kernel", "xr": "gemm_xr_kernel",
+KERNEL_NAMES = {"gemv": "gemv_", "mfma": "gemm_mfma_kernel", "xr": "gemm_xr_kernel", "qs": "gemm_qs_kernel",
+                "q4": "gemm_q4_kernel", "ts": "gemm_ts_kernel", "sk": "gemm_sk_kernel", "kw": "gemm_kw_kernel",
                 "quantize": "quantize_"}
 
 
