@@ -14,16 +14,22 @@
 //     holds the 16-byte code chunk of row 16 t + r16 at k [32 g4, 32 g4 + 32)
 //     of the round, the weight operand of v_mfma_f32_16x16x32_f16 for the
 //     round's 4 k-steps, dequantized in registers to fp16 (q - z) * s / 2;
-//   - code chunks and group headers come two rounds at a time (the two halves
-//     of each 128-byte line of a row together) into a two-deep register ring;
-//   - a wave copies its rounds of X [16 NCB rows x 128 k] into a two-round
-//     LDS ring with LDS-DMA loads that read whole lines (4 rows x 256 bytes
-//     per instruction); chunk p of row r goes to position p ^ (r & 15), so the
-//     X-operand reads (16 rows, one chunk each, per 16 lanes) hit distinct
-//     banks;
+//   - code chunks come two rounds at a time (the two halves of each 128-byte
+//     line of a row together) into a two-deep register ring;
+//   - the group headers of the block's tiles (all of K) are copied into LDS
+//     once, at the start, by LDS-DMA loads of whole 16-byte chunks, while the
+//     first code loads are already in flight; header chunk p of row r sits at
+//     position p ^ (r & (chunks per row - 1));
+//   - a wave copies its rounds of X [16 NCB rows x 128 k] into an LDS ring of
+//     DX rounds (four at B <= 32, two past) with LDS-DMA loads that read whole
+//     lines (4 rows x 256 bytes per instruction); chunk p of row r goes to
+//     position p ^ (r & 15), so the X-operand reads (16 rows, one chunk each,
+//     per 16 lanes) hit distinct banks;
 //   - a wave's loads complete in issue order, so X and codes are issued with
-//     the same lead: X of round r + 2 after round r, the codes of step d + 2
-//     (rounds 2d + 4, 2d + 5) after round 2d + 1, behind X of round 2d + 3.
+//     a fixed lead: X of round r + DX after round r, the codes of step d + 2
+//     (rounds 2d + 4, 2d + 5) after round 2d + 1, behind that round's X; the
+//     wait before each round counts exactly the loads issued after the ones
+//     it needs.
 // Needs group 128, K = 2048, 4096 or 8192, X 16-byte aligned; it uses no
 // scratch.
 #include "wq_device.h"

@@ -36,46 +36,6 @@
 // return zero without touching memory.  No scratch memory.  Requires 4-bit
 // codes, K % 32 == 0, group % 64 == 0, an even group count per row, 16-byte
 // aligned header arrays and K <= 16384.
-// Small-batch product (B <= 8) on the matrix cores' 4 x 4 x 4 blocks, fed by a
-// stream of code chunks that goes straight from HBM into LDS:
-// Y[B,N] = X[B,K] * dequant(W)[N,K]^T.
-//
-// At decode batch sizes the product is a stream of the packed weights
-// ("Quantization & inference optimisation", "Bandwidth, not compute": 2B/w
-// FLOP per byte), and what limits such a stream is how many bytes are in
-// flight, not arithmetic.  So the kernel is built around a deep, uniform ring:
-//   - an item is 4 weight rows (a quad) x 512 k: 4 x 256 bytes of codes, one
-//     128-bit load per lane (lane 4b + j: row j, bytes 16b..16b+15 of the
-//     256), the shape HBM serves at 6 TB/s and more, plus the quad's group
-//     headers over those 512 k (4-byte loads of 16 lanes each for scales and
-//     zeros);
-//   - all of it goes straight into LDS (buffer_load ... lds), 16 items ahead
-//     of use per wave, so the ring costs no registers and the loop holds no
-//     register loads at all: every wait in it is a counted wait on one of
-//     eight LDS arrays of two items each (the compiler tracks each array on
-//     its own); every lane reads back the 16 code bytes it loaded;
-//   - v_mfma_f32_4x4x4_16b_f16 takes that layout as it is: block b (lanes
-//     4b..4b+3) multiplies the 32 k of chunk b, lane 4b + j holding row j of
-//     the codes (B operand) and batch row j of X (A operand);
-//   - a wave keeps the same one, two or four 512-k positions of K for the
-//     whole kernel, so its X operands and their chunk sums live in registers,
-//     loaded once; the P waves of a row stream split K between them and walk
-//     the stream's quads together;
-//   - codes unpack exactly to fp16 1024 + q (even k) and 64 + q (odd k); each
-//     block's accumulation starts at -C1 (the offsets' weighted X sum) and the
-//     chunk's group header is applied once per item in fp32 ("the kernel
-//     reconstructs an approximate float from the integer and the endpoints as
-//     it reads", "Quantization"):
-//         sum_k (q - z) s x = s * (sum_k u_k x_k - C1 - z * C2);
-//   - after a quad's positions, the 16 blocks' sums of each (batch row, weight
-//     row) are added across lanes (two half swaps and two row rotations) and
-//     the wave's 16 sums per set go to LDS; every 16 items the block meets at
-//     a barrier (one that leaves the loads in flight), adds the P waves' sums
-//     of every finished output in wave order (deterministic) and writes Y.
-// Loads past a row's end or the stream's end fall outside the buffer and
-// return zero without touching memory.  No scratch memory.  Requires 4-bit
-// codes, K % 32 == 0, group % 64 == 0, an even group count per row, 4-byte
-// aligned header arrays and K <= 16384.
 #include "wq_device.h"
 #include "wq_launch.h"
 
