@@ -29,7 +29,9 @@
 //     a fixed lead: X of round r + DX after round r, the codes of step d + 2
 //     (rounds 2d + 4, 2d + 5) after round 2d + 1, behind that round's X; the
 //     wait before each round counts exactly the loads issued after the ones
-//     it needs.
+//     it needs;
+//   - blocks start their walks through their quarters at different steps, so
+//     that the chip's loads are spread over the columns of the matrix.
 // Needs group 128, K = 2048, 4096 or 8192, X 16-byte aligned; it uses no
 // scratch.
 #include "wq_device.h"
@@ -136,6 +138,10 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     }
     const int d0 = w * a.nd;   // the wave's first two-round step
     const int nr = 2 * a.nd;   // the wave's rounds
+    // Blocks start their walks at different steps (and wrap), so that the
+    // chip's loads do not all fall on the same columns at once; blocks are
+    // dealt to the 8 XCDs in turn, so neighbours on one XCD differ too.
+    const int soff = (int)((blockIdx.x + (blockIdx.x >> 3)) & (uint32_t)(a.nd - 1));
 
     // X of local round rl: instruction q covers rows 4q .. 4q + 3; lane l takes
     // chunk (l & 15) ^ (row & 15) of row 4q + l / 16 and writes position l.
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     // nothing and write zeros into a free slot, and every round of the loop
     // issues the same loads (one wait count holds).
     auto load_x = [&](int rl, int slot) {   // slot = rl % DX, a compile-time constant at every call
-        const uint32_t rg = (uint32_t)(2 * d0 + rl);
+        const uint32_t rg = (uint32_t)(2 * d0 + ((rl + 2 * soff) & (nr - 1)));
         const __amdgpu_buffer_rsrc_t xrs =
             kw_rsrc(reinterpret_cast<const uint8_t*>(a.X) + 256u * rg, rl < nr ? xbytes - 256u * rg : 0u);
 #pragma unroll
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     // The same for the code chunks of a step (128 bytes of every row from
     // byte 128 dg on; the last row's last chunk ends within the buffer).
     auto load_step = [&](int dl, Step& st) {
-        const uint32_t dg = (uint32_t)(d0 + dl);
+        const uint32_t dg = (uint32_t)(d0 + ((dl + soff) & (a.nd - 1)));
         const __amdgpu_buffer_rsrc_t crs = kw_rsrc(cbase + 128u * dg, dl < a.nd ? cbytes - 128u * dg : 0u);
 #pragma unroll
         for (int t = 0; t < TPB; ++t) {
@@ -224,7 +230,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
         __builtin_amdgcn_s_waitcnt(WAIT_EVEN);
         asm volatile("" ::: "memory");
         // The step's two groups (2 dg, 2 dg + 1) share one 8-group chunk.
-        const int dg = d0 + dl;
+        const int dg = d0 + ((dl + soff) & (a.nd - 1));
         uint32_t hsv[TPB], hzv[TPB];
 #pragma unroll
         for (int t = 0; t < TPB; ++t) {
