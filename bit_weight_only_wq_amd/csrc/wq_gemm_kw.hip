@@ -13,7 +13,11 @@
 //   - K is walked in rounds of 128 k (one group): lane (r16, g4) of tile t
 //     holds the 16-byte code chunk of row 16 t + r16 at k [32 g4, 32 g4 + 32)
 //     of the round, the weight operand of v_mfma_f32_16x16x32_f16 for the
-//     round's 4 k-steps, dequantized in registers to fp16 (q - z) * s / 2;
+//     round's 4 k-steps: at B <= 16 the exact integers 1024 + q (even k) and
+//     64 + q (odd k), with the round's group header applied to the products
+//     in fp32 (s * (sum u x - C1 - z C2), C1 and C2 from two more products
+//     per k-step), past 16 dequantized in registers to fp16 (q - z) * s / 2,
+//     once for all the batch blocks;
 //   - code chunks come two rounds at a time (the two halves of each 128-byte
 //     line of a row together) into a two-deep register ring;
 //   - the group headers of the block's tiles (all of K) are copied into LDS
@@ -86,7 +90,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kw_rsrc(const void* base, uint
 // DX: rounds in the X ring (2 or 4): X is issued DX - 1 rounds before use,
 // the codes of a step two rounds before its first round.  W: waves per block
 // (one per SIMD), each taking a W-th of K.
-template <int NCB, int TPB, int DX, int W>
+template <int NCB, int TPB, int DX, int W, bool EXACT>
 __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     static_assert(DX == 2 || DX == 4, "an X ring of 2 or 4 rounds");
     constexpr int XR = NCB * 16 * 16;   // 16-byte X chunks per round
@@ -185,6 +189,11 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
 
     const dq::DqConsts cst{vgpr_const(0x000F000Fu), vgpr_const(0x00F000F0u), vgpr_const(0x60006000u),
                            vgpr_const(0x50005000u)};
+    // Exact-integer operands: exponents of 1024 (ulp 1) and 64 (ulp 1/16),
+    // and the B operands whose products give C1 and C2 (same k order).
+    const uint32_t ex_lo = vgpr_const(0x64006400u), ex_hi = vgpr_const(0x54005400u);
+    const h8_t koff = __builtin_bit_cast(h8_t, uint4{ex_lo, ex_hi, ex_lo, ex_hi});
+    const h8_t kone = __builtin_bit_cast(h8_t, uint4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
     const h2_t zmul = {(_Float16)0.5f, (_Float16)0.5f};
     const h2_t zadd = {(_Float16)512.0f, (_Float16)32.0f};
 
@@ -196,6 +205,58 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
 
     // One round: half h of a step's codes and headers, X from LDS slot xr.
     auto compute = [&](const Step& st, const uint32_t* hsv, const uint32_t* hzv, int h, const uint4* xr) {
+        if constexpr (EXACT) {
+            // The codes enter as exact integers (1024 + q at even k, 64 + q at
+            // odd k); two more products per k-step give C1 = sum off_k x_k and
+            // C2 = sum x_k in every column, and the group header is applied
+            // once per round in fp32:  s * (sum u x - C1 - z C2).
+            float sf[TPB], zf[TPB];
+#pragma unroll
+            for (int t = 0; t < TPB; ++t) {
+                const h2_t s2 = as_h2(hsv[t]), z2 = as_h2(hzv[t]);
+                sf[t] = (float)(h ? s2.y : s2.x);
+                zf[t] = (float)(h ? z2.y : z2.x);
+            }
+            f4_t c1[NCB], c2[NCB], ra[TPB][NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                c1[cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                c2[cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t = 0; t < TPB; ++t) ra[t][cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h8_t xo[NCB];
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    xo[cb] = __builtin_bit_cast(h8_t, dq::permute8<4>(xr[(cb * 16 + r16) * 16 + ((4 * g4 + j) ^ r16)]));
+                    c1[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xo[cb], koff, c1[cb], 0, 0, 0);
+                    c2[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xo[cb], kone, c2[cb], 0, 0, 0);
+                }
+#pragma unroll
+                for (int t = 0; t < TPB; ++t) {
+                    const uint4 cw = __builtin_bit_cast(uint4, st.c[t][h]);
+                    const uint32_t wv = j == 0 ? cw.x : j == 1 ? cw.y : j == 2 ? cw.z : cw.w;
+                    const uint32_t w8 = wv >> 8;
+                    const uint4 u = {(wv & cst.m_lo) | ex_lo, (wv & cst.m_hi) | ex_hi, (w8 & cst.m_lo) | ex_lo,
+                                     (w8 & cst.m_hi) | ex_hi};
+                    const h8_t bop = __builtin_bit_cast(h8_t, u);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        ra[t][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xo[cb], bop, ra[t][cb], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TPB; ++t)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[t][cb][i] = __builtin_fmaf(
+                            sf[t], __builtin_fmaf(-zf[t], c2[cb][i], ra[t][cb][i] - c1[cb][i]), acc[t][cb][i]);
+            return;
+        }
         h2_t nz[TPB], ss[TPB];
         const uint32_t sel = h ? 0x07060706u : 0x05040504u;   // that group's half, twice
 #pragma unroll
@@ -328,7 +389,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
         const int t = q / (NCB * 4), cb = (q / 4) % NCB, i = q % 4;
         const int row = tile0 * 16 + t * 16 + (l & 15);
         const int b = cb * 16 + 4 * (l >> 4) + i;
-        if (row < a.N && b < a.B) a.Y[(size_t)b * a.N + row] = float_to_half_bits_rne(2.0f * v);
+        if (row < a.N && b < a.B) a.Y[(size_t)b * a.N + row] = float_to_half_bits_rne(EXACT ? v : 2.0f * v);
     }
 }
 
@@ -338,10 +399,14 @@ hipError_t launch_tpb(KwArgs a, hipStream_t stream) {
     const dim3 grid((unsigned)((ntiles + TPB - 1) / TPB));
     // Four waves (eight would double the row streams each compute unit keeps
     // open, and the code stream slows down); four rounds of X in flight
-    // where they fit in LDS (4 * NCB * 16 KB).
+    // where they fit in LDS (4 * NCB * 16 KB).  Exact-integer operands with
+    // the header applied per round at one batch block, where the fp16
+    // dequantization of every weight feeds a single product; from two batch
+    // blocks on, the per-round correction of every block costs more than
+    // the dequantization it saves.
     constexpr int DX = NCB <= 2 ? 4 : 2;
     a.nd = a.K / (256 * 4);
-    gemm_kw_kernel<NCB, TPB, DX, 4><<<grid, dim3(256), 0, stream>>>(a);
+    gemm_kw_kernel<NCB, TPB, DX, 4, NCB == 1><<<grid, dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
