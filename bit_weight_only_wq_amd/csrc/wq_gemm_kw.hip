@@ -438,11 +438,11 @@ bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits) {
            N >= 16 && N <= (1 << 24);
 }
 
-// Taken past 8 batch rows (at 8 and below the tile-stream kernel is as fast
-// and reads no more X than it needs) on matrices of more than three tiles per
-// compute unit.
+// Taken past 4 batch rows (at 4 and below the quad-stream kernel reads the
+// codes in a faster load shape and needs no padding rows) on matrices of more
+// than three tiles per compute unit.
 bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* X, int num_cus) {
-    return B > 8 && kw_supports(B, K, N, group, bits) && reinterpret_cast<uintptr_t>(X) % 16 == 0 &&
+    return B > 4 && kw_supports(B, K, N, group, bits) && reinterpret_cast<uintptr_t>(X) % 16 == 0 &&
            (N + 15) / 16 > 3 * (int64_t)num_cus;
 }
 

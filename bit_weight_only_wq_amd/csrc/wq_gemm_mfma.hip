@@ -414,8 +414,8 @@ bool qs_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, cons
            aligned_to(zeros, 16);
 }
 
-// The tile-stream kernel takes B <= 16 on tall matrices (at B <= 4 where the
-// quad kernels do not).
+// The tile-stream kernel takes B <= 16 on matrices of at least 2048 rows
+// (where the quad and K-split-wave kernels do not).
 bool ts_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
               const void* zeros) {
     return ts_supports(B, K, N, group, bits) && N >= 2048 && aligned_to(scales, 8) && aligned_to(zeros, 8);
@@ -432,9 +432,11 @@ hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales
                             int32_t group, int32_t bits, int num_cus, const Scratch& ws,
                             hipStream_t stream) {
     // Tall matrices at B <= 4 take the quad-stream kernel (groups of 64 and
-    // more) or the quad-row kernel, at B <= 16 the tile-stream kernel or (with
-    // header arrays it cannot stage) the streaming 16-row kernel; none of
-    // them needs scratch.
+    // more) or the quad-row kernel; from B = 5 to 64, matrices of more than
+    // three 16-row tiles per compute unit take the K-split-wave kernel, and
+    // up to B = 16 the others take the tile-stream kernel or (with header
+    // arrays it cannot stage) the streaming 16-row kernel; none of them needs
+    // scratch.
     if (qs_takes(B, K, N, group, bits, scales, zeros)) {
         if (ws.sizing()) return hipSuccess;
         return launch_gemm_qs(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
