@@ -60,14 +60,14 @@ def parse():
     p.add_argument("--format", choices=["nf4", "offset"], default=None,
                    help="another weight format on the step's workload: NF4 at blocks of 64, or "
                         "the float-offset variant at the workload's group and --bits; quantize + "
-                        "GEMV at --batches (default 1) (table line)")
+                        "product at --batches (default 1) (table line)")
     p.add_argument("--ceiling", action="store_true",
                    help="what plain torch kernels read and copy on this GPU over 1 GiB buffers "
                         "(context for the roofline fractions; table line)")
     p.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
     p.add_argument("--bits", type=int, default=0,
                    help="code width of the step (default: the workload's, 4); 2 and 3 take "
-                        "the bit-stream GEMV")
+                        "the bit-stream GEMV at B = 1 and past 32, the matrix cores between")
     p.add_argument("--batches", default="",
                    help="comma-separated batch sizes of the step (default: the workload's)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,

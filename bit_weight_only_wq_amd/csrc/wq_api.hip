@@ -268,8 +268,6 @@ static wq_status check_gemm_shape(int64_t B, int64_t K, int64_t N, int32_t group
             return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: K=%lld and group=%lld must be multiples of the 16-byte chunk",
                         K, group);
     }
-    if (low && path == WQ_PATH_MFMA)
-        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: bits=%lld runs on the GEMV path only", bits);
     if (low && !wq::gemv_lowbit_supports(K, group, bits))
         return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: the 2/3-bit GEMV does not take K=%lld at bits=%lld", K, bits);
     if (B == 0 || N == 0) {
@@ -277,7 +275,15 @@ static wq_status check_gemm_shape(int64_t B, int64_t K, int64_t N, int32_t group
         return WQ_OK;
     }
     if (low) {
-        path = WQ_PATH_GEMV;
+        // The K-split-wave matrix-core kernel where it takes the shape (X's
+        // alignment is checked with the pointers), the bit-stream GEMV
+        // otherwise.
+        const bool kw = wq::kw_takes(B, K, N, group, bits, false, nullptr, num_cus());
+        if (path == WQ_PATH_MFMA && !kw)
+            return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: bits=%lld takes the MFMA path only for 2 <= B <= 32, "
+                        "group 128, K = 2048, 4096 or 8192 and more than three 16-row tiles per compute unit",
+                        bits);
+        path = (path == WQ_PATH_GEMV || !kw) ? WQ_PATH_GEMV : WQ_PATH_MFMA;
         return WQ_OK;
     }
     const bool gemv_ok = wq::gemv_supports(K, bits);
@@ -599,6 +605,10 @@ wq_status wq_gemm_offset(const void* X, const void* codes, const void* scales, c
     if (!X || !codes || !scales || !mins || !Y) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_offset: null pointer");
     if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(mins, 2) || !aligned(Y, 2))
         return fail(WQ_ERR_MISALIGNED, "wq_gemm_offset: X and codes need 16-byte alignment");
+    if (wq::kw_takes(B, K, N, group, bits, true, X, num_cus()))
+        return check_hip(wq::launch_gemm_kw(X, codes, scales, mins, Y, B, K, N, group, bits, true, num_cus(),
+                                            static_cast<hipStream_t>(stream)),
+                         "wq_gemm_offset (mfma) launch");
     return check_hip(wq::launch_gemv_lowbit(X, codes, scales, mins, Y, B, K, N, group, bits, 1, num_cus(),
                                             static_cast<hipStream_t>(stream)),
                      "wq_gemm_offset launch");

@@ -51,6 +51,13 @@ constexpr uint32_t kKwFar = 0x80000000u;    // a per-lane offset past every buff
 
 typedef __attribute__((address_space(3))) void kw_lds_void;
 typedef unsigned int kw_v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int kw_v3u __attribute__((ext_vector_type(3)));
+typedef unsigned int kw_v2u __attribute__((ext_vector_type(2)));
+
+// How the weight operand is formed: dequantized in registers to fp16
+// (q - z) * s / 2 (4-bit codes), or exact integers with the header applied
+// per round in fp32, with an integer zero point or a float offset.
+constexpr int KW_DEQUANT = 0, KW_ZERO = 1, KW_OFFSET = 2;
 
 struct KwArgs {
     const uint16_t* X;
@@ -90,9 +97,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kw_rsrc(const void* base, uint
 // DX: rounds in the X ring (2 or 4): X is issued DX - 1 rounds before use,
 // the codes of a step two rounds before its first round.  W: waves per block
 // (one per SIMD), each taking a W-th of K.
-template <int NCB, int TPB, int DX, int W, bool EXACT>
+template <int NCB, int TPB, int DX, int W, int BITS, int MODE>
 __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     static_assert(DX == 2 || DX == 4, "an X ring of 2 or 4 rounds");
+    static_assert(BITS == 2 || BITS == 3 || BITS == 4, "2-, 3- or 4-bit codes");
+    static_assert(MODE != KW_DEQUANT || BITS == 4, "fp16 dequantization takes 4-bit codes");
+    constexpr bool EXACT = MODE != KW_DEQUANT;
     constexpr int XR = NCB * 16 * 16;   // 16-byte X chunks per round
     // The rounds of the ring are separate objects, so that the compiler can
     // tell the LDS-DMA writes of one from those of another and waits only for
@@ -121,7 +131,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
 
     const int tile0 = blockIdx.x * TPB;
     const int rows_blk = a.N - tile0 * 16 < TPB * 16 ? a.N - tile0 * 16 : TPB * 16;
-    const uint32_t row_bytes = (uint32_t)a.K / 2;
+    const uint32_t row_bytes = (uint32_t)a.K * BITS / 8;
+    constexpr uint32_t RB = 16 * BITS;   // bytes of a row per 128-k round
     const uint8_t* const cbase = a.codes + (size_t)tile0 * 16 * row_bytes;
     const uint32_t cbytes = (uint32_t)rows_blk * row_bytes;
     const size_t hbase = (size_t)tile0 * 16 * a.ngrp;
@@ -136,7 +147,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     for (int t = 0; t < TPB; ++t) {
         int rl = t * 16 + r16;
         rl = rl < rows_blk ? rl : rows_blk - 1;
-        coff[t] = (uint32_t)rl * row_bytes + 16u * g4;
+        coff[t] = (uint32_t)rl * row_bytes + (RB / 4) * g4;
         hrow[t] = rl * a.cpr;
         hswz[t] = rl & (a.cpr - 1);
     }
@@ -173,26 +184,62 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     };
 
     struct Step {
-        kw_v4u c[TPB][2];   // code chunks of the step's two rounds
+        uint32_t c[TPB][2][BITS];   // this lane's code words of the step's two rounds
     };
-    // The same for the code chunks of a step (128 bytes of every row from
-    // byte 128 dg on; the last row's last chunk ends within the buffer).
+    // The same for the code words of a step (2 RB bytes of every row from
+    // byte 2 RB dg on; the last row's last words end within the buffer): one
+    // load of BITS words per lane, tile and round (32 codes: k in
+    // [32 g4, 32 g4 + 32) of the round).
+    auto load_words = [&](const __amdgpu_buffer_rsrc_t& crs, uint32_t off, uint32_t* dst) {
+        if constexpr (BITS == 4) {
+            const kw_v4u v = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)off, 0, 0);
+            dst[0] = v.x, dst[1] = v.y, dst[2] = v.z, dst[3] = v.w;
+        } else if constexpr (BITS == 3) {
+            const kw_v3u v = __builtin_amdgcn_raw_buffer_load_b96(crs, (int)off, 0, 0);
+            dst[0] = v.x, dst[1] = v.y, dst[2] = v.z;
+        } else {
+            const kw_v2u v = __builtin_amdgcn_raw_buffer_load_b64(crs, (int)off, 0, 0);
+            dst[0] = v.x, dst[1] = v.y;
+        }
+    };
+    // (At 2 bits, one 16-byte load per lane covering both rounds of a step,
+    // regrouped across lanes with half swaps, measured slower than two 8-byte
+    // loads: 27.8/29.8 against 26.2/27.8 us at B = 16 on 28672 x 8192.)
     auto load_step = [&](int dl, Step& st) {
         const uint32_t dg = (uint32_t)(d0 + ((dl + soff) & (a.nd - 1)));
-        const __amdgpu_buffer_rsrc_t crs = kw_rsrc(cbase + 128u * dg, dl < a.nd ? cbytes - 128u * dg : 0u);
+        const __amdgpu_buffer_rsrc_t crs = kw_rsrc(cbase + 2 * RB * dg, dl < a.nd ? cbytes - 2 * RB * dg : 0u);
 #pragma unroll
         for (int t = 0; t < TPB; ++t) {
-            st.c[t][0] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)coff[t], 0, 0);
-            st.c[t][1] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)(coff[t] + 64u), 0, 0);
+            load_words(crs, coff[t], st.c[t][0]);
+            load_words(crs, coff[t] + RB, st.c[t][1]);
         }
     };
 
     const dq::DqConsts cst{vgpr_const(0x000F000Fu), vgpr_const(0x00F000F0u), vgpr_const(0x60006000u),
                            vgpr_const(0x50005000u)};
-    // Exact-integer operands: exponents of 1024 (ulp 1) and 64 (ulp 1/16),
-    // and the B operands whose products give C1 and C2 (same k order).
-    const uint32_t ex_lo = vgpr_const(0x64006400u), ex_hi = vgpr_const(0x54005400u);
-    const h8_t koff = __builtin_bit_cast(h8_t, uint4{ex_lo, ex_hi, ex_lo, ex_hi});
+    // Exact-integer operands.  A code masked in place at bit position p of a
+    // half, under an exponent whose ulp is 2^-p, is the fp16 value E + q
+    // exactly; the B operand whose products give C1 holds each slot's E, and
+    // the one for C2 holds ones (same k order).
+    //   4 bits: word j = k-step j, pairs (k0,k4) (k1,k5) (k2,k6) (k3,k7) at
+    //     bit 0, 4, 0, 4 (w, w, w >> 8, w >> 8): E = 1024, 64, 1024, 64.
+    //   3 bits: 24-bit unit j = k-step j; t = low half of u | high half of
+    //     u << 4 holds the pair (k_r, k_r+4) at bit 3r, r = 0..3; r = 3 (bits
+    //     9-11) does not fit the 10-bit mantissa and is taken from t >> 9 at
+    //     bit 0: E = 1024, 128, 16, 1024.
+    //   2 bits: word d = k-steps 2d, 2d + 1; (w, w >> 8) masked at bit 2m hold
+    //     (k_m, k_m+8) and (k_m+4, k_m+12); k-step 2d + hs takes m = 2 hs and
+    //     2 hs + 1: E = 1024, 1024, 256, 256 (hs 0) and 64, 64, 16, 16 (hs 1).
+    constexpr uint32_t E1024 = 0x64006400u, E256 = 0x5C005C00u, E128 = 0x58005800u, E64 = 0x54005400u,
+                       E16 = 0x4C004C00u;
+    const uint32_t ex_a = vgpr_const(BITS == 2 ? E256 : BITS == 3 ? E128 : E64);
+    const uint32_t ex_b = vgpr_const(BITS == 2 ? E64 : E16);
+    const uint32_t ex_c = vgpr_const(E16);
+    const uint32_t ex_0 = vgpr_const(E1024);
+    const uint32_t mk_0 = vgpr_const(BITS == 2 ? 0x00030003u : BITS == 3 ? 0x00070007u : 0x000F000Fu);
+    const uint32_t mk_1 = vgpr_const(BITS == 2 ? 0x000C000Cu : BITS == 3 ? 0x00380038u : 0x00F000F0u);
+    const uint32_t mk_2 = vgpr_const(BITS == 2 ? 0x00300030u : 0x01C001C0u);
+    const uint32_t mk_3 = vgpr_const(0x00C000C0u);
     const h8_t kone = __builtin_bit_cast(h8_t, uint4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
     const h2_t zmul = {(_Float16)0.5f, (_Float16)0.5f};
     const h2_t zadd = {(_Float16)512.0f, (_Float16)32.0f};
@@ -206,10 +253,15 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     // One round: half h of a step's codes and headers, X from LDS slot xr.
     auto compute = [&](const Step& st, const uint32_t* hsv, const uint32_t* hzv, int h, const uint4* xr) {
         if constexpr (EXACT) {
-            // The codes enter as exact integers (1024 + q at even k, 64 + q at
-            // odd k); two more products per k-step give C1 = sum off_k x_k and
-            // C2 = sum x_k in every column, and the group header is applied
-            // once per round in fp32:  s * (sum u x - C1 - z C2).
+            // The codes enter as exact integers E + q (E per operand slot); two
+            // more products per k-step give C1 = sum E_k x_k and C2 = sum x_k
+            // in every column, and the group header is applied once per round
+            // in fp32:  s * (sum u x - C1) - s z C2  (integer zero point), or
+            // s * (sum u x - C1) + m C2  (float offset m).  At 2 and 3 bits E
+            // is subtracted from each operand in fp16 (exact), so the operand
+            // is q itself and C1 = 0: with so few levels most codes sit near
+            // the zero point, sum q x is small next to sum E x, and carrying E
+            // through the fp32 sums loses too much of it.
             float sf[TPB], zf[TPB];
 #pragma unroll
             for (int t = 0; t < TPB; ++t) {
@@ -225,22 +277,64 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
 #pragma unroll
                 for (int t = 0; t < TPB; ++t) ra[t][cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
             }
+            uint4 xc[NCB][2];   // 2 bits: the two X chunks of a code word
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 h8_t xo[NCB];
+                uint4 ko;
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
-                    xo[cb] = __builtin_bit_cast(h8_t, dq::permute8<4>(xr[(cb * 16 + r16) * 16 + ((4 * g4 + j) ^ r16)]));
-                    c1[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xo[cb], koff, c1[cb], 0, 0, 0);
+                    const uint4* xrow = xr + (cb * 16 + r16) * 16;
+                    if constexpr (BITS == 2) {
+                        const int hs = j & 1;
+                        if (hs == 0) {
+                            xc[cb][0] = xrow[(4 * g4 + j) ^ r16];
+                            xc[cb][1] = xrow[(4 * g4 + j + 1) ^ r16];
+                        }
+                        const uint32_t a0 = hs ? xc[cb][0].y : xc[cb][0].x, a1 = hs ? xc[cb][1].y : xc[cb][1].x;
+                        const uint32_t b0 = hs ? xc[cb][0].w : xc[cb][0].z, b1 = hs ? xc[cb][1].w : xc[cb][1].z;
+                        const uint4 v = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(b1, b0, 0x05040100u),
+                                         __builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(b1, b0, 0x07060302u)};
+                        xo[cb] = __builtin_bit_cast(h8_t, v);
+                    } else {
+                        xo[cb] = __builtin_bit_cast(h8_t, dq::permute8<4>(xrow[(4 * g4 + j) ^ r16]));
+                    }
+                }
+                if constexpr (BITS == 4) ko = uint4{ex_0, ex_a, ex_0, ex_a};
+                else if constexpr (BITS == 3) ko = uint4{ex_0, ex_a, ex_b, ex_0};
+                else ko = (j & 1) ? uint4{ex_b, ex_b, ex_c, ex_c} : uint4{ex_0, ex_0, ex_a, ex_a};
+                const h8_t koff = __builtin_bit_cast(h8_t, ko);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    if constexpr (BITS == 4)
+                        c1[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xo[cb], koff, c1[cb], 0, 0, 0);
                     c2[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xo[cb], kone, c2[cb], 0, 0, 0);
                 }
 #pragma unroll
                 for (int t = 0; t < TPB; ++t) {
-                    const uint4 cw = __builtin_bit_cast(uint4, st.c[t][h]);
-                    const uint32_t wv = j == 0 ? cw.x : j == 1 ? cw.y : j == 2 ? cw.z : cw.w;
-                    const uint32_t w8 = wv >> 8;
-                    const uint4 u = {(wv & cst.m_lo) | ex_lo, (wv & cst.m_hi) | ex_hi, (w8 & cst.m_lo) | ex_lo,
-                                     (w8 & cst.m_hi) | ex_hi};
+                    const uint32_t* cw = st.c[t][h];
+                    uint4 u;
+                    if constexpr (BITS == 4) {
+                        const uint32_t wv = cw[j], w8 = wv >> 8;
+                        u = uint4{(wv & mk_0) | ex_0, (wv & mk_1) | ex_a, (w8 & mk_0) | ex_0, (w8 & mk_1) | ex_a};
+                    } else if constexpr (BITS == 3) {
+                        const uint32_t uu = j == 0   ? cw[0]
+                                            : j == 1 ? __builtin_amdgcn_alignbit(cw[1], cw[0], 24)
+                                            : j == 2 ? __builtin_amdgcn_alignbit(cw[2], cw[1], 16)
+                                                     : cw[2] >> 8;
+                        const uint32_t tt = ((uu << 4) & 0xFFFF0000u) | (uu & 0x0000FFFFu);
+                        u = uint4{(tt & mk_0) | ex_0, (tt & mk_1) | ex_a, (tt & mk_2) | ex_b, ((tt >> 9) & mk_0) | ex_0};
+                    } else {
+                        const uint32_t wv = cw[j >> 1], w8 = wv >> 8;
+                        if (j & 1)
+                            u = uint4{(wv & mk_2) | ex_b, (w8 & mk_2) | ex_b, (wv & mk_3) | ex_c, (w8 & mk_3) | ex_c};
+                        else
+                            u = uint4{(wv & mk_0) | ex_0, (w8 & mk_0) | ex_0, (wv & mk_1) | ex_a, (w8 & mk_1) | ex_a};
+                    }
+                    if constexpr (BITS != 4) {   // q, exactly
+                        u = uint4{as_u32(as_h2(u.x) - as_h2(ko.x)), as_u32(as_h2(u.y) - as_h2(ko.y)),
+                                  as_u32(as_h2(u.z) - as_h2(ko.z)), as_u32(as_h2(u.w) - as_h2(ko.w))};
+                    }
                     const h8_t bop = __builtin_bit_cast(h8_t, u);
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb)
@@ -252,9 +346,13 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[t][cb][i] = __builtin_fmaf(
-                            sf[t], __builtin_fmaf(-zf[t], c2[cb][i], ra[t][cb][i] - c1[cb][i]), acc[t][cb][i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const float v = ra[t][cb][i] - c1[cb][i];
+                        if constexpr (MODE == KW_OFFSET)
+                            acc[t][cb][i] = __builtin_fmaf(zf[t], c2[cb][i], __builtin_fmaf(sf[t], v, acc[t][cb][i]));
+                        else
+                            acc[t][cb][i] = __builtin_fmaf(sf[t], __builtin_fmaf(-zf[t], c2[cb][i], v), acc[t][cb][i]);
+                    }
             return;
         }
         h2_t nz[TPB], ss[TPB];
@@ -272,7 +370,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
                 xo[cb] = __builtin_bit_cast(h8_t, dq::permute8<4>(xr[(cb * 16 + r16) * 16 + ((4 * g4 + j) ^ r16)]));
 #pragma unroll
             for (int t = 0; t < TPB; ++t) {
-                const uint4 cw = __builtin_bit_cast(uint4, st.c[t][h]);
+                const uint32_t* cwp = st.c[t][h];
+                const uint4 cw = {cwp[0], cwp[1], cwp[2], cwp[3]};
                 const h8_t bop = dq::dequant<4>(cw, j, cst, nz[t], ss[t]);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
@@ -393,32 +492,36 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     }
 }
 
-template <int NCB, int TPB>
+template <int NCB, int TPB, int BITS, int MODE>
 hipError_t launch_tpb(KwArgs a, hipStream_t stream) {
     const int ntiles = (a.N + 15) / 16;
     const dim3 grid((unsigned)((ntiles + TPB - 1) / TPB));
     // Four waves (eight would double the row streams each compute unit keeps
     // open, and the code stream slows down); four rounds of X in flight
-    // where they fit in LDS (4 * NCB * 16 KB).  Exact-integer operands with
-    // the header applied per round at one batch block, where the fp16
-    // dequantization of every weight feeds a single product; from two batch
-    // blocks on, the per-round correction of every block costs more than
-    // the dequantization it saves.
+    // where they fit in LDS (4 * NCB * 16 KB).
     constexpr int DX = NCB <= 2 ? 4 : 2;
     a.nd = a.K / (256 * 4);
-    gemm_kw_kernel<NCB, TPB, DX, 4, NCB == 1><<<grid, dim3(256), 0, stream>>>(a);
+    gemm_kw_kernel<NCB, TPB, DX, 4, BITS, MODE><<<grid, dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
-template <int NCB>
+template <int NCB, int BITS, int MODE>
 hipError_t launch_ncb(const KwArgs& a, int tpb, hipStream_t stream) {
     switch (tpb) {
-        case 4: return launch_tpb<NCB, 4>(a, stream);
-        case 5: return launch_tpb<NCB, 5>(a, stream);
-        case 6: return launch_tpb<NCB, 6>(a, stream);
-        case 7: return launch_tpb<NCB, 7>(a, stream);
-        default: return launch_tpb<NCB, 8>(a, stream);
+        case 4: return launch_tpb<NCB, 4, BITS, MODE>(a, stream);
+        case 5: return launch_tpb<NCB, 5, BITS, MODE>(a, stream);
+        case 6: return launch_tpb<NCB, 6, BITS, MODE>(a, stream);
+        case 7: return launch_tpb<NCB, 7, BITS, MODE>(a, stream);
+        default: return launch_tpb<NCB, 8, BITS, MODE>(a, stream);
     }
+}
+
+// Up to 32 batch rows: one or two 16-row batch blocks on exact-integer
+// operands (2-, 3-bit codes, float offsets).
+template <int BITS, int MODE>
+hipError_t launch_exact(const KwArgs& a, int tpb, hipStream_t stream) {
+    if (a.B <= 16) return launch_ncb<1, BITS, MODE>(a, tpb, stream);
+    return launch_ncb<2, BITS, MODE>(a, tpb, stream);
 }
 
 }  // namespace
@@ -431,24 +534,31 @@ int kw_tiles_per_block(int64_t N, int num_cus) {
     return tpb < 4 ? 4 : tpb > 8 ? 8 : (int)tpb;
 }
 
-bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits) {
+bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset) {
     // K = 2048, 4096 or 8192: 16, 32 or 64 groups per row (a power-of-two
     // number of 16-byte header chunks, all of them in LDS).
-    return bits == 4 && group == 128 && B >= 1 && B <= 64 && (K == 2048 || K == 4096 || K == 8192) &&
-           N >= 16 && N <= (1 << 24);
+    const bool int4 = bits == 4 && !offset;
+    return (bits == 2 || bits == 3 || bits == 4) && group == 128 && B >= 1 && B <= (int4 ? 64 : 32) &&
+           (K == 2048 || K == 4096 || K == 8192) && N >= 16 && N <= (1 << 24);
 }
 
-// Taken past 4 batch rows (at 4 and below the quad-stream kernel reads the
-// codes in a faster load shape and needs no padding rows) on matrices of more
-// than three tiles per compute unit.
-bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* X, int num_cus) {
-    return B > 4 && kw_supports(B, K, N, group, bits) && reinterpret_cast<uintptr_t>(X) % 16 == 0 &&
-           (N + 15) / 16 > 3 * (int64_t)num_cus;
+// Taken on matrices of more than three tiles per compute unit; for 4-bit
+// codes with integer zero points past 4 batch rows (at 4 and below the
+// quad-stream kernel reads the codes in a faster load shape and needs no
+// padding rows), for the other formats from 2 batch rows (at 1 the bit-stream
+// GEMV streams them as fast).
+bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset, const void* X,
+              int num_cus) {
+    const bool int4 = bits == 4 && !offset;
+    return B > (int4 ? 4 : 1) && kw_supports(B, K, N, group, bits, offset) &&
+           reinterpret_cast<uintptr_t>(X) % 16 == 0 && (N + 15) / 16 > 3 * (int64_t)num_cus;
 }
 
 hipError_t launch_gemm_kw(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,
-                          int64_t B, int64_t K, int64_t N, int32_t group, int num_cus, hipStream_t stream) {
-    if (!kw_supports(B, K, N, group, 4) || reinterpret_cast<uintptr_t>(X) % 16 != 0) return hipErrorInvalidValue;
+                          int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset, int num_cus,
+                          hipStream_t stream) {
+    if (!kw_supports(B, K, N, group, bits, offset) || reinterpret_cast<uintptr_t>(X) % 16 != 0)
+        return hipErrorInvalidValue;
     KwArgs a;
     a.X = static_cast<const uint16_t*>(X);
     a.codes = static_cast<const uint8_t*>(codes);
@@ -461,9 +571,20 @@ hipError_t launch_gemm_kw(const void* X, const void* codes, const void* scales, 
     a.ngrp = (int32_t)(K / 128);
     a.cpr = a.ngrp / 8;
     const int tpb = kw_tiles_per_block(N, num_cus);
-    if (B <= 16) return launch_ncb<1>(a, tpb, stream);
-    if (B <= 32) return launch_ncb<2>(a, tpb, stream);
-    return launch_ncb<4>(a, tpb, stream);
+    if (offset) {
+        if (bits == 2) return launch_exact<2, KW_OFFSET>(a, tpb, stream);
+        if (bits == 3) return launch_exact<3, KW_OFFSET>(a, tpb, stream);
+        return launch_exact<4, KW_OFFSET>(a, tpb, stream);
+    }
+    if (bits == 2) return launch_exact<2, KW_ZERO>(a, tpb, stream);
+    if (bits == 3) return launch_exact<3, KW_ZERO>(a, tpb, stream);
+    // 4-bit codes with integer zero points: exact-integer operands at one
+    // batch block, where the fp16 dequantization of every weight feeds a
+    // single product; from two batch blocks on, the per-round correction of
+    // every block costs more than the dequantization it saves.
+    if (B <= 16) return launch_ncb<1, 4, KW_ZERO>(a, tpb, stream);
+    if (B <= 32) return launch_ncb<2, 4, KW_DEQUANT>(a, tpb, stream);
+    return launch_ncb<4, 4, KW_DEQUANT>(a, tpb, stream);
 }
 
 }  // namespace wq

@@ -95,15 +95,20 @@ bool mfma_path_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bit
                      const void* zeros);
 bool ts_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* scales,
               const void* zeros);
-// K-split-wave matrix-core kernel for B <= 64 (wq_gemm_kw.hip): needs no
-// scratch; group 128, K = 2048, 4096 or 8192, X 16-byte aligned.  kw_takes
-// adds the shape choice: B > 8 and more than three 16-row tiles per compute
-// unit.
-bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);
-bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, const void* X, int num_cus);
+// K-split-wave matrix-core kernel (wq_gemm_kw.hip): needs no scratch; group
+// 128, K = 2048, 4096 or 8192, X 16-byte aligned.  4-bit codes with integer
+// zero points up to B = 64; 2- and 3-bit codes, and float offsets (offset:
+// `zeros` holds the group minima m, x_hat = q s + m) at bits 2, 3 and 4, up
+// to B = 32.  kw_takes adds the shape choice: more than three 16-row tiles
+// per compute unit, and B > 4 for 4-bit integer-zero codes (where the
+// quad-stream kernel takes B <= 4), B >= 2 otherwise.
+bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset);
+bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset, const void* X,
+              int num_cus);
 int kw_tiles_per_block(int64_t N, int num_cus);
 hipError_t launch_gemm_kw(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,
-                          int64_t B, int64_t K, int64_t N, int32_t group, int num_cus, hipStream_t stream);
+                          int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset, int num_cus,
+                          hipStream_t stream);
 // Tile-stream 16x16x32 matrix-core kernel for B <= 16 (wq_gemm_ts.hip): needs
 // no scratch; group 128, K % 512 == 0, header arrays 8-byte aligned.
 bool ts_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits);

@@ -171,9 +171,12 @@ wq_status wq_quantize_workspace_size(int64_t N, int64_t K, int32_t group, int32_
  * bits 2 and 3 (the bit-stream layout of wq_quantize_pack; "Quantization &
  * inference optimisation", "Quantization", prints their errors next to 4 and
  * 8 bits): group % 32 == 0, K % 64 == 0 (bits 2) or K % 128 == 0 (bits 3),
- * K <= 32768; GEMV path only, at any B (the codes are streamed once per four
- * batch rows, so large batches are correct but not fast); bits 1, 5, 6 and 7
- * are WQ_ERR_UNSUPPORTED.
+ * K <= 32768.  They run on the GEMV path (the codes streamed once per four
+ * batch rows), except that from B = 2 to 32, on matrices of more than three
+ * 16-row tiles per compute unit with group 128 and K = 2048, 4096 or 8192
+ * (and X 16-byte aligned), the MFMA path takes them (exact-integer operands,
+ * header applied per group in fp32); WQ_PATH_MFMA outside those shapes is
+ * WQ_ERR_UNSUPPORTED.  bits 1, 5, 6 and 7 are WQ_ERR_UNSUPPORTED.
  * Results are deterministic: no atomics, fixed reduction order.
  * wq_gemm takes no workspace: it runs plans that need none (the matrix-core
  * kernels without K splits).  wq_gemm_ex with a workspace is faster where
@@ -238,8 +241,11 @@ wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void
  * fp32 accumulation, Y rounded once to fp16.  bits 2, 3, 4 or 8 (others
  * WQ_ERR_UNSUPPORTED); group % 32 == 0; K % 64 (bits 2), % 128 (bits 3) or
  * % 32 (bits 4, 8); K <= 16384 (32768 at bits 3).  Layout and alignment as
- * wq_gemm, `mins` in place of `zeros`.  VALU bit-stream kernel, any B (codes
- * are streamed once per four batch rows).
+ * wq_gemm, `mins` in place of `zeros`.  From B = 2 to 32 at bits 2, 3 or 4,
+ * group 128, K = 2048, 4096 or 8192 and more than three 16-row tiles per
+ * compute unit: a matrix-core kernel (exact-integer operands; per group
+ * s * sum q x + m * sum x in fp32); otherwise the VALU bit-stream kernel, any
+ * B (codes streamed once per four batch rows).
  */
 wq_status wq_gemm_offset(const void* X, const void* codes, const void* scales, const void* mins,
                          void* Y, int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits,
