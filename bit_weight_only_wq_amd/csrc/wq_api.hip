@@ -628,6 +628,10 @@ wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void
     if (!X || !codes || !scales || !Y) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_nf4: null pointer");
     if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(Y, 2))
         return fail(WQ_ERR_MISALIGNED, "wq_gemm_nf4: X and codes need 16-byte alignment");
+    if (wq::kw_nf4_takes(B, K, N, group, X, num_cus()))
+        return check_hip(wq::launch_gemm_kw_nf4(X, codes, scales, Y, B, K, N, group, num_cus(),
+                                                static_cast<hipStream_t>(stream)),
+                         "wq_gemm_nf4 (mfma) launch");
     return check_hip(wq::launch_gemv_nf4(X, codes, scales, Y, B, K, N, group, num_cus(),
                                          static_cast<hipStream_t>(stream)),
                      "wq_gemm_nf4 launch");

@@ -41,6 +41,7 @@
 #include "wq_device.h"
 #include "wq_launch.h"
 #include "wq_mfma_dq.h"
+#include "wq_nf4_levels.h"
 
 namespace wq {
 
@@ -56,8 +57,10 @@ typedef unsigned int kw_v2u __attribute__((ext_vector_type(2)));
 
 // How the weight operand is formed: dequantized in registers to fp16
 // (q - z) * s / 2 (4-bit codes), or exact integers with the header applied
-// per round in fp32, with an integer zero point or a float offset.
-constexpr int KW_DEQUANT = 0, KW_ZERO = 1, KW_OFFSET = 2;
+// per round in fp32, with an integer zero point or a float offset, or (NF4,
+// 4-bit codes, blocks of 64) looked up as fp16 level pairs and scaled in fp16.
+constexpr int KW_DEQUANT = 0, KW_ZERO = 1, KW_OFFSET = 2, KW_NF4 = 3;
+constexpr int kKwLutCopies = 32;   // NF4 table copies (one per LDS bank of a 32-lane cycle)
 
 struct KwArgs {
     const uint16_t* X;
@@ -101,8 +104,9 @@ template <int NCB, int TPB, int DX, int W, int BITS, int MODE>
 __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     static_assert(DX == 2 || DX == 4, "an X ring of 2 or 4 rounds");
     static_assert(BITS == 2 || BITS == 3 || BITS == 4, "2-, 3- or 4-bit codes");
-    static_assert(MODE != KW_DEQUANT || BITS == 4, "fp16 dequantization takes 4-bit codes");
-    constexpr bool EXACT = MODE != KW_DEQUANT;
+    static_assert((MODE != KW_DEQUANT && MODE != KW_NF4) || BITS == 4, "fp16 operands take 4-bit codes");
+    constexpr bool EXACT = MODE == KW_ZERO || MODE == KW_OFFSET;
+    constexpr bool NF4 = MODE == KW_NF4;
     constexpr int XR = NCB * 16 * 16;   // 16-byte X chunks per round
     // The rounds of the ring are separate objects, so that the compiler can
     // tell the LDS-DMA writes of one from those of another and waits only for
@@ -115,9 +119,14 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     // row: row r's 16-byte chunk p (8 groups) at position r * cpr +
     // (p ^ (r & (cpr - 1))), so that 16 rows read at one group hit distinct
     // banks.
-    constexpr int HCH = TPB * 16 * 8;
+    // NF4 has no zero points and blocks of 64: up to 128 scales (16 chunks)
+    // per row in hs, in the space the zero points take otherwise.
+    constexpr int HCH = TPB * 16 * (NF4 ? 16 : 8);
     __shared__ __align__(16) uint4 hs[HCH];
-    __shared__ __align__(16) uint4 hz[HCH];
+    __shared__ __align__(16) uint4 hz[NF4 ? 1 : HCH];
+    // NF4: code byte b -> fp16 pair (level[b & 15], level[b >> 4]), entry b of
+    // copy c at word b * 32 + c; lane l reads copy l % 32.
+    __shared__ uint32_t lut[NF4 ? 256 * kKwLutCopies : 1];
     constexpr int NXL = NCB * 4;        // LDS-DMA loads per round (4 rows each)
     constexpr int NSL = 2 * TPB;        // code loads per two-round step
     constexpr int WAIT_EVEN = kw_vmcnt(kw_inflight(DX, NXL, NSL, 100));
@@ -126,6 +135,14 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, g4 = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if constexpr (NF4) {
+        for (int e = (int)threadIdx.x; e < 256 * kKwLutCopies; e += 64 * W) {
+            const int b = e / kKwLutCopies;
+            lut[e] = (uint32_t)kNf4LevelBits[b & 15] | ((uint32_t)kNf4LevelBits[b >> 4] << 16);
+        }
+        __syncthreads();
+    }
+    const uint32_t* const lutl = lut + (NF4 ? (lane & (kKwLutCopies - 1)) : 0);
     uint4* const xw[4] = {xs0 + w * XR, xs1 + w * XR, xs2 + (DX > 2 ? w * XR : 0),
                           xs3 + (DX > 2 ? w * XR : 0)};   // this wave's rounds (slot = round % DX)
 
@@ -252,6 +269,37 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
 
     // One round: half h of a step's codes and headers, X from LDS slot xr.
     auto compute = [&](const Step& st, const uint32_t* hsv, const uint32_t* hzv, int h, const uint4* xr) {
+        if constexpr (NF4) {
+            // Lane g4's 32 codes of the round lie in block 2 (round) + g4 / 2 of
+            // 64; hsv[t] holds the two blocks of round h (low: g4 < 2).  Each
+            // code byte is the pair (k even, k odd), so X is read in its
+            // natural order; the operand is level * s, rounded once to fp16.
+            const uint32_t selg = g4 >= 2 ? 0x07060706u : 0x05040504u;
+            h2_t ss[TPB];
+#pragma unroll
+            for (int t = 0; t < TPB; ++t) ss[t] = as_h2(__builtin_amdgcn_perm(hsv[t], hsv[t], selg));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h8_t xo[NCB];
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    xo[cb] = __builtin_bit_cast(h8_t, xr[(cb * 16 + r16) * 16 + ((4 * g4 + j) ^ r16)]);
+#pragma unroll
+                for (int t = 0; t < TPB; ++t) {
+                    const uint32_t wv = st.c[t][h][j];
+                    uint32_t pr[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pr[i] = lutl[((wv >> (8 * i)) & 0xFFu) * kKwLutCopies];
+                    const uint4 u = {as_u32(as_h2(pr[0]) * ss[t]), as_u32(as_h2(pr[1]) * ss[t]),
+                                     as_u32(as_h2(pr[2]) * ss[t]), as_u32(as_h2(pr[3]) * ss[t])};
+                    const h8_t bop = __builtin_bit_cast(h8_t, u);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        acc[t][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xo[cb], bop, acc[t][cb], 0, 0, 0);
+                }
+            }
+            return;
+        }
         if constexpr (EXACT) {
             // The codes enter as exact integers E + q (E per operand slot); two
             // more products per k-step give C1 = sum E_k x_k and C2 = sum x_k
@@ -391,12 +439,21 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
         asm volatile("" ::: "memory");
         // The step's two groups (2 dg, 2 dg + 1) share one 8-group chunk.
         const int dg = d0 + ((dl + soff) & (a.nd - 1));
-        uint32_t hsv[TPB], hzv[TPB];
+        uint32_t hsv[TPB], hzv[TPB], hs1[TPB];
 #pragma unroll
         for (int t = 0; t < TPB; ++t) {
-            const int at = (hrow[t] + ((dg >> 2) ^ hswz[t])) * 4 + (dg & 3);
-            hsv[t] = reinterpret_cast<const uint32_t*>(hs)[at];
-            hzv[t] = reinterpret_cast<const uint32_t*>(hz)[at];
+            if constexpr (NF4) {
+                // Four blocks of 64 per step: dwords 2 (dg & 1) and + 1 of chunk dg / 2.
+                const int at = (hrow[t] + ((dg >> 1) ^ hswz[t])) * 4 + 2 * (dg & 1);
+                hsv[t] = reinterpret_cast<const uint32_t*>(hs)[at];
+                hs1[t] = reinterpret_cast<const uint32_t*>(hs)[at + 1];
+                hzv[t] = 0;
+            } else {
+                const int at = (hrow[t] + ((dg >> 2) ^ hswz[t])) * 4 + (dg & 3);
+                hsv[t] = reinterpret_cast<const uint32_t*>(hs)[at];
+                hzv[t] = reinterpret_cast<const uint32_t*>(hz)[at];
+                hs1[t] = hsv[t];
+            }
         }
         compute(st, hsv, hzv, 0, xw[(2 * pos) % DX]);
         asm volatile("" ::: "memory");
@@ -404,7 +461,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAIT_ODD);
         asm volatile("" ::: "memory");
-        compute(st, hsv, hzv, 1, xw[(2 * pos + 1) % DX]);
+        compute(st, NF4 ? hs1 : hsv, hzv, 1, xw[(2 * pos + 1) % DX]);
         asm volatile("" ::: "memory");
         load_x(r + 1 + DX, (2 * pos + 1) % DX);
         // The wait counts need X of a round issued wholly before the next
@@ -426,7 +483,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
             const int row = flat / a.cpr, p = flat & (a.cpr - 1);
             const uint32_t src = flat < total ? (uint32_t)(row * a.cpr + (p ^ (row & (a.cpr - 1)))) * 16u : kKwFar;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (kw_lds_void*)(hs + i * 64), 16, (int)src, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, (kw_lds_void*)(hz + i * 64), 16, (int)src, 0, 0, 0);
+            if constexpr (!NF4)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, (kw_lds_void*)(hz + i * 64), 16, (int)src, 0, 0, 0);
         }
     }
     Step ring0, ring1;
@@ -488,7 +546,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
         const int t = q / (NCB * 4), cb = (q / 4) % NCB, i = q % 4;
         const int row = tile0 * 16 + t * 16 + (l & 15);
         const int b = cb * 16 + 4 * (l >> 4) + i;
-        if (row < a.N && b < a.B) a.Y[(size_t)b * a.N + row] = float_to_half_bits_rne(EXACT ? v : 2.0f * v);
+        if (row < a.N && b < a.B) a.Y[(size_t)b * a.N + row] = float_to_half_bits_rne(MODE == KW_DEQUANT ? 2.0f * v : v);
     }
 }
 
@@ -499,7 +557,8 @@ hipError_t launch_tpb(KwArgs a, hipStream_t stream) {
     // Four waves (eight would double the row streams each compute unit keeps
     // open, and the code stream slows down); four rounds of X in flight
     // where they fit in LDS (4 * NCB * 16 KB).
-    constexpr int DX = NCB <= 2 ? 4 : 2;
+    // (NF4 keeps a 32 KB level table: two rounds of X past one batch block.)
+    constexpr int DX = NCB == 1 || (NCB == 2 && MODE != KW_NF4) ? 4 : 2;
     a.nd = a.K / (256 * 4);
     gemm_kw_kernel<NCB, TPB, DX, 4, BITS, MODE><<<grid, dim3(256), 0, stream>>>(a);
     return hipGetLastError();
@@ -552,6 +611,29 @@ bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool
     const bool int4 = bits == 4 && !offset;
     return B > (int4 ? 4 : 1) && kw_supports(B, K, N, group, bits, offset) &&
            reinterpret_cast<uintptr_t>(X) % 16 == 0 && (N + 15) / 16 > 3 * (int64_t)num_cus;
+}
+
+// NF4 (blocks of 64, 4-bit codes indexing the level table): 2 <= B <= 32.
+bool kw_nf4_takes(int64_t B, int64_t K, int64_t N, int32_t group, const void* X, int num_cus) {
+    return B >= 2 && B <= 32 && group == 64 && (K == 2048 || K == 4096 || K == 8192) && N >= 16 &&
+           N <= (1 << 24) && reinterpret_cast<uintptr_t>(X) % 16 == 0 && (N + 15) / 16 > 3 * (int64_t)num_cus;
+}
+
+hipError_t launch_gemm_kw_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B, int64_t K,
+                              int64_t N, int32_t group, int num_cus, hipStream_t stream) {
+    if (!kw_nf4_takes(B, K, N, group, X, num_cus)) return hipErrorInvalidValue;
+    KwArgs a;
+    a.X = static_cast<const uint16_t*>(X);
+    a.codes = static_cast<const uint8_t*>(codes);
+    a.scales = static_cast<const uint16_t*>(scales);
+    a.zeros = static_cast<const uint16_t*>(scales);   // unused
+    a.Y = static_cast<uint16_t*>(Y);
+    a.B = (int32_t)B;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.ngrp = (int32_t)(K / 64);
+    a.cpr = a.ngrp / 8;
+    return launch_exact<4, KW_NF4>(a, kw_tiles_per_block(N, num_cus), stream);
 }
 
 hipError_t launch_gemm_kw(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,

@@ -106,6 +106,11 @@ bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, b
 bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset, const void* X,
               int num_cus);
 int kw_tiles_per_block(int64_t N, int num_cus);
+// NF4 codes (wq_gemm_nf4) on the same kernel: blocks of 64 only, 2 <= B <= 32,
+// K = 2048, 4096 or 8192, more than three 16-row tiles per compute unit.
+bool kw_nf4_takes(int64_t B, int64_t K, int64_t N, int32_t group, const void* X, int num_cus);
+hipError_t launch_gemm_kw_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B, int64_t K,
+                              int64_t N, int32_t group, int num_cus, hipStream_t stream);
 hipError_t launch_gemm_kw(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,
                           int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset, int num_cus,
                           hipStream_t stream);

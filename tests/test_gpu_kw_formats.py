@@ -1,12 +1,13 @@
-"""GPU parity of 2- and 3-bit codes, and of the float-offset variant at 2, 3
-and 4 bits, on the K-split-wave matrix-core kernel (2 <= B <= 32, group 128,
+"""GPU parity of 2- and 3-bit codes, of the float-offset variant at 2, 3 and
+4 bits, and of NF4 codes (blocks of 64) on the K-split-wave matrix-core kernel (2 <= B <= 32, group 128,
 K = 2048, 4096 or 8192, more than three 16-row tiles per compute unit;
 wq_gemm_kw.hip) against the CPU oracle.
 
 The codes are unpacked as exact fp16 integers E + q, each operand slot with
 its own exponent E (2 bits: 1024, 256, 64, 16; 3 bits: 1024, 128, 16, 1024),
 E is subtracted exactly in fp16, and the group header is applied once per
-128-k round in fp32
+128-k round in fp32; NF4 codes become fp16 level pairs through an LDS table
+and are scaled in fp16 (level * s, rounded once)
 ("Quantization & inference optimisation", section "Quantization": the integer
 and the group's endpoints give back the weight; its error table covers 8, 4,
 3 and 2 bits).  What the shapes exercise:
@@ -25,6 +26,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.nf4 as onf4
 import wq_inputs
 from gpu_util import assert_close, device, note, to_dev
 
@@ -135,3 +137,47 @@ def test_float_offset_on_the_70b_matrix_sampled_rows(bits):
                                      np.random.default_rng(9).choice(N, 512, replace=False)]))
     cn, sn, mn = (t.cpu().numpy()[rows] for t in (c, s, m))
     assert_close(Y[:, rows], oracle.gemm_offset(Xb, cn, sn, mn, K, 128, bits), f"offset {name} b={bits}")
+
+
+@pytest.mark.parametrize("N,K,batches", [(12305, 2048, (2, 16, 17, 32)), (16400, 4096, (3, 16)),
+                                         (12400, 8192, (9,))])
+def test_nf4_all_outputs(N, K, batches):
+    """NF4 ("Gör inference billig", the NF4 paragraph): sixteen normal-quantile
+    levels, one absolute-maximum scale per block of 64."""
+    device()
+    W, X = _draw(N, K, max(batches), 5 * N + K)
+    W[3, 7] = 0.6   # one outlier block
+    c, s = onf4.quantize(W, 64)
+    dc, ds = to_dev(c), to_dev(s)
+    for B in batches:
+        note(f"kw formats nf4 N={N} K={K} B={B}")
+        Y = wq.gemm_nf4(to_dev(X[:B]), dc, ds, N=N, K=K, group=64)
+        assert_close(Y, onf4.gemm(X[:B], c, s, K, 64), f"nf4 N={N} K={K} B={B}")
+
+
+def test_nf4_routing_edges():
+    """B = 1, B = 33 and blocks of 128 run on the NF4 GEMV; all match the oracle."""
+    device()
+    N, K = 12305, 2048
+    W, X = _draw(N, K, 33, 71)
+    for B, G in ((1, 64), (33, 64), (16, 128)):
+        c, s = onf4.quantize(W, G)
+        note(f"kw formats nf4 routing B={B} G={G}")
+        Y = wq.gemm_nf4(to_dev(X[:B]), to_dev(c), to_dev(s), N=N, K=K, group=G)
+        assert_close(Y, onf4.gemm(X[:B], c, s, K, G), f"nf4 B={B} G={G}")
+
+
+def test_nf4_on_the_70b_matrix_sampled_rows():
+    """The 70B-class up-projection at B = 16, quantized on the GPU: rows
+    sampled across the whole matrix."""
+    device()
+    name = "mlp70b_up_k8192_n28672_g128"
+    W, X = wq_inputs.workload_arrays(name)
+    N, K = W.shape
+    Xb = np.random.default_rng(10).standard_normal((16, K)).astype(np.float16)
+    c, s, _ = wq.quantize_pack(to_dev(W), 64, 4, scheme="nf4")
+    note(f"kw formats nf4 {name}")
+    Y = wq.gemm_nf4(to_dev(Xb), c, s, N=N, K=K, group=64).cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, 256), np.arange(N - 256, N),
+                                     np.random.default_rng(11).choice(N, 512, replace=False)]))
+    assert_close(Y[:, rows], onf4.gemm(Xb, c.cpu().numpy()[rows], s.cpu().numpy()[rows], K, 64), f"nf4 {name}")
