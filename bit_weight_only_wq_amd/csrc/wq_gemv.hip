@@ -407,9 +407,11 @@ __global__ __launch_bounds__(256) void gemv_row_kernel(
     // then read zeros without touching memory.  Narrower groups (several rows
     // per wave) reread the last row instead.
     auto load_pass = [&](int pass, uint4* w, uint32_t* hw) {
-        int n = pass * RPB + rs;
-        const bool live = n < Nr;
-        n = live ? n : Nr - 1;
+        // The prefetched pass may lie up to a grid's worth past the last one:
+        // its row is formed in 64 bits (no overflow for N near 2^31).
+        const int64_t n64 = (int64_t)pass * RPB + rs;
+        const bool live = n64 < (int64_t)Nr;
+        const int n = live ? (int)n64 : Nr - 1;
         if constexpr (TG == 64) {
             const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint4*>(codes + (int64_t)n * C), (short)0, live ? C * 16 : 0, kBufferWord3);
