@@ -338,13 +338,29 @@ __global__ __launch_bounds__(128) void kv_combine_kernel(const float* __restrict
 // ---- quantize-on-append ------------------------------------------------------
 // Eight workgroups per head (K by channel quarters, V by token quarters): the
 // head's block of G tokens of K and V (fp16, token-major [G][D]) becomes
-// block `block` of its cache.  K: min/max per
-// channel over the G tokens; V: per token over the D channels; both with the
-// exact decisions of the weight quantizer.
-__device__ __forceinline__ uint32_t encode_one(float x, float s, float rcp, float Z) {
-    const float k = rne_div_exact(x, s, rcp, -Z - 2.0f, 17.0f - Z);
-    const float q = __builtin_amdgcn_fmed3f(k + Z, 0.0f, 15.0f);
-    return (uint32_t)q;
+// block `block` of its cache.  K: min/max per channel over the G tokens; V:
+// per token over the D channels; both with the exact decisions of the weight
+// quantizer.
+//
+// A workgroup owns Q = 32 groups of 128 elements (K: channels 32q .. 32q + 31
+// over the tokens; V: tokens 32q .. 32q + 31 over the channels).  Thread
+// (p, e) = (tid % 16, tid / 16) holds groups 2p and 2p + 1 at elements
+// 8e .. 8e + 7 in registers, so its two group headers are two values in
+// registers rather than one LDS read per code: min/max over the element
+// blocks (lanes 16 and 32 apart, then the 4 waves through LDS), the headers
+// from 32 lanes, then the fp32 estimate of every code with the exact
+// fallback of the weight quantizer when a lane of the wave needs it.  Code
+// byte (2p, 2p + 1) of element row r goes into an LDS tile of the
+// workgroup's 128 rows x 16 bytes, from which each thread writes 8 bytes of
+// one row.
+__device__ __forceinline__ float kv_encode_exact(float x, float s, float rcp, float Z) {
+    const float t = __builtin_amdgcn_fmed3f(x * rcp, -Z - 2.0f, 15.0f - Z + 2.0f);
+    const float kl = __builtin_floorf(t);
+    const float r = __builtin_fmaf(-(kl + 0.5f), s, x);
+    const float half = kl * 0.5f;
+    const bool odd = __builtin_rintf(half) != half;
+    const bool inc = (r > 0.0f) | ((r == 0.0f) & odd);   // no short-circuit branches
+    return inc ? kl + 1.0f : kl;
 }
 
 __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __restrict__ K,
@@ -353,128 +369,116 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
                                                           uint16_t* __restrict__ kz, uint8_t* __restrict__ vc,
                                                           uint16_t* __restrict__ vs, uint16_t* __restrict__ vz,
                                                           int64_t max_blocks, int64_t block) {
-    // blockIdx.y = 4 * side + q.  Side 0 (K) takes channels [32q, 32q + 32)
-    // over all G tokens; side 1 (V) takes tokens [32q, 32q + 32) over all D
-    // channels.  Each group then lies inside one workgroup, which writes a
-    // 16-byte column of every code row it touches.
-    constexpr int Q = 32;                        // channels (K) or tokens (V) per workgroup
-    __shared__ uint16_t tile[kG * (Q + 2)];      // K: [G][Q + 2]; V: [Q][D + 2] (same size)
-    __shared__ float hs[Q], hr[Q], hzf[Q];
-    __shared__ float mnx[8][2][Q];
+    constexpr int Q = 32;                       // groups per workgroup
+    __shared__ float mnx[4][2][Q];              // per-wave partial min / max
+    __shared__ float4 hdr[Q];                   // s, rcp, Z, thr
+    __shared__ __align__(8) uint8_t ctile[kG * (Q / 2)];   // [128 rows][16 bytes]
 
     const int h = blockIdx.x;
     const int side = blockIdx.y >> 2, q = blockIdx.y & 3;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int p = tid & 15, e = tid >> 4;
     const int64_t blk = (int64_t)h * max_blocks + block;
 
+    // x[g][i]: group 2p + g at element 8e + i.
+    float x[2][8];
     if (side == 0) {
-        // ---- K: one group per channel; this workgroup's 32 channels.
-        constexpr int PAD = Q + 2;
-        const uint16_t* src = K + (int64_t)h * kG * kD + Q * q;
-        for (int i = tid; i < kG * (Q / 8); i += 256) {
-            const int t = i / (Q / 8), c = i % (Q / 8);
-            const uint4 u = reinterpret_cast<const uint4*>(src + (int64_t)t * kD)[c];
-            uint32_t* dst = reinterpret_cast<uint32_t*>(tile + t * PAD + 8 * c);
-            dst[0] = u.x;
-            dst[1] = u.y;
-            dst[2] = u.z;
-            dst[3] = u.w;
-        }
-        __syncthreads();
-        {
-            const int c = tid & (Q - 1), part = tid >> 5;     // 8 parts of 16 tokens
-            float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-            for (int t = part * 16; t < part * 16 + 16; ++t) {
-                const float x = half_bits_to_float(tile[t * PAD + c]);
-                mn = __builtin_fminf(mn, x);
-                mx = __builtin_fmaxf(mx, x);
-            }
-            mnx[part][0][c] = mn;
-            mnx[part][1][c] = mx;
-        }
-        __syncthreads();
-        if (tid < Q) {
-            float mn = mnx[0][0][tid], mx = mnx[0][1][tid];
+        // K [G][D]: channels 32q + 2p, + 1 of tokens 8e .. 8e + 7 (one dword each).
+        const uint16_t* src = K + ((int64_t)h * kG + 8 * e) * kD + Q * q + 2 * p;
 #pragma unroll
-            for (int p2 = 1; p2 < 8; ++p2) {
-                mn = __builtin_fminf(mn, mnx[p2][0][tid]);
-                mx = __builtin_fmaxf(mx, mnx[p2][1][tid]);
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t u = *reinterpret_cast<const uint32_t*>(src + (int64_t)i * kD);
+            x[0][i] = half_bits_to_float((uint16_t)u);
+            x[1][i] = half_bits_to_float((uint16_t)(u >> 16));
+        }
+    } else {
+        // V [G][D]: channels 8e .. 8e + 7 of tokens 32q + 2p, + 1 (16 bytes each).
+        const uint16_t* src = V + ((int64_t)h * kG + Q * q + 2 * p) * kD + 8 * e;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const uint4 u = *reinterpret_cast<const uint4*>(src + (int64_t)g * kD);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[g][2 * j] = half_bits_to_float((uint16_t)w[j]);
+                x[g][2 * j + 1] = half_bits_to_float((uint16_t)(w[j] >> 16));
             }
-            const GroupHeader g = make_header(mn, mx, 15);
-            hs[tid] = g.s;
-            hr[tid] = g.rcp;
-            hzf[tid] = g.Z;
+        }
+    }
+    float mn[2], mx[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        mn[g] = x[g][0];
+        mx[g] = x[g][0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+            mn[g] = __builtin_fminf(mn[g], x[g][i]);
+            mx[g] = __builtin_fmaxf(mx[g], x[g][i]);
+        }
+#pragma unroll
+        for (int o = 16; o < 64; o <<= 1) {   // the wave's 4 element blocks
+            mn[g] = __builtin_fminf(mn[g], __shfl_xor(mn[g], o, 64));
+            mx[g] = __builtin_fmaxf(mx[g], __shfl_xor(mx[g], o, 64));
+        }
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            mnx[wv][0][2 * p + g] = mn[g];
+            mnx[wv][1][2 * p + g] = mx[g];
+        }
+    }
+    __syncthreads();
+    if (tid < Q) {
+        float a = mnx[0][0][tid], b = mnx[0][1][tid];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) {
+            a = __builtin_fminf(a, mnx[ww][0][tid]);
+            b = __builtin_fmaxf(b, mnx[ww][1][tid]);
+        }
+        const GroupHeader g = make_header(a, b, 15);
+        hdr[tid] = make_float4(g.s, g.rcp, g.Z, g.thr);
+        if (side == 0) {
             ks[blk * kD + Q * q + tid] = g.sbits;
             kz[blk * kD + Q * q + tid] = g.zbits;
-        }
-        __syncthreads();
-        // Token t = tid / 2, channels [16 * (tid & 1), +16) of the quarter -> 8 bytes of its row.
-        const int t = tid >> 1, c0 = (tid & 1) * 16;
-        uint32_t w[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const int c = c0 + 8 * i + n;
-                v |= encode_one(half_bits_to_float(tile[t * PAD + c]), hs[c], hr[c], hzf[c]) << (4 * n);
-            }
-            w[i] = v;
-        }
-        *reinterpret_cast<uint2*>(kc + (blk * kG + t) * kRow + (Q / 2) * q + c0 / 2) = make_uint2(w[0], w[1]);
-        return;
-    }
-
-    // ---- V: one group per token; this workgroup's 32 tokens.
-    constexpr int PAD = kD + 2;
-    const uint16_t* src = V + ((int64_t)h * kG + Q * q) * kD;
-    for (int i = tid; i < Q * (kD / 8); i += 256) {
-        const int t = i / (kD / 8), c = i % (kD / 8);
-        const uint4 u = reinterpret_cast<const uint4*>(src + (int64_t)t * kD)[c];
-        uint32_t* dst = reinterpret_cast<uint32_t*>(tile + t * PAD + 8 * c);
-        dst[0] = u.x;
-        dst[1] = u.y;
-        dst[2] = u.z;
-        dst[3] = u.w;
-    }
-    __syncthreads();
-    {
-        const int t = tid >> 3, part = tid & 7;              // 8 lanes of 16 channels per token
-        float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-        for (int d = part * 16; d < part * 16 + 16; ++d) {
-            const float x = half_bits_to_float(tile[t * PAD + d]);
-            mn = __builtin_fminf(mn, x);
-            mx = __builtin_fmaxf(mx, x);
-        }
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-            mn = __builtin_fminf(mn, __shfl_xor(mn, o, 64));
-            mx = __builtin_fmaxf(mx, __shfl_xor(mx, o, 64));
-        }
-        if (part == 0) {
-            const GroupHeader g = make_header(mn, mx, 15);
-            hs[t] = g.s;
-            hr[t] = g.rcp;
-            hzf[t] = g.Z;
-            vs[blk * kG + Q * q + t] = g.sbits;
-            vz[blk * kG + Q * q + t] = g.zbits;
+        } else {
+            vs[blk * kG + Q * q + tid] = g.sbits;
+            vz[blk * kG + Q * q + tid] = g.zbits;
         }
     }
     __syncthreads();
-    // Channel d = tid / 2, tokens [16 * (tid & 1), +16) of the quarter -> 8 bytes of its row.
-    const int d = tid >> 1, t0 = (tid & 1) * 16;
-    uint32_t w[2];
+    const float4 h0 = hdr[2 * p], h1 = hdr[2 * p + 1];
+    const float hs_[2] = {h0.x, h1.x}, hr_[2] = {h0.y, h1.y}, hz_[2] = {h0.z, h1.z}, ht_[2] = {h0.w, h1.w};
+    float k[2][8];
+    bool near = false;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        uint32_t v = 0;
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            const int t = t0 + 8 * i + n;
-            v |= encode_one(half_bits_to_float(tile[t * PAD + d]), hs[t], hr[t], hzf[t]) << (4 * n);
+        for (int i = 0; i < 8; ++i) {
+            const float t = x[g][i] * hr_[g];
+            k[g][i] = __builtin_rintf(t);
+            near |= __builtin_fabsf(t - k[g][i]) > ht_[g];
         }
-        w[i] = v;
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) k[g][i] = kv_encode_exact(x[g][i], hs_[g], hr_[g], hz_[g]);
     }
-    *reinterpret_cast<uint2*>(vc + (blk * kD + d) * kRow + (Q / 2) * q + t0 / 2) = make_uint2(w[0], w[1]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t q0 = (uint32_t)__builtin_amdgcn_fmed3f(k[0][i] + hz_[0], 0.0f, 15.0f);
+        const uint32_t q1 = (uint32_t)__builtin_amdgcn_fmed3f(k[1][i] + hz_[1], 0.0f, 15.0f);
+        ctile[(8 * e + i) * (Q / 2) + p] = (uint8_t)(q0 | (q1 << 4));
+    }
+    __syncthreads();
+    // Row r = tid / 2 (K: token, V: channel), bytes [8 (tid & 1), + 8) of the
+    // quarter's 16.
+    const int r = tid >> 1, hb = tid & 1;
+    const uint2 w = *reinterpret_cast<const uint2*>(ctile + r * (Q / 2) + 8 * hb);
+    uint8_t* dst = side == 0 ? kc + (blk * kG + r) * kRow : vc + (blk * kD + r) * kRow;
+    *reinterpret_cast<uint2*>(dst + (Q / 2) * q + 8 * hb) = w;
 }
 
 }  // namespace

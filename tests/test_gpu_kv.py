@@ -90,6 +90,38 @@ def test_quantize_block_bit_exact():
     assert not cache.kcodes[:, 1].any() and not cache.vcodes[:, 1].any()
 
 
+def test_quantize_block_bit_exact_many_heads():
+    """256 heads at the benchmark's distribution (N(0, 1), one hot K channel),
+    written into block 3 of 5: every code and header bit for bit, and the
+    other blocks untouched.  Each head's 16 384 values go through the fp32
+    quotient estimate, and the waves with a value near a half-integer through
+    the exact decision."""
+    device()
+    H, nb, j = 256, 5, 3
+    rng = np.random.default_rng(17)
+    Kb = np.empty((H, G, D), np.float16)
+    Vb = np.empty((H, G, D), np.float16)
+    for h in range(H):
+        Kb[h], Vb[h] = draw_kv(rng, G)
+    note("kv quantize block: 256 heads, block 3")
+    cache = wq.KVCache(H, nb)
+    wq.kv_quantize_block(to_dev(Kb), to_dev(Vb), cache, j)
+    torch.cuda.synchronize()
+    kc, vc = cache.kcodes[:, j].cpu().numpy(), cache.vcodes[:, j].cpu().numpy()
+    ks, kz = _u16(cache.kscales[:, j]), _u16(cache.kzeros[:, j])
+    vs, vz = _u16(cache.vscales[:, j * G:(j + 1) * G]), _u16(cache.vzeros[:, j * G:(j + 1) * G])
+    for h in range(H):
+        blk = okv.quantize_block(Kb[h], Vb[h])
+        assert np.array_equal(kc[h], blk["kcodes"]), h
+        assert np.array_equal(ks[h], blk["ks"].view(np.uint16)), h
+        assert np.array_equal(kz[h], blk["kz"].view(np.uint16)), h
+        assert np.array_equal(vc[h], blk["vcodes"]), h
+        assert np.array_equal(vs[h], blk["vs"].view(np.uint16)), h
+        assert np.array_equal(vz[h], blk["vz"].view(np.uint16)), h
+    others = [b for b in range(nb) if b != j]
+    assert not cache.kcodes[:, others].any() and not cache.vcodes[:, others].any()
+
+
 @pytest.mark.parametrize("use_ws", [True, False])
 @pytest.mark.parametrize("max_blocks", [32, 1])
 def test_attention_ragged_lengths(max_blocks, use_ws):
