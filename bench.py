@@ -108,7 +108,7 @@ KERNEL_SOURCES = {
     "q4": ["wq_gemm_q4.hip", "wq_device.h"],
     "ts": ["wq_gemm_ts.hip", "wq_device.h"],
     "sk": ["wq_gemm_sk.hip", "wq_device.h"],
-    "kw": ["wq_gemm_kw.hip", "wq_mfma_dq.h", "wq_device.h"],
+    "kw": ["wq_gemm_kw.hip", "wq_mfma_dq.h", "wq_nf4_levels.h", "wq_device.h"],
     "quantize": ["wq_quantize.hip", "wq_device.h"],
     "kv_attn": ["wq_kv.hip", "wq_device.h"],
     "kv_quantize": ["wq_kv.hip", "wq_device.h"],
@@ -803,7 +803,7 @@ def run_format(args):
     kernels[f"wq_quantize_pack_{fmt}"] = {"avg_us": round(ms_q * 1e3, 2), "bytes": qb,
                                           "achieved_GBps": round(qb / (ms_q * 1e-3) / 1e9, 1)}
     head = kernels[f"wq_gemm_{fmt}_B{batches[0]}"]
-    row = {"metric": f"{fmt} decode GEMV, achieved HBM GB/s", "value": head["achieved_GBps"], "unit": "GB/s",
+    row = {"metric": f"{fmt} decode product, achieved HBM GB/s", "value": head["achieved_GBps"], "unit": "GB/s",
            "n_gpus": 1, "steps": args.steps, "ms_per_step": round(head["avg_us"] / 1e3, 5),
            "higher_is_better": True, "dtype": "f16", "data": "synthetic",
            "config": {"workload": args.workload, "N": N, "K": K, "group": G, "bits": bits, "format": fmt,
