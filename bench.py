@@ -155,6 +155,32 @@ def read_traffic(kernel_tag):
         return None
 
 
+def read_mfma_counters(workload, path=None):
+    """Per batch size, the matrix-core busy share of the product kernel from a
+    committed rocprofv3 counter summary, if it was taken on the current
+    sources of those kernels (else {})."""
+    import re
+    path = path or os.path.join(ROOT, "profiles", f"mfma_counters_wq_gemm_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    files, sha, cur, out = [], None, None, {}
+    for line in open(path):
+        if line.startswith("sources:"):
+            files = line.split(":", 1)[1].split()
+        elif line.startswith("sources_sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        elif line.startswith("["):
+            m = re.search(r"B = ([0-9, ]+), grid", line)
+            cur = [int(v) for v in m.group(1).split(",")] if m else None
+        elif "mfma_busy_frac:" in line and cur:
+            frac = float(line.rsplit("mfma_busy_frac:", 1)[1].split()[0])
+            for B in cur:
+                out[B] = frac
+    if not files or sha != sources_sha256(files):
+        return {}
+    return out
+
+
 def traffic_from(fetch_csv, write_csv, copy_mib):
     """Per-launch HBM bytes of each wq kernel from two rocprofv3 --pmc CSVs.
 
@@ -427,6 +453,10 @@ def run_step_bench(args):
         for e in kernels.values():
             e["frac_measured_read_ceiling"] = round(e["achieved_GBps"] / ceiling["GBps"], 4)
 
+    busy = read_mfma_counters(args.workload) if bits == cfg["bits"] else {}
+    for B in batches:
+        if B in busy:
+            kernels[f"wq_gemm_B{B}"]["mfma_busy_frac"] = busy[B]
     # The dominant product (longest launch) carries the roofline object.
     Bd = max(batches, key=lambda B: per[B])
     head = kernels[f"wq_gemm_B{Bd}"]
@@ -435,6 +465,8 @@ def run_step_bench(args):
             "peak": rl.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
             "frac": round(head["achieved_GBps"] * 1e9 / rl.MI355X_HBM_BYTES_PER_S, 4),
             "traffic": traffic, "avg_us": head["avg_us"], "bytes_per_launch": head["bytes"]}
+    if Bd in busy:
+        roof["mfma_busy_frac"] = busy[Bd]
     if ceiling:
         roof["measured_read_ceiling_GBps"] = ceiling["GBps"]
         roof["frac_measured_read_ceiling"] = round(head["achieved_GBps"] / ceiling["GBps"], 4)

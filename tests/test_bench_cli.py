@@ -37,3 +37,35 @@ def test_gemm_bytes_match_the_layout():
     for B in (1, 16, 64):
         expect = N * K // 2 + 4 * N * (K // G) + 2 * B * K + 2 * B * N
         assert rl.gemm_bytes(B, N, K, G, 4) == expect
+
+
+def _bench_module():
+    sys.path.insert(0, ROOT)
+    import bench
+    return bench
+
+
+def test_committed_counter_and_traffic_summaries_match_the_sources():
+    """The profiles the bench line reads (per-launch HBM traffic, matrix-core
+    busy share per batch size) were taken on the kernel sources as they are:
+    their recorded source hashes match, so the bench reports them instead of
+    null."""
+    bench = _bench_module()
+    w = "mlp70b_up_k8192_n28672_g128"
+    for B in (1, 16, 64):
+        assert bench.read_traffic(f"wq_gemm_b{B}_{w}") is not None, B
+    busy = bench.read_mfma_counters(w)
+    assert sorted(busy) == [1, 2, 4, 8, 16, 32, 64]
+    assert busy[1] == 0.0 and all(0.0 < busy[B] < 1.0 for B in (2, 4, 8, 16, 32, 64))
+
+
+def test_counter_summary_with_other_sources_is_ignored(tmp_path):
+    """A counter summary whose source hash does not match is not used."""
+    bench = _bench_module()
+    text = open(os.path.join(ROOT, "profiles", "mfma_counters_wq_gemm_mlp70b_up_k8192_n28672_g128.txt")).read()
+    lines = [("sources_sha256: " + "0" * 64) if l.startswith("sources_sha256:") else l for l in text.splitlines()]
+    p = tmp_path / "mfma_counters.txt"
+    p.write_text("\n".join(lines))
+    assert bench.read_mfma_counters("x", path=str(p)) == {}
+    p.write_text(text)
+    assert bench.read_mfma_counters("x", path=str(p))[64] > 0.0
