@@ -100,7 +100,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kw_rsrc(const void* base, uint
 // DX: rounds in the X ring (2 or 4): X is issued DX - 1 rounds before use,
 // the codes of a step two rounds before its first round.  W: waves per block
 // (one per SIMD), each taking a W-th of K.
-template <int NCB, int TPB, int DX, int W, int BITS, int MODE>
+template <int NCB, int TPB, int DX, int W, int BITS, int MODE, int NXL = NCB * 4>
 __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     static_assert(DX == 2 || DX == 4, "an X ring of 2 or 4 rounds");
     static_assert(BITS == 2 || BITS == 3 || BITS == 4, "2-, 3- or 4-bit codes");
@@ -127,7 +127,11 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     // NF4: code byte b -> fp16 pair (level[b & 15], level[b >> 4]), entry b of
     // copy c at word b * 32 + c; lane l reads copy l % 32.
     __shared__ uint32_t lut[NF4 ? 256 * kKwLutCopies : 1];
-    constexpr int NXL = NCB * 4;        // LDS-DMA loads per round (4 rows each)
+    // NXL: LDS-DMA loads per round (4 batch rows each).  At B <= 8 only the
+    // first two are issued: rows 8 .. 15 of the slot keep whatever it held,
+    // which only reaches output rows past B (each output row of a product
+    // depends on its own A row), and those are not stored.
+    static_assert(NXL >= 1 && NXL <= NCB * 4, "X loads per round");
     constexpr int NSL = 2 * TPB;        // code loads per two-round step
     constexpr int WAIT_EVEN = kw_vmcnt(kw_inflight(DX, NXL, NSL, 100));
     constexpr int WAIT_ODD = kw_vmcnt(kw_inflight(DX, NXL, NSL, 101));
@@ -550,7 +554,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
     }
 }
 
-template <int NCB, int TPB, int BITS, int MODE>
+template <int NCB, int TPB, int BITS, int MODE, int NXL = NCB * 4>
 hipError_t launch_tpb(KwArgs a, hipStream_t stream) {
     const int ntiles = (a.N + 15) / 16;
     const dim3 grid((unsigned)((ntiles + TPB - 1) / TPB));
@@ -560,18 +564,18 @@ hipError_t launch_tpb(KwArgs a, hipStream_t stream) {
     // (NF4 keeps a 32 KB level table: two rounds of X past one batch block.)
     constexpr int DX = NCB == 1 || (NCB == 2 && MODE != KW_NF4) ? 4 : 2;
     a.nd = a.K / (256 * 4);
-    gemm_kw_kernel<NCB, TPB, DX, 4, BITS, MODE><<<grid, dim3(256), 0, stream>>>(a);
+    gemm_kw_kernel<NCB, TPB, DX, 4, BITS, MODE, NXL><<<grid, dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
-template <int NCB, int BITS, int MODE>
+template <int NCB, int BITS, int MODE, int NXL = NCB * 4>
 hipError_t launch_ncb(const KwArgs& a, int tpb, hipStream_t stream) {
     switch (tpb) {
-        case 4: return launch_tpb<NCB, 4, BITS, MODE>(a, stream);
-        case 5: return launch_tpb<NCB, 5, BITS, MODE>(a, stream);
-        case 6: return launch_tpb<NCB, 6, BITS, MODE>(a, stream);
-        case 7: return launch_tpb<NCB, 7, BITS, MODE>(a, stream);
-        default: return launch_tpb<NCB, 8, BITS, MODE>(a, stream);
+        case 4: return launch_tpb<NCB, 4, BITS, MODE, NXL>(a, stream);
+        case 5: return launch_tpb<NCB, 5, BITS, MODE, NXL>(a, stream);
+        case 6: return launch_tpb<NCB, 6, BITS, MODE, NXL>(a, stream);
+        case 7: return launch_tpb<NCB, 7, BITS, MODE, NXL>(a, stream);
+        default: return launch_tpb<NCB, 8, BITS, MODE, NXL>(a, stream);
     }
 }
 
@@ -664,6 +668,7 @@ hipError_t launch_gemm_kw(const void* X, const void* codes, const void* scales, 
     // batch block, where the fp16 dequantization of every weight feeds a
     // single product; from two batch blocks on, the per-round correction of
     // every block costs more than the dequantization it saves.
+    if (B <= 8) return launch_ncb<1, 4, KW_ZERO, 2>(a, tpb, stream);
     if (B <= 16) return launch_ncb<1, 4, KW_ZERO>(a, tpb, stream);
     if (B <= 32) return launch_ncb<2, 4, KW_DEQUANT>(a, tpb, stream);
     return launch_ncb<4, 4, KW_DEQUANT>(a, tpb, stream);
