@@ -281,7 +281,7 @@ static wq_status check_gemm_shape(int64_t B, int64_t K, int64_t N, int32_t group
         const bool kw = wq::kw_takes(B, K, N, group, bits, false, nullptr, num_cus());
         if (path == WQ_PATH_MFMA && !kw)
             return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: bits=%lld takes the MFMA path only for 2 <= B <= 32, "
-                        "group 128, K = 2048, 4096 or 8192 and more than three 16-row tiles per compute unit",
+                        "group 128, K = 2048, 4096 or 8192 and at least 1.8 16-row tiles per compute unit",
                         bits);
         path = (path == WQ_PATH_GEMV || !kw) ? WQ_PATH_GEMV : WQ_PATH_MFMA;
         return WQ_OK;

@@ -49,6 +49,7 @@ namespace {
 
 constexpr int kKwBufWord3 = 0x00020000;     // raw, unswizzled gfx9 buffer
 constexpr uint32_t kKwFar = 0x80000000u;    // a per-lane offset past every buffer the kernel reads
+constexpr int kKwLgkm0 = 0xC07F;             // s_waitcnt lgkmcnt(0), vmcnt and expcnt unconstrained
 
 typedef __attribute__((address_space(3))) void kw_lds_void;
 typedef unsigned int kw_v4u __attribute__((ext_vector_type(4)));
@@ -460,12 +461,19 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_kw_kernel(const KwArgs a) {
             }
         }
         compute(st, hsv, hzv, 0, xw[(2 * pos) % DX]);
+        // The next load into this slot writes LDS behind the wave's back: every
+        // LDS read of the round must have returned first (the compiler leaves
+        // the last X reads in flight past the issue of the load otherwise, and
+        // a load that lands early, e.g. rows past B, which read as zeros at
+        // once, overwrites X the round has not read yet).
+        __builtin_amdgcn_s_waitcnt(kKwLgkm0);
         asm volatile("" ::: "memory");
         load_x(r + DX, (2 * pos) % DX);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAIT_ODD);
         asm volatile("" ::: "memory");
         compute(st, NF4 ? hs1 : hsv, hzv, 1, xw[(2 * pos + 1) % DX]);
+        __builtin_amdgcn_s_waitcnt(kKwLgkm0);
         asm volatile("" ::: "memory");
         load_x(r + 1 + DX, (2 * pos + 1) % DX);
         // The wait counts need X of a round issued wholly before the next
@@ -571,6 +579,8 @@ hipError_t launch_tpb(KwArgs a, hipStream_t stream) {
 template <int NCB, int BITS, int MODE, int NXL = NCB * 4>
 hipError_t launch_ncb(const KwArgs& a, int tpb, hipStream_t stream) {
     switch (tpb) {
+        case 2: return launch_tpb<NCB, 2, BITS, MODE, NXL>(a, stream);
+        case 3: return launch_tpb<NCB, 3, BITS, MODE, NXL>(a, stream);
         case 4: return launch_tpb<NCB, 4, BITS, MODE, NXL>(a, stream);
         case 5: return launch_tpb<NCB, 5, BITS, MODE, NXL>(a, stream);
         case 6: return launch_tpb<NCB, 6, BITS, MODE, NXL>(a, stream);
@@ -589,12 +599,21 @@ hipError_t launch_exact(const KwArgs& a, int tpb, hipStream_t stream) {
 
 }  // namespace
 
-// Tiles per block: the fewest that keep one block per compute unit, at least 4
-// (fewer would make the X stream, whole for every block, outweigh the codes).
+// Tiles per block: the fewest that keep one block per compute unit, 2 to 8.
+// Every block streams its quarter-K slices of X whole, so a block of two tiles
+// reads as many X bytes as code bytes at B = 16; that still beats a grid with
+// K split across blocks, whose partial sums go through HBM.
 int kw_tiles_per_block(int64_t N, int num_cus) {
     const int64_t ntiles = (N + 15) / 16;
     int64_t tpb = (ntiles + num_cus - 1) / num_cus;
-    return tpb < 4 ? 4 : tpb > 8 ? 8 : (int)tpb;
+    return tpb < 2 ? 2 : tpb > 8 ? 8 : (int)tpb;
+}
+
+// At least 1.8 tiles per compute unit: blocks of two tiles then still occupy
+// 90 % of the compute units; below that, half-empty grids leave the kernels
+// that split K the faster choice.
+static bool kw_enough_tiles(int64_t N, int num_cus) {
+    return (N + 15) / 16 * 10 >= 18 * (int64_t)num_cus;
 }
 
 bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset) {
@@ -605,7 +624,7 @@ bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, b
            (K == 2048 || K == 4096 || K == 8192) && N >= 16 && N <= (1 << 24);
 }
 
-// Taken on matrices of more than three tiles per compute unit; for 4-bit
+// Taken on matrices of at least 1.8 tiles per compute unit; for 4-bit
 // codes with integer zero points past 4 batch rows (at 4 and below the
 // quad-stream kernel reads the codes in a faster load shape and needs no
 // padding rows), for the other formats from 2 batch rows (at 1 the bit-stream
@@ -614,13 +633,13 @@ bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool
               int num_cus) {
     const bool int4 = bits == 4 && !offset;
     return B > (int4 ? 4 : 1) && kw_supports(B, K, N, group, bits, offset) &&
-           reinterpret_cast<uintptr_t>(X) % 16 == 0 && (N + 15) / 16 > 3 * (int64_t)num_cus;
+           reinterpret_cast<uintptr_t>(X) % 16 == 0 && kw_enough_tiles(N, num_cus);
 }
 
 // NF4 (blocks of 64, 4-bit codes indexing the level table): 2 <= B <= 32.
 bool kw_nf4_takes(int64_t B, int64_t K, int64_t N, int32_t group, const void* X, int num_cus) {
     return B >= 2 && B <= 32 && group == 64 && (K == 2048 || K == 4096 || K == 8192) && N >= 16 &&
-           N <= (1 << 24) && reinterpret_cast<uintptr_t>(X) % 16 == 0 && (N + 15) / 16 > 3 * (int64_t)num_cus;
+           N <= (1 << 24) && reinterpret_cast<uintptr_t>(X) % 16 == 0 && kw_enough_tiles(N, num_cus);
 }
 
 hipError_t launch_gemm_kw_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B, int64_t K,

@@ -432,8 +432,8 @@ hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales
                             int32_t group, int32_t bits, int num_cus, const Scratch& ws,
                             hipStream_t stream) {
     // Tall matrices at B <= 4 take the quad-stream kernel (groups of 64 and
-    // more) or the quad-row kernel; from B = 5 to 64, matrices of more than
-    // three 16-row tiles per compute unit take the K-split-wave kernel, and
+    // more) or the quad-row kernel; from B = 5 to 64, matrices of at least
+    // 1.8 16-row tiles per compute unit take the K-split-wave kernel, and
     // up to B = 16 the others take the tile-stream kernel or (with header
     // arrays it cannot stage) the streaming 16-row kernel; none of them needs
     // scratch.

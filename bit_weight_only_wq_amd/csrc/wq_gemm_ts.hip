@@ -1,5 +1,5 @@
-// Small-batch product (5 <= B <= 16 on matrices of up to three 16-row tiles
-// per compute unit) on the matrix cores' 16 x 16 x 32 blocks:
+// Small-batch product (5 <= B <= 16 on matrices of fewer than 1.8 16-row
+// tiles per compute unit) on the matrix cores' 16 x 16 x 32 blocks:
 // Y[B,N] = X[B,K] * dequant(W)[N,K]^T.
 //
 // The decode product streams the packed weights once for the whole batch

@@ -172,7 +172,7 @@ wq_status wq_quantize_workspace_size(int64_t N, int64_t K, int32_t group, int32_
  * inference optimisation", "Quantization", prints their errors next to 4 and
  * 8 bits): group % 32 == 0, K % 64 == 0 (bits 2) or K % 128 == 0 (bits 3),
  * K <= 32768.  They run on the GEMV path (the codes streamed once per four
- * batch rows), except that from B = 2 to 32, on matrices of more than three
+ * batch rows), except that from B = 2 to 32, on matrices of at least 1.8
  * 16-row tiles per compute unit with group 128 and K = 2048, 4096 or 8192
  * (and X 16-byte aligned), the MFMA path takes them (exact-integer operands,
  * header applied per group in fp32); WQ_PATH_MFMA outside those shapes is
@@ -242,7 +242,7 @@ wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void
  * WQ_ERR_UNSUPPORTED); group % 32 == 0; K % 64 (bits 2), % 128 (bits 3) or
  * % 32 (bits 4, 8); K <= 16384 (32768 at bits 3).  Layout and alignment as
  * wq_gemm, `mins` in place of `zeros`.  From B = 2 to 32 at bits 2, 3 or 4,
- * group 128, K = 2048, 4096 or 8192 and more than three 16-row tiles per
+ * group 128, K = 2048, 4096 or 8192 and at least 1.8 16-row tiles per
  * compute unit: a matrix-core kernel (exact-integer operands; per group
  * s * sum q x + m * sum x in fp32); otherwise the VALU bit-stream kernel, any
  * B (codes streamed once per four batch rows).

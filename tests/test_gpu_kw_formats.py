@@ -1,6 +1,6 @@
 """GPU parity of 2- and 3-bit codes, of the float-offset variant at 2, 3 and
 4 bits, and of NF4 codes (blocks of 64) on the K-split-wave matrix-core kernel (2 <= B <= 32, group 128,
-K = 2048, 4096 or 8192, more than three 16-row tiles per compute unit;
+K = 2048, 4096 or 8192, at least 1.8 16-row tiles per compute unit;
 wq_gemm_kw.hip) against the CPU oracle.
 
 The codes are unpacked as exact fp16 integers E + q, each operand slot with
@@ -12,7 +12,7 @@ and are scaled in fp16 (level * s, rounded once)
 and the group's endpoints give back the weight; its error table covers 8, 4,
 3 and 2 bits).  What the shapes exercise:
   - K = 2048, 4096, 8192 (one, two or four two-round steps per wave);
-  - 4 to 8 tiles per block, a partial last tile (N % 16 != 0);
+  - 2 to 8 tiles per block, a partial last tile (N % 16 != 0);
   - one and two 16-row batch blocks, batch rows past B read as zeros;
   - integer zero points from the asymmetric and both symmetric schemes, and
     float offsets (x_hat = q s + m);
@@ -35,6 +35,8 @@ import bit_weight_only_wq_amd as wq
 pytestmark = pytest.mark.gpu
 
 SHAPES = [  # (N, K, batches)
+    (8192, 8192, (2, 16, 32)),           # 2 tiles per block
+    (11990, 4096, (5, 17)),              # 3 tiles per block, partial last tile
     (12305, 2048, (2, 5, 16, 17, 32)),   # 4 tiles per block, partial last tile
     (16400, 4096, (3, 16, 24)),          # 5 tiles per block
     (12400, 8192, (2, 16, 32)),          # 4 tiles per block, four steps per wave
@@ -107,7 +109,8 @@ def test_low_bit_on_the_70b_matrix_all_rows(bits, B):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("N,K,batches", [(12305, 2048, (2, 16, 17, 32)), (16400, 4096, (9,))])
+@pytest.mark.parametrize("N,K,batches", [(12305, 2048, (2, 16, 17, 32)), (16400, 4096, (9,)),
+                                         (7400, 4096, (3, 32))])
 def test_float_offset_all_outputs(bits, N, K, batches):
     device()
     W, X = _draw(N, K, max(batches), 3 * N + K + bits)
@@ -140,7 +143,7 @@ def test_float_offset_on_the_70b_matrix_sampled_rows(bits):
 
 
 @pytest.mark.parametrize("N,K,batches", [(12305, 2048, (2, 16, 17, 32)), (16400, 4096, (3, 16)),
-                                         (12400, 8192, (9,))])
+                                         (12400, 8192, (9,)), (8192, 8192, (2, 32)), (11990, 4096, (16,))])
 def test_nf4_all_outputs(N, K, batches):
     """NF4 ("Gör inference billig", the NF4 paragraph): sixteen normal-quantile
     levels, one absolute-maximum scale per block of 64."""

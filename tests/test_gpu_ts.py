@@ -84,22 +84,19 @@ def test_tile_stream_repeat_is_bitwise_equal():
         assert torch.equal(a, b)
 
 
-def test_tile_stream_on_the_7b_matrix_sampled_rows():
-    """The 7B-class up-projection (11008 x 4096, 0.1 % outliers; fewer than
-    three tiles per compute unit, so the tile-stream kernel takes B = 5 .. 16):
-    rows sampled across the whole matrix (every stream's first and last tiles
-    included)."""
+def test_tile_stream_on_7b_rows_all_outputs():
+    """The first 7360 rows of the 7B-class up-projection (K = 4096, 0.1 %
+    outliers): 460 tiles, just under 1.8 per compute unit, so the tile-stream
+    kernel takes B = 5 .. 16; every output against the oracle."""
     device()
     name = "mlp7b_up_k4096_n11008_g128"
-    W, X = wq_inputs.workload_arrays(name)
+    W, _ = wq_inputs.workload_arrays(name)
+    W = np.ascontiguousarray(W[:7360])
     N, K = W.shape
     c, s, z = wq.quantize_pack(to_dev(W), 128, 4)
     cn, sn, zn = (t.cpu().numpy() for t in (c, s, z))
-    rows = np.unique(np.concatenate([np.arange(0, 256), np.arange(N - 256, N),
-                                     np.random.default_rng(6).choice(N, 512, replace=False)]))
     Xb = np.random.default_rng(7).standard_normal((16, K)).astype(np.float16)
     for B in (8, 16):
-        note(f"tile-stream {name} B={B}")
-        Y = wq.gemm(to_dev(Xb[:B]), c, s, z, N=N, K=K, group=128, bits=4, path="mfma").cpu().numpy()
-        ref = oracle.gemm(Xb[:B], cn[rows], sn[rows], zn[rows], len(rows), K, 128, 4)
-        assert_close(Y[:, rows], ref, f"{name} B={B}")
+        note(f"tile-stream {name}[:7360] B={B}")
+        Y = wq.gemm(to_dev(Xb[:B]), c, s, z, N=N, K=K, group=128, bits=4, path="mfma")
+        assert_close(Y, oracle.gemm(Xb[:B], cn, sn, zn, N, K, 128, 4), f"{name}[:7360] B={B}")
