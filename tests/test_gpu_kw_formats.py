@@ -28,7 +28,7 @@ import pytest
 import oracle
 import oracle.nf4 as onf4
 import wq_inputs
-from gpu_util import assert_close, device, note, to_dev
+from gpu_util import assert_close, device, note, to_dev, torch
 
 import bit_weight_only_wq_amd as wq
 
@@ -184,3 +184,29 @@ def test_nf4_on_the_70b_matrix_sampled_rows():
     rows = np.unique(np.concatenate([np.arange(0, 256), np.arange(N - 256, N),
                                      np.random.default_rng(11).choice(N, 512, replace=False)]))
     assert_close(Y[:, rows], onf4.gemm(Xb, c.cpu().numpy()[rows], s.cpu().numpy()[rows], K, 64), f"nf4 {name}")
+
+
+@pytest.mark.parametrize("bits,scheme,B", [(3, "offset", 3), (2, "offset", 3), (4, "offset", 3), (4, "asym", 5)])
+def test_small_batch_two_tile_blocks_repeat_is_bitwise_equal(bits, scheme, B):
+    """Blocks of two tiles at B = 3 and 5: the X rows past B of every slot read
+    as zeros at once, so a slot refill that overtook the round's own LDS reads
+    would change the result from call to call.  Ten calls agree bit for bit
+    and match the oracle."""
+    device()
+    N, K = 7400, 4096
+    W, X = _draw(N, K, B, 97 + bits)
+    if scheme == "offset":
+        c, s, m = oracle.quantize(W, 128, bits, scheme="offset")
+        ref = oracle.gemm_offset(X, c, s, m, K, 128, bits)
+        call = lambda: wq.gemm_offset(Xd, *dev, N=N, K=K, group=128, bits=bits)
+    else:
+        c, s, m = oracle.quantize(W, 128, bits)
+        ref = oracle.gemm(X, c, s, m, N, K, 128, bits)
+        call = lambda: wq.gemm(Xd, *dev, N=N, K=K, group=128, bits=bits, path="mfma")
+    dev = [to_dev(a) for a in (c, s, m)]
+    Xd = to_dev(X)
+    note(f"kw formats repeat {scheme} b={bits} N={N} K={K} B={B}")
+    first = call()
+    assert_close(first, ref, f"repeat {scheme} b={bits}")
+    for _ in range(9):
+        assert torch.equal(call(), first)
