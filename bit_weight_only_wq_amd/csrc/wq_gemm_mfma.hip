@@ -390,7 +390,13 @@ hipError_t launch_bits(const void* X, const void* codes, const void* scales, con
         if (tall) return launch_bt<BITS, 32, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, ws, st);
         return launch_bt<BITS, 32, KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, ws, st);
     }
-    if (tall) return launch_bt<BITS, 64, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, ws, st);
+    // Past 32 columns, 128-row tiles also pay when they alone give one to two
+    // blocks per CU (B = 256 on 8192 x 8192 and 11008 x 4096: 7-10 % faster;
+    // B = 512 on 8192 x 8192 and 4096 x 4096: 3-6 %; fewer or more tiles than
+    // that measured equal or slower).
+    const int64_t tiles128 = ((N + 127) / 128) * ((B + 63) / 64);
+    if (tall || (tiles128 >= cus && tiles128 <= 2 * (int64_t)cus))
+        return launch_bt<BITS, 64, KR, 2>(X, codes, scales, zeros, Y, B, K, N, G, cus, ws, st);
     return launch_bt<BITS, 64, KR, 1>(X, codes, scales, zeros, Y, B, K, N, G, cus, ws, st);
 }
 

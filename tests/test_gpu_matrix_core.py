@@ -152,3 +152,18 @@ def test_two_streams():
     torch.cuda.synchronize()
     for y in outs:
         assert np.array_equal(y.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("N,K,B", [(8192, 1024, 256), (4100, 1024, 500), (12000, 512, 160)])
+def test_tiled_128_row_tiles_past_the_ridge(N, K, B):
+    """Past 64 batch columns, matrices whose 128-row tiles give one to two
+    blocks per compute unit take two 16-row tiles per wave (ragged N and B,
+    K-splits added in order); every output against the oracle."""
+    device()
+    rng = np.random.default_rng(N + B)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    X = rng.standard_normal((B, K)).astype(np.float16)
+    host, dev = packed(W, 128, 4)
+    note(f"tiled 128-row N={N} K={K} B={B}")
+    Y = wq.gemm(to_dev(X), *dev, N=N, K=K, group=128, bits=4, path="mfma")
+    assert_close(Y, oracle.gemm(X, *host, N, K, 128, 4), f"N={N} K={K} B={B}")
