@@ -30,6 +30,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [  # (N, K, batches)
     (7400, 4096, (9, 33)),              # 2 tiles per block, last block one partial tile
+    (7376, 2048, (5, 16, 64)),          # 461 tiles, the fewest taken: 2 per block, one step per wave
     (8192, 8192, (5, 16, 32, 64)),      # 2 tiles per block, one block per compute unit
     (11990, 2048, (6, 24)),             # 3 tiles per block, partial last tile
     (12305, 2048, (5, 9, 16, 17, 64)),  # 4 tiles per block, partial last tile

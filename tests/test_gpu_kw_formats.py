@@ -36,6 +36,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [  # (N, K, batches)
     (8192, 8192, (2, 16, 32)),           # 2 tiles per block
+    (7376, 2048, (2, 32)),               # 461 tiles (the fewest taken), one step per wave
     (11990, 4096, (5, 17)),              # 3 tiles per block, partial last tile
     (12305, 2048, (2, 5, 16, 17, 32)),   # 4 tiles per block, partial last tile
     (16400, 4096, (3, 16, 24)),          # 5 tiles per block
