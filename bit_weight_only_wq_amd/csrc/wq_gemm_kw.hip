@@ -6,10 +6,10 @@
 // stream sets the time ("Quantization & inference optimisation", "Bandwidth,
 // not compute"), so the design keeps that stream whole and moves as little
 // else as it can:
-//   - a block (4 waves, one per SIMD) owns TPB 16-row tiles of W across all of
-//     K; wave w takes the w-th quarter of K, so each X value reaches the
-//     compute unit once, and the waves' fp32 sums are added in LDS, in wave
-//     order, at the end: no partial sums leave the compute unit;
+//   - a block (4 waves, one per SIMD) owns TPB (2 to 8) 16-row tiles of W
+//     across all of K; wave w takes the w-th quarter of K, so each X value
+//     reaches the compute unit once, and the waves' fp32 sums are added in
+//     LDS, in wave order, at the end: no partial sums leave the compute unit;
 //   - K is walked in rounds of 128 k (one group): lane (r16, g4) of tile t
 //     holds the 16-byte code chunk of row 16 t + r16 at k [32 g4, 32 g4 + 32)
 //     of the round, the weight operand of v_mfma_f32_16x16x32_f16 for the
