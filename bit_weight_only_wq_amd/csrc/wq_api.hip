@@ -275,14 +275,14 @@ static wq_status check_gemm_shape(int64_t B, int64_t K, int64_t N, int32_t group
         return WQ_OK;
     }
     if (low) {
-        // The K-split-wave matrix-core kernel where it takes the shape (X's
-        // alignment is checked with the pointers), the bit-stream GEMV
-        // otherwise.
-        const bool kw = wq::kw_takes(B, K, N, group, bits, false, nullptr, num_cus());
+        // The K-split-wave matrix-core kernel where it takes the shape and
+        // the header arrays (X's alignment is checked with the pointers),
+        // the bit-stream GEMV otherwise.
+        const bool kw = wq::kw_takes(B, K, N, group, bits, false, nullptr, scales, zeros, num_cus());
         if (path == WQ_PATH_MFMA && !kw)
             return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: bits=%lld takes the MFMA path only for 2 <= B <= 32, "
-                        "group 128, K = 2048, 4096 or 8192 and at least 1.8 16-row tiles per compute unit",
-                        bits);
+                        "group 128, K = 2048, 4096 or 8192, at least 1.8 16-row tiles per compute unit and "
+                        "16-byte aligned header arrays", bits);
         path = (path == WQ_PATH_GEMV || !kw) ? WQ_PATH_GEMV : WQ_PATH_MFMA;
         return WQ_OK;
     }
@@ -605,7 +605,7 @@ wq_status wq_gemm_offset(const void* X, const void* codes, const void* scales, c
     if (!X || !codes || !scales || !mins || !Y) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_offset: null pointer");
     if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(mins, 2) || !aligned(Y, 2))
         return fail(WQ_ERR_MISALIGNED, "wq_gemm_offset: X and codes need 16-byte alignment");
-    if (wq::kw_takes(B, K, N, group, bits, true, X, num_cus()))
+    if (wq::kw_takes(B, K, N, group, bits, true, X, scales, mins, num_cus()))
         return check_hip(wq::launch_gemm_kw(X, codes, scales, mins, Y, B, K, N, group, bits, true, num_cus(),
                                             static_cast<hipStream_t>(stream)),
                          "wq_gemm_offset (mfma) launch");
@@ -628,7 +628,7 @@ wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void
     if (!X || !codes || !scales || !Y) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_nf4: null pointer");
     if (!aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(Y, 2))
         return fail(WQ_ERR_MISALIGNED, "wq_gemm_nf4: X and codes need 16-byte alignment");
-    if (wq::kw_nf4_takes(B, K, N, group, X, num_cus()))
+    if (wq::kw_nf4_takes(B, K, N, group, X, scales, num_cus()))
         return check_hip(wq::launch_gemm_kw_nf4(X, codes, scales, Y, B, K, N, group, num_cus(),
                                                 static_cast<hipStream_t>(stream)),
                          "wq_gemm_nf4 (mfma) launch");

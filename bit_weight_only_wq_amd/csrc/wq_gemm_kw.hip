@@ -624,27 +624,32 @@ bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, b
            (K == 2048 || K == 4096 || K == 8192) && N >= 16 && N <= (1 << 24);
 }
 
-// Taken on matrices of at least 1.8 tiles per compute unit; for 4-bit
+static bool kw_aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// Taken on matrices of at least 1.8 tiles per compute unit, with X and the
+// header arrays 16-byte aligned (the headers are staged by 16-byte loads; a
+// null pointer, as in a size query, counts as aligned); for 4-bit
 // codes with integer zero points past 4 batch rows (at 4 and below the
 // quad-stream kernel reads the codes in a faster load shape and needs no
 // padding rows), for the other formats from 2 batch rows (at 1 the bit-stream
 // GEMV streams them as fast).
 bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset, const void* X,
-              int num_cus) {
+              const void* scales, const void* zeros, int num_cus) {
     const bool int4 = bits == 4 && !offset;
-    return B > (int4 ? 4 : 1) && kw_supports(B, K, N, group, bits, offset) &&
-           reinterpret_cast<uintptr_t>(X) % 16 == 0 && kw_enough_tiles(N, num_cus);
+    return B > (int4 ? 4 : 1) && kw_supports(B, K, N, group, bits, offset) && kw_aligned16(X) &&
+           kw_aligned16(scales) && kw_aligned16(zeros) && kw_enough_tiles(N, num_cus);
 }
 
 // NF4 (blocks of 64, 4-bit codes indexing the level table): 2 <= B <= 32.
-bool kw_nf4_takes(int64_t B, int64_t K, int64_t N, int32_t group, const void* X, int num_cus) {
+bool kw_nf4_takes(int64_t B, int64_t K, int64_t N, int32_t group, const void* X, const void* scales,
+                  int num_cus) {
     return B >= 2 && B <= 32 && group == 64 && (K == 2048 || K == 4096 || K == 8192) && N >= 16 &&
-           N <= (1 << 24) && reinterpret_cast<uintptr_t>(X) % 16 == 0 && kw_enough_tiles(N, num_cus);
+           N <= (1 << 24) && kw_aligned16(X) && kw_aligned16(scales) && kw_enough_tiles(N, num_cus);
 }
 
 hipError_t launch_gemm_kw_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B, int64_t K,
                               int64_t N, int32_t group, int num_cus, hipStream_t stream) {
-    if (!kw_nf4_takes(B, K, N, group, X, num_cus)) return hipErrorInvalidValue;
+    if (!kw_nf4_takes(B, K, N, group, X, scales, num_cus)) return hipErrorInvalidValue;
     KwArgs a;
     a.X = static_cast<const uint16_t*>(X);
     a.codes = static_cast<const uint8_t*>(codes);
@@ -662,7 +667,8 @@ hipError_t launch_gemm_kw_nf4(const void* X, const void* codes, const void* scal
 hipError_t launch_gemm_kw(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,
                           int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset, int num_cus,
                           hipStream_t stream) {
-    if (!kw_supports(B, K, N, group, bits, offset) || reinterpret_cast<uintptr_t>(X) % 16 != 0)
+    if (!kw_supports(B, K, N, group, bits, offset) || !kw_aligned16(X) || !kw_aligned16(scales) ||
+        !kw_aligned16(zeros))
         return hipErrorInvalidValue;
     KwArgs a;
     a.X = static_cast<const uint16_t*>(X);

@@ -453,7 +453,7 @@ hipError_t launch_gemm_mfma(const void* X, const void* codes, const void* scales
         if (ws.sizing()) return hipSuccess;
         return launch_gemm_q4(X, codes, scales, zeros, Y, B, K, N, group, num_cus, stream);
     }
-    if (kw_takes(B, K, N, group, bits, false, X, num_cus)) {
+    if (kw_takes(B, K, N, group, bits, false, X, scales, zeros, num_cus)) {
         if (ws.sizing()) return hipSuccess;
         return launch_gemm_kw(X, codes, scales, zeros, Y, B, K, N, group, bits, false, num_cus, stream);
     }

@@ -100,15 +100,18 @@ bool ts_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, cons
 // zero points up to B = 64; 2- and 3-bit codes, and float offsets (offset:
 // `zeros` holds the group minima m, x_hat = q s + m) at bits 2, 3 and 4, up
 // to B = 32.  kw_takes adds the shape choice: at least 1.8 16-row tiles
-// per compute unit, and B > 4 for 4-bit integer-zero codes (where the
-// quad-stream kernel takes B <= 4), B >= 2 otherwise.
+// per compute unit, 16-byte aligned header arrays (null counts as aligned),
+// and B > 4 for 4-bit integer-zero codes (where the quad-stream kernel takes
+// B <= 4), B >= 2 otherwise.
 bool kw_supports(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset);
 bool kw_takes(int64_t B, int64_t K, int64_t N, int32_t group, int32_t bits, bool offset, const void* X,
-              int num_cus);
+              const void* scales, const void* zeros, int num_cus);
 int kw_tiles_per_block(int64_t N, int num_cus);
 // NF4 codes (wq_gemm_nf4) on the same kernel: blocks of 64 only, 2 <= B <= 32,
-// K = 2048, 4096 or 8192, at least 1.8 16-row tiles per compute unit.
-bool kw_nf4_takes(int64_t B, int64_t K, int64_t N, int32_t group, const void* X, int num_cus);
+// K = 2048, 4096 or 8192, at least 1.8 16-row tiles per compute unit, X and
+// scales 16-byte aligned.
+bool kw_nf4_takes(int64_t B, int64_t K, int64_t N, int32_t group, const void* X, const void* scales,
+                  int num_cus);
 hipError_t launch_gemm_kw_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B, int64_t K,
                               int64_t N, int32_t group, int num_cus, hipStream_t stream);
 hipError_t launch_gemm_kw(const void* X, const void* codes, const void* scales, const void* zeros, void* Y,

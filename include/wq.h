@@ -174,7 +174,8 @@ wq_status wq_quantize_workspace_size(int64_t N, int64_t K, int32_t group, int32_
  * K <= 32768.  They run on the GEMV path (the codes streamed once per four
  * batch rows), except that from B = 2 to 32, on matrices of at least 1.8
  * 16-row tiles per compute unit with group 128 and K = 2048, 4096 or 8192
- * (and X 16-byte aligned), the MFMA path takes them (exact-integer operands,
+ * (and X and both header arrays 16-byte aligned), the MFMA path takes them
+ * (exact-integer operands,
  * header applied per group in fp32); WQ_PATH_MFMA outside those shapes is
  * WQ_ERR_UNSUPPORTED.  bits 1, 5, 6 and 7 are WQ_ERR_UNSUPPORTED.
  * Results are deterministic: no atomics, fixed reduction order.
@@ -227,8 +228,12 @@ wq_status wq_gemm_workspace_size(int64_t B, int64_t K, int64_t N, int32_t group,
  * fp32 accumulation, Y rounded once to fp16.  X fp16 [B, K] (16-byte
  * aligned), codes u8 [N, K/2] (16-byte aligned), scales fp16 [N, K/group],
  * Y fp16 [B, N].  K % 32 == 0, group % 32 == 0, K <= 16384 (else
- * WQ_ERR_UNSUPPORTED); B or N == 0 is a no-op.  VALU kernel with a level
- * lookup table, any B (codes are streamed once per four batch rows).
+ * WQ_ERR_UNSUPPORTED); B or N == 0 is a no-op.  From B = 2 to 32 with group
+ * 64, K = 2048, 4096 or 8192, at least 1.8 16-row tiles per compute unit and
+ * 16-byte aligned `scales`: a matrix-core kernel (each code byte becomes a
+ * pair of fp16 levels through an LDS table, times the scale in fp16);
+ * otherwise a VALU kernel with the same table, any B (codes streamed once per
+ * four batch rows).
  */
 wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void* Y, int64_t B,
                       int64_t K, int64_t N, int32_t group, void* stream);
@@ -242,8 +247,9 @@ wq_status wq_gemm_nf4(const void* X, const void* codes, const void* scales, void
  * WQ_ERR_UNSUPPORTED); group % 32 == 0; K % 64 (bits 2), % 128 (bits 3) or
  * % 32 (bits 4, 8); K <= 16384 (32768 at bits 3).  Layout and alignment as
  * wq_gemm, `mins` in place of `zeros`.  From B = 2 to 32 at bits 2, 3 or 4,
- * group 128, K = 2048, 4096 or 8192 and at least 1.8 16-row tiles per
- * compute unit: a matrix-core kernel (exact-integer operands; per group
+ * group 128, K = 2048, 4096 or 8192, at least 1.8 16-row tiles per compute
+ * unit and 16-byte aligned `scales` and `mins`: a matrix-core kernel
+ * (exact-integer operands; per group
  * s * sum q x + m * sum x in fp32); otherwise the VALU bit-stream kernel, any
  * B (codes streamed once per four batch rows).
  */

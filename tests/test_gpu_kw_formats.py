@@ -211,3 +211,41 @@ def test_small_batch_two_tile_blocks_repeat_is_bitwise_equal(bits, scheme, B):
     assert_close(first, ref, f"repeat {scheme} b={bits}")
     for _ in range(9):
         assert torch.equal(call(), first)
+
+
+def _offset_headers(a):
+    """Device copy of a header array one entry past a 16-byte boundary."""
+    flat = torch.zeros(a.size + 8, dtype=torch.float16, device=device())
+    flat[1:1 + a.size] = to_dev(a.reshape(-1))
+    return flat[1:1 + a.size].view(a.shape)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int2", "int3", "offset", "nf4"])
+def test_unaligned_headers_take_other_kernels(fmt):
+    """Header arrays that are only 2-byte aligned (allowed by the interface)
+    are not staged by the K-split-wave kernel's 16-byte loads: the shape
+    (12305 x 2048, B = 16) then runs on another kernel, and matches the
+    oracle and the aligned call's result."""
+    device()
+    N, K, B = 12305, 2048, 16
+    W, X = _draw(N, K, B, 211)
+    Xd = to_dev(X)
+    note(f"kw formats unaligned headers {fmt}")
+    if fmt == "nf4":
+        c, s = onf4.quantize(W, 64)
+        ref = onf4.gemm(X, c, s, K, 64)
+        ya = wq.gemm_nf4(Xd, to_dev(c), to_dev(s), N=N, K=K, group=64)
+        yu = wq.gemm_nf4(Xd, to_dev(c), _offset_headers(s), N=N, K=K, group=64)
+    elif fmt == "offset":
+        c, s, m = oracle.quantize(W, 128, 4, scheme="offset")
+        ref = oracle.gemm_offset(X, c, s, m, K, 128, 4)
+        ya = wq.gemm_offset(Xd, to_dev(c), to_dev(s), to_dev(m), N=N, K=K, group=128, bits=4)
+        yu = wq.gemm_offset(Xd, to_dev(c), _offset_headers(s), _offset_headers(m), N=N, K=K, group=128, bits=4)
+    else:
+        bits = {"int4": 4, "int2": 2, "int3": 3}[fmt]
+        c, s, z = oracle.quantize(W, 128, bits)
+        ref = oracle.gemm(X, c, s, z, N, K, 128, bits)
+        ya = wq.gemm(Xd, to_dev(c), to_dev(s), to_dev(z), N=N, K=K, group=128, bits=bits)
+        yu = wq.gemm(Xd, to_dev(c), _offset_headers(s), _offset_headers(z), N=N, K=K, group=128, bits=bits)
+    assert_close(ya, ref, f"{fmt} aligned")
+    assert_close(yu, ref, f"{fmt} unaligned")
